@@ -1,0 +1,140 @@
+/*
+ * tri_attn.h — C ABI of the gfx950 (MI355X) triangle-attention library, libtriattn.so.
+ *
+ * The operation is starting-node triangular attention as used in AlphaFold3-style
+ * models ("TurboPairFormer: Fast and Stable Protein Folding Model Training with an
+ * Optimized Triangle Attention Kernel", arXiv 2610.05854, Abstract).  For every batch
+ * b, slice i and head h, with alpha = 1/sqrt(D):
+ *
+ *   s[j,k] = alpha * sum_c q[b,i,h,j,c] k[b,i,h,k,c] + bias[b,h,j,k] + m[b,i,k]
+ *   o[b,i,h,j,:] = sum_k softmax_k(s[j,:]) v[b,i,h,k,:]
+ *
+ * where the pair bias is shared by all N slices and m = -1e9 for a masked key, else 0.
+ * The backward returns dq, dk, dv and dbias[b,h,j,k] = sum_i dS[b,i,h,j,k], the
+ * reduction across slices that the shared bias adds (same Abstract).
+ *
+ * Memory layouts (row-major, contiguous, caller-owned DEVICE memory):
+ *   q, k, v, o, residual, dO, dq, dk, dv : bf16 [B, N, H, N, D]   index [b, i, h, j, c]
+ *   bias                                 : bf16 [B, H, N, N]      index [b, h, j, k]
+ *   key_mask (optional)                  : uint8 [B, N, N]        index [b, i, k]; 1 keep, 0 mask
+ *   lse                                  : fp32 [B, N, H, N]      natural-log logsumexp of each row
+ *   dbias                                : fp32 [B, H, N, N]
+ *
+ * Conventions shared by every entry point:
+ *   - All pointers are device pointers, 16-byte aligned (key_mask: any alignment).
+ *   - Supported shapes: D in {16, 32}; 1 <= N <= TRI_ATTN_MAX_N; B, H >= 1.
+ *   - The library allocates no memory and keeps no state between calls.  Scratch
+ *     space comes from the caller through (workspace, workspace_bytes), sized by the
+ *     matching *_workspace_bytes function, and is only valid for the call it is passed to.
+ *   - Arguments are validated synchronously before anything is launched.  On any
+ *     error nothing is launched and no output is written.
+ *   - Work is enqueued on `stream` and runs asynchronously; faults inside kernels
+ *     surface at the caller's next synchronisation.
+ *   - Outputs are overwritten, never accumulated into; outputs must not overlap inputs.
+ *   - Every floating-point reduction runs in a fixed order that depends only on the
+ *     shape, with no floating-point atomics: repeated calls with the same inputs and
+ *     shape on the same device return bitwise-identical outputs.
+ *   - Every row must keep at least one key; a fully masked row gives finite but
+ *     otherwise unspecified results.
+ */
+#ifndef TRI_ATTN_H
+#define TRI_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TRI_ATTN_MAX_N 768
+
+typedef enum {
+  TRI_ATTN_SUCCESS = 0,
+  TRI_ATTN_ERROR_INVALID_VALUE = 1, /* NULL required pointer, B/N/H < 1, or output overlapping an input */
+  TRI_ATTN_ERROR_UNSUPPORTED = 2,   /* D not in {16, 32}, or N > TRI_ATTN_MAX_N */
+  TRI_ATTN_ERROR_MISALIGNED = 3,    /* a tensor pointer that is not 16-byte aligned */
+  TRI_ATTN_ERROR_WORKSPACE = 4,     /* workspace NULL or smaller than *_workspace_bytes() */
+  TRI_ATTN_ERROR_LAUNCH = 5         /* the HIP runtime rejected a kernel launch */
+} tri_attn_status;
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char *tri_attn_status_string(int status);
+
+/* Bytes of device workspace tri_attn_fwd needs for this shape (0 if the shape is invalid). */
+size_t tri_attn_fwd_workspace_bytes(int64_t B, int64_t N, int64_t H, int64_t D);
+
+/*
+ * Forward: writes o, lse and (optionally) the output-rounding residual.
+ *
+ * residual: if non-NULL, receives bf16(o_fp32 - float(o)), the rounding error of the
+ *   bf16 output kept at bf16 precision ("output-residual compensation", TurboPairFormer
+ *   Abstract).  The bf16 output o itself does not depend on whether residual is stored.
+ *   Pass NULL to skip it.
+ * key_mask: NULL means no mask.
+ */
+tri_attn_status tri_attn_fwd(int64_t B, int64_t N, int64_t H, int64_t D,
+                             const void *q, const void *k, const void *v, const void *bias,
+                             const uint8_t *key_mask,
+                             void *o, float *lse, void *residual,
+                             void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of device workspace tri_attn_bwd needs for this shape (0 if the shape is invalid). */
+size_t tri_attn_bwd_workspace_bytes(int64_t B, int64_t N, int64_t H, int64_t D);
+
+/*
+ * Backward: given the forward's o, lse (and residual) and the output gradient dO,
+ * writes dq, dk, dv (bf16) and dbias (fp32).
+ *
+ * The softmax backward correction D[j] = sum_c dO[j,c] * o_fp32[j,c] is computed in
+ * FP32 from o + residual when residual is non-NULL (compensated), or from the bf16 o
+ * alone when residual is NULL.  dv does not depend on this choice.
+ *
+ * The key-tile-parallel scheme recomputes each probability tile once for all four
+ * gradients and reduces dq (over key blocks) and dbias (over slice groups) through
+ * ordered partial buffers held in the workspace (TurboPairFormer Abstract).
+ */
+tri_attn_status tri_attn_bwd(int64_t B, int64_t N, int64_t H, int64_t D,
+                             const void *q, const void *k, const void *v, const void *bias,
+                             const uint8_t *key_mask,
+                             const void *o, const float *lse, const void *residual,
+                             const void *dO,
+                             void *dq, void *dk, void *dv, float *dbias,
+                             void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Staged forms of the two calls, for callers that interleave their own work or time the
+ * kernels individually.  tri_attn_fwd / tri_attn_bwd are exactly the staged call with
+ * TRI_ATTN_STAGE_ALL.  Stages must run in ascending order, on one stream, with the same
+ * arguments and the same workspace; the workspace carries intermediate results from one
+ * stage to the next.  Validation is the same as for the unstaged call.
+ *   forward : PREP = bias conversion into the workspace; MAIN = attention kernel; FINAL = none
+ *   backward: PREP = bias conversion and the correction D; MAIN = the key-tile-parallel kernel
+ *             (all five products); FINAL = ordered sums of the dq and dbias partials
+ */
+#define TRI_ATTN_STAGE_PREP 1u
+#define TRI_ATTN_STAGE_MAIN 2u
+#define TRI_ATTN_STAGE_FINAL 4u
+#define TRI_ATTN_STAGE_ALL 7u
+
+tri_attn_status tri_attn_fwd_stages(unsigned stages, int64_t B, int64_t N, int64_t H, int64_t D,
+                                    const void *q, const void *k, const void *v, const void *bias,
+                                    const uint8_t *key_mask,
+                                    void *o, float *lse, void *residual,
+                                    void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+tri_attn_status tri_attn_bwd_stages(unsigned stages, int64_t B, int64_t N, int64_t H, int64_t D,
+                                    const void *q, const void *k, const void *v, const void *bias,
+                                    const uint8_t *key_mask,
+                                    const void *o, const float *lse, const void *residual,
+                                    const void *dO,
+                                    void *dq, void *dk, void *dv, float *dbias,
+                                    void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TRI_ATTN_H */

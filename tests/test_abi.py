@@ -1,0 +1,123 @@
+"""The C ABI of libtriattn.so: exported symbols and synchronous argument validation.
+
+These tests run without a GPU.  Every call below is built to fail validation
+(the library validates every argument before touching the HIP runtime), so the fake
+integer pointers are never dereferenced and nothing is launched.
+"""
+import os
+import re
+
+import pytest
+
+import triangle_attention_amd as ta
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SUCCESS, INVALID, UNSUPPORTED, MISALIGNED, WORKSPACE, LAUNCH = range(6)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ta.LIB_PATH):
+        ta.build()
+    return ta.load_library()
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "tri_attn.h")).read()
+    return sorted(set(re.findall(r"\b(tri_attn_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert {"tri_attn_fwd", "tri_attn_bwd", "tri_attn_fwd_workspace_bytes",
+            "tri_attn_bwd_workspace_bytes", "tri_attn_status_string"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code, name in [(SUCCESS, "SUCCESS"), (INVALID, "INVALID_VALUE"), (UNSUPPORTED, "UNSUPPORTED"),
+                       (MISALIGNED, "MISALIGNED"), (WORKSPACE, "WORKSPACE"), (LAUNCH, "LAUNCH")]:
+        assert ta.tri_attn_status_string(code).endswith(name)
+    assert "UNKNOWN" in ta.tri_attn_status_string(1234)
+
+
+def test_workspace_sizes(lib):
+    for B, N, H, D in [(1, 1, 1, 16), (1, 64, 4, 16), (2, 100, 3, 32), (1, 768, 4, 32)]:
+        f = ta.tri_attn_fwd_workspace_bytes(B, N, H, D)
+        b = ta.tri_attn_bwd_workspace_bytes(B, N, H, D)
+        assert f > 0 and b > f and f % 256 == 0 and b % 256 == 0
+    for bad in [(0, 8, 1, 16), (1, 0, 1, 16), (1, 8, 0, 16), (1, 8, 1, 64), (1, 769, 1, 16)]:
+        assert ta.tri_attn_fwd_workspace_bytes(*bad) == 0
+        assert ta.tri_attn_bwd_workspace_bytes(*bad) == 0
+    # the backward partial buffers grow with N (dq partials per 64-key block)
+    assert ta.tri_attn_bwd_workspace_bytes(1, 768, 4, 32) > ta.tri_attn_bwd_workspace_bytes(1, 384, 4, 32)
+
+
+# fake, well-separated, 16-byte-aligned device addresses; never dereferenced
+def _ptrs(n, base=1 << 40, step=1 << 32):
+    return [base + i * step for i in range(n)]
+
+
+def _fwd(shape=(1, 64, 4, 16), ptrs=None, mask=None, res=True, ws=None, wsb=None):
+    p = ptrs or _ptrs(8)
+    q, k, v, bias, o, lse, r, w = p
+    wsb = ta.tri_attn_fwd_workspace_bytes(*shape) if wsb is None else wsb
+    return ta.tri_attn_fwd(*shape, q, k, v, bias, mask, o, lse, r if res else None, w if ws is None else ws, wsb, 0)
+
+
+def _bwd(shape=(1, 64, 4, 16), ptrs=None, mask=None, ws=None, wsb=None):
+    p = ptrs or _ptrs(14)
+    q, k, v, bias, o, lse, r, dO, dq, dk, dv, db, w = p[:13]
+    wsb = ta.tri_attn_bwd_workspace_bytes(*shape) if wsb is None else wsb
+    return ta.tri_attn_bwd(*shape, q, k, v, bias, mask, o, lse, r, dO, dq, dk, dv, db, w if ws is None else ws, wsb, 0)
+
+
+def test_fwd_validation(lib):
+    assert _fwd(shape=(0, 64, 4, 16)) == INVALID
+    assert _fwd(shape=(1, 0, 4, 16)) == INVALID
+    assert _fwd(shape=(1, 64, 0, 16)) == INVALID
+    assert _fwd(shape=(1, 64, 4, 64)) == UNSUPPORTED
+    assert _fwd(shape=(1, 64, 4, 8)) == UNSUPPORTED
+    assert _fwd(shape=(1, 769, 4, 16)) == UNSUPPORTED
+    for idx in range(6):  # q, k, v, bias, o, lse are required
+        p = _ptrs(8)
+        p[idx] = 0
+        assert _fwd(ptrs=p) == INVALID, idx
+    p = _ptrs(8)
+    p[4] = p[0] + 64  # o overlaps q
+    assert _fwd(ptrs=p) == INVALID
+    p = _ptrs(8)
+    p[7] = p[1]  # workspace overlaps k
+    assert _fwd(ptrs=p) == INVALID
+    for idx in (0, 1, 2, 3, 4, 5, 6, 7):
+        p = _ptrs(8)
+        p[idx] += 8
+        assert _fwd(ptrs=p) == MISALIGNED, idx
+    assert _fwd(ws=0) == WORKSPACE
+    assert _fwd(wsb=ta.tri_attn_fwd_workspace_bytes(1, 64, 4, 16) - 256) == WORKSPACE
+    # the mask may have any alignment; with everything else valid except the workspace size
+    assert _fwd(mask=(1 << 40) + 13 * (1 << 32) + 3, wsb=16) == WORKSPACE
+
+
+def test_bwd_validation(lib):
+    assert _bwd(shape=(1, 64, 4, 48)) == UNSUPPORTED
+    assert _bwd(shape=(2, 0, 4, 16)) == INVALID
+    for idx in (0, 1, 2, 3, 4, 5, 7, 8, 9, 10, 11):  # every tensor except the residual is required
+        p = _ptrs(14)
+        p[idx] = 0
+        assert _bwd(ptrs=p) == INVALID, idx
+    p = _ptrs(14)
+    p[11] = p[3]  # dbias aliases bias
+    assert _bwd(ptrs=p) == INVALID
+    p = _ptrs(14)
+    p[9] = p[8] + 32  # dk overlaps dq
+    assert _bwd(ptrs=p) == INVALID
+    p = _ptrs(14)
+    p[6] = 0  # no residual: uncompensated correction, still only the workspace is wrong
+    assert _bwd(ptrs=p, wsb=64) == WORKSPACE
+    p = _ptrs(14)
+    p[10] += 4
+    assert _bwd(ptrs=p) == MISALIGNED
+    assert _bwd(wsb=ta.tri_attn_bwd_workspace_bytes(1, 64, 4, 16) - 1) == WORKSPACE
+    assert _bwd(ws=0) == WORKSPACE

@@ -1,0 +1,185 @@
+"""Python binding of libtriattn.so: gfx950 triangle attention (starting node), forward + backward.
+
+The C entry points of ``include/tri_attn.h`` are exposed under the same names; the
+binding only marshals arguments (tensor pointers, sizes, the current HIP stream).  Every
+step of the computation runs in the HIP library.  If the library is not built, every
+call raises: there is no fallback implementation.
+
+Method: "TurboPairFormer: Fast and Stable Protein Folding Model Training with an
+Optimized Triangle Attention Kernel" (arXiv 2610.05854), Abstract.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from ._build import LIB_PATH, build  # noqa: F401
+
+__all__ = [
+    "TriAttnError", "load_library", "tri_attn_status_string", "tri_attn_fwd_workspace_bytes",
+    "tri_attn_bwd_workspace_bytes", "tri_attn_fwd", "tri_attn_bwd", "tri_attn_fwd_stages", "tri_attn_bwd_stages",
+    "triangle_attention", "TRI_ATTN_MAX_N",
+]
+
+TRI_ATTN_MAX_N = 768
+_lib = None
+
+
+class TriAttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {tri_attn_status_string(status)} ({status})")
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libtriattn.so (once) and declare its C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with __graft_entry__.build() (hipcc, gfx950)")
+    lib = ctypes.CDLL(path)
+    i64, vp, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+    lib.tri_attn_status_string.argtypes = [ctypes.c_int]
+    lib.tri_attn_status_string.restype = ctypes.c_char_p
+    for name in ("tri_attn_fwd_workspace_bytes", "tri_attn_bwd_workspace_bytes"):
+        f = getattr(lib, name)
+        f.argtypes = [i64, i64, i64, i64]
+        f.restype = sz
+    lib.tri_attn_fwd.argtypes = [i64, i64, i64, i64] + [vp] * 8 + [vp, sz, vp]
+    lib.tri_attn_fwd.restype = ctypes.c_int
+    lib.tri_attn_bwd.argtypes = [i64, i64, i64, i64] + [vp] * 13 + [vp, sz, vp]
+    lib.tri_attn_bwd.restype = ctypes.c_int
+    lib.tri_attn_fwd_stages.argtypes = [ctypes.c_uint] + lib.tri_attn_fwd.argtypes
+    lib.tri_attn_fwd_stages.restype = ctypes.c_int
+    lib.tri_attn_bwd_stages.argtypes = [ctypes.c_uint] + lib.tri_attn_bwd.argtypes
+    lib.tri_attn_bwd_stages.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream if isinstance(stream, int) else stream.cuda_stream
+
+
+def tri_attn_status_string(status: int) -> str:
+    return load_library().tri_attn_status_string(int(status)).decode()
+
+
+def tri_attn_fwd_workspace_bytes(B: int, N: int, H: int, D: int) -> int:
+    return int(load_library().tri_attn_fwd_workspace_bytes(B, N, H, D))
+
+
+def tri_attn_bwd_workspace_bytes(B: int, N: int, H: int, D: int) -> int:
+    return int(load_library().tri_attn_bwd_workspace_bytes(B, N, H, D))
+
+
+def tri_attn_fwd(B, N, H, D, q, k, v, bias, key_mask, o, lse, residual, workspace, workspace_bytes,
+                 stream=None) -> int:
+    """Marshal to the C entry point; returns the status code (0 = success)."""
+    return int(load_library().tri_attn_fwd(B, N, H, D, _ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(key_mask),
+                                           _ptr(o), _ptr(lse), _ptr(residual), _ptr(workspace),
+                                           int(workspace_bytes), _stream(stream)))
+
+
+def tri_attn_bwd(B, N, H, D, q, k, v, bias, key_mask, o, lse, residual, dO, dq, dk, dv, dbias, workspace,
+                 workspace_bytes, stream=None) -> int:
+    """Marshal to the C entry point; returns the status code (0 = success)."""
+    return int(load_library().tri_attn_bwd(B, N, H, D, _ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(key_mask),
+                                           _ptr(o), _ptr(lse), _ptr(residual), _ptr(dO), _ptr(dq), _ptr(dk),
+                                           _ptr(dv), _ptr(dbias), _ptr(workspace), int(workspace_bytes),
+                                           _stream(stream)))
+
+
+STAGE_PREP, STAGE_MAIN, STAGE_FINAL, STAGE_ALL = 1, 2, 4, 7
+
+
+def tri_attn_fwd_stages(stages, B, N, H, D, q, k, v, bias, key_mask, o, lse, residual, workspace, workspace_bytes,
+                        stream=None) -> int:
+    return int(load_library().tri_attn_fwd_stages(stages, B, N, H, D, _ptr(q), _ptr(k), _ptr(v), _ptr(bias),
+                                                  _ptr(key_mask), _ptr(o), _ptr(lse), _ptr(residual),
+                                                  _ptr(workspace), int(workspace_bytes), _stream(stream)))
+
+
+def tri_attn_bwd_stages(stages, B, N, H, D, q, k, v, bias, key_mask, o, lse, residual, dO, dq, dk, dv, dbias,
+                        workspace, workspace_bytes, stream=None) -> int:
+    return int(load_library().tri_attn_bwd_stages(stages, B, N, H, D, _ptr(q), _ptr(k), _ptr(v), _ptr(bias),
+                                                  _ptr(key_mask), _ptr(o), _ptr(lse), _ptr(residual), _ptr(dO),
+                                                  _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbias), _ptr(workspace),
+                                                  int(workspace_bytes), _stream(stream)))
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise TriAttnError(status, where)
+
+
+def _shape(q):
+    if q.dim() != 5:
+        raise ValueError("q must be [B, N, H, N, D]")
+    B, N, H, N2, D = q.shape
+    if N2 != N:
+        raise ValueError("q must be [B, N, H, N, D] with equal slice and token extents")
+    return B, N, H, D
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+
+
+def forward(q, k, v, bias, key_mask=None, residual_compensation=True):
+    """Returns (o, lse, residual-or-None).  Tensors must be contiguous bf16 (mask uint8) on one GPU."""
+    B, N, H, D = _shape(q)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, N, H, N), dtype=torch.float32, device=q.device)
+    res = torch.empty_like(q) if residual_compensation else None
+    nws = tri_attn_fwd_workspace_bytes(B, N, H, D)
+    ws = _workspace(nws, q.device)
+    _check(tri_attn_fwd(B, N, H, D, q, k, v, bias, key_mask, o, lse, res, ws, ws.numel()), "tri_attn_fwd")
+    return o, lse, res
+
+
+def backward(q, k, v, bias, key_mask, o, lse, residual, dO):
+    """Returns (dq, dk, dv, dbias) with dbias in float32."""
+    B, N, H, D = _shape(q)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dbias = torch.empty((B, H, N, N), dtype=torch.float32, device=q.device)
+    nws = tri_attn_bwd_workspace_bytes(B, N, H, D)
+    ws = _workspace(nws, q.device)
+    _check(tri_attn_bwd(B, N, H, D, q, k, v, bias, key_mask, o, lse, residual, dO, dq, dk, dv, dbias, ws,
+                        ws.numel()), "tri_attn_bwd")
+    return dq, dk, dv, dbias
+
+
+class _TriAttnFn(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, bias, key_mask, residual_compensation):
+        o, lse, res = forward(q, k, v, bias, key_mask, residual_compensation)
+        ctx.save_for_backward(q, k, v, bias, o, lse, res, key_mask)
+        return o
+
+    @staticmethod
+    def backward(ctx, dO):
+        q, k, v, bias, o, lse, res, key_mask = ctx.saved_tensors
+        dq, dk, dv, dbias = backward(q, k, v, bias, key_mask, o, lse, res, dO.contiguous())
+        return dq, dk, dv, dbias.to(bias.dtype), None, None
+
+
+def triangle_attention(q, k, v, bias, key_mask=None, residual_compensation=True):
+    """Starting-node triangle attention, differentiable in q, k, v and the shared bias.
+
+    q, k, v: bf16 [B, N, H, N, D]; bias: bf16 [B, H, N, N]; key_mask: uint8 [B, N, N] or None.
+    """
+    return _TriAttnFn.apply(q, k, v, bias, key_mask, residual_compensation)

@@ -1,0 +1,802 @@
+// Triangle attention (starting node), forward and backward, for AMD gfx950 (MI355X).
+//
+// Method: "TurboPairFormer: Fast and Stable Protein Folding Model Training with an
+// Optimized Triangle Attention Kernel" (arXiv 2610.05854), Abstract.  Per batch b,
+// slice i and head h:  o[j] = sum_k softmax_k(alpha q[j].k[k] + bias[j,k] + m[k]) v[k],
+// with the pair bias shared across all slices.  The backward is key-tile parallel: each
+// probability tile is recomputed once and feeds all four gradients; dq (a sum over key
+// blocks) and dbias (a sum over slices) go through ordered partial buffers, so there
+// are no floating-point atomics and the results are bitwise reproducible.  The
+// forward stores a bf16 copy of the output-rounding residual so that the softmax
+// backward correction D = rowsum(dO * o) can be formed in FP32 (output-residual
+// compensation, same Abstract).
+//
+// Hardware mapping (gfx950):
+//  * QK^T and PV (and the five backward products) run on v_mfma_f32_32x32x16_bf16 /
+//    v_mfma_f32_16x16x32_bf16 with FP32 accumulation.
+//  * Operands whose contraction index is the token index (V in PV, Q/dO in dK/dV, K and
+//    dS in dQ) are read from LDS with ds_read_b64_tr_b16, which hands each lane four
+//    consecutive rows of one column.
+//  * The pair bias is pre-scaled to FP32 (bias / alpha) in a tile order that matches the
+//    MFMA accumulator layout, and is loaded straight into the accumulator before the
+//    QK^T product, so adding it costs no vector ALU work.  Padding rows/columns hold
+//    -inf, which turns every out-of-range key or query into an exact zero probability.
+//  * Work-groups are numbered so that consecutive ids land on the same XCD (dispatch is
+//    round-robin over the 8 XCDs), keeping one head's bias and the tiles shared by
+//    neighbouring work-groups in that XCD's L2.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+#include <math.h>
+
+#include "tri_attn.h"
+
+namespace {
+
+typedef __bf16 bf16;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kMaskNeg = -1e9f;  // additive score term of a masked key
+constexpr int kXcd = 8;            // XCDs per MI355X; dispatch is round-robin over them
+
+// ------------------------------------------------------------------ small helpers
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 zero8() {
+  bf16x8 z;
+#pragma unroll
+  for (int i = 0; i < 8; i++) z[i] = (bf16)0.0f;
+  return z;
+}
+
+typedef __attribute__((address_space(3))) bf16 lbf16;
+typedef __attribute__((address_space(3))) float lf32;
+typedef __attribute__((address_space(3))) bf16x8 lbf16x8;
+typedef __attribute__((address_space(3))) bf16x4 lbf16x4;
+typedef __attribute__((address_space(3))) f32x4 lf32x4;
+typedef __attribute__((address_space(3))) s16x4 ls16x4;
+
+// Lane part of a transposed read: lane t of a 16-lane group addresses row t/4 and
+// column 4*(t%4) of the 4x16 block it helps to load.
+__device__ __forceinline__ int tr_lane(int ld) {
+  const int t = threadIdx.x & 15;
+  return (t >> 2) * ld + 4 * (t & 3);
+}
+// ds_read_b64_tr_b16 at an LDS address that already contains the lane part: with
+// p = &X[r0][c0] + tr_lane(ld), lane t of each 16-lane group receives X[r0+e][c0+t], e = 0..3.
+__device__ __forceinline__ s16x4 tr16p(const lbf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((ls16x4*)p);
+}
+
+// Transposed LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes, lane t
+// receives X[r0 + e][c0 + t] for e = 0..3, where X is a row-major bf16 matrix in LDS
+// with leading dimension ld (elements).  r0, c0 must be uniform over the 16-lane group.
+__device__ __forceinline__ s16x4 tr16(const bf16* X, int ld, int r0, int c0) {
+  const int t = threadIdx.x & 15;
+  const bf16* p = X + (r0 + (t >> 2)) * ld + c0 + 4 * (t & 3);
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+}
+__device__ __forceinline__ bf16x8 cat8(s16x4 a, s16x4 b) {
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+__device__ __forceinline__ bf16x8 pack8(const float* f) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; i++) r[i] = (bf16)f[i];
+  return r;
+}
+
+// Work-group id -> logical tile, so that tiles [x*per, (x+1)*per) run on XCD x.
+__device__ __forceinline__ int64_t xcd_tile(int64_t ntiles) {
+  const int64_t per = (ntiles + kXcd - 1) / kXcd;
+  return (int64_t)(blockIdx.x % kXcd) * per + blockIdx.x / kXcd;
+}
+
+__host__ __device__ constexpr int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+// Offset of element (m, n) inside a 32x32 FP32 tile stored in "accumulator order":
+// lane n%32 of lane-group g reads 16 contiguous bytes holding rows 8R+4g+0..3.
+__host__ __device__ __forceinline__ int64_t ctile_off(int m, int n) {
+  const int R = m >> 3, g = (m >> 2) & 1, e = m & 3;
+  return ((int64_t)((R * 2 + g) * 32 + n)) * 4 + e;
+}
+
+// ------------------------------------------------------------------ bias preparation
+// biasF: forward operand, tiles indexed (b,h, jb, kb), element (row m = key k%32,
+// column n = query j%32); value bias[b,h,j,k]/alpha, -inf for k >= N.
+// biasT: backward operand, tiles (b,h, kb, jb), element (row m = query, column n = key);
+// value bias[b,h,j,k]/alpha, -inf if j >= N or k >= N.
+__global__ void bias_prep_kernel(const bf16* __restrict__ bias, float* __restrict__ out, int N,
+                                 int Rp, int Cp, bool fwd, float inv_alpha, int64_t total) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= total) return;
+  // decode idx -> (bh, rb, cb, in-tile offset); tiles are 32x32 over (row block rb, col block cb)
+  const int64_t tile = idx >> 10;
+  const int off = (int)(idx & 1023);
+  const int e = off & 3, n = (off >> 2) & 31, Rg = off >> 7;  // Rg = R*2+g
+  const int m = (Rg >> 1) * 8 + (Rg & 1) * 4 + e;
+  const int ncb = Cp / 32, nrb = Rp / 32;
+  const int cb = (int)(tile % ncb);
+  const int rb = (int)((tile / ncb) % nrb);
+  const int64_t bh = tile / ((int64_t)ncb * nrb);
+  // forward tiles: rows = query blocks (rb), inside a tile row m = key, column n = query
+  // backward tiles: rows = key blocks (rb), inside a tile row m = query, column n = key
+  int j, k;
+  if (fwd) { j = rb * 32 + n; k = cb * 32 + m; }
+  else     { k = rb * 32 + n; j = cb * 32 + m; }
+  float val;
+  if (k >= N) val = -INFINITY;
+  else if (j >= N) val = fwd ? 0.0f : -INFINITY;
+  else val = (float)bias[(bh * N + j) * N + k] * inv_alpha;
+  out[idx] = val;
+}
+
+// ------------------------------------------------------------------ forward
+// One work-group = 4 waves = 128 queries of one slice (b,i,h); wave w owns 32 queries.
+// S^T (keys x queries) = K Q^T on 32x32x16 MFMA: each lane holds one query column and
+// 16 keys per 32-key tile, so the running max/sum of a query needs one cross-lane step.
+template <int D, bool MASK>
+__global__ __launch_bounds__(256, 2)
+void fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+                const float* __restrict__ biasF, const uint8_t* __restrict__ mask,
+                bf16* __restrict__ o, float* __restrict__ lse, bf16* __restrict__ res,
+                int B, int N, int H, float alpha) {
+  constexpr int KT = 64;        // keys per iteration
+  constexpr int NC = D / 16;    // 16-wide channel chunks
+  __shared__ __attribute__((aligned(16))) bf16 Ks[KT * D];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[KT * D];
+  __shared__ __attribute__((aligned(16))) uint8_t Ms[KT];
+
+  const int QT = (N + 127) / 128;
+  const int64_t ntiles = (int64_t)B * H * N * QT;
+  const int64_t tile = xcd_tile(ntiles);
+  if (tile >= ntiles) return;
+  const int qt = (int)(tile % QT);
+  int64_t rest = tile / QT;
+  const int i = (int)(rest % N); rest /= N;
+  const int h = (int)(rest % H);
+  const int b = (int)(rest / H);
+
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 5, ln = l & 31;
+  const int64_t sbase = (((int64_t)b * N + i) * H + h) * (int64_t)N * D;
+  const int j = qt * 128 + w * 32 + ln;  // this lane's query
+  const bool jok = j < N;
+  const int Kp = (int)round_up(N, 64), Jp = (int)round_up(N, 128);
+  const float* btile = biasF + ((int64_t)(b * H + h) * (Jp / 32) + (qt * 4 + w)) * (int64_t)(Kp / 32) * 1024;
+  const float c1 = alpha * kLog2e;
+  const float mneg = kMaskNeg / alpha;
+
+  bf16x8 qf[NC];
+#pragma unroll
+  for (int cc = 0; cc < NC; cc++)
+    qf[cc] = jok ? *(const bf16x8*)(q + sbase + (int64_t)j * D + cc * 16 + g * 8) : zero8();
+
+  f32x16 acc_o = {};
+  float m_run = -INFINITY, l_run = 0.0f;
+
+  const int nkt = (N + KT - 1) / KT;
+  for (int kt = 0; kt < nkt; kt++) {
+    const int k0 = kt * KT;
+    // stage K and V tiles (zero beyond N) and the mask bytes
+    for (int c = tid; c < KT * D / 8; c += 256) {
+      const int r = c / (D / 8), col = (c % (D / 8)) * 8;
+      bf16x8 kv = zero8(), vv = zero8();
+      if (k0 + r < N) {
+        kv = *(const bf16x8*)(k + sbase + (int64_t)(k0 + r) * D + col);
+        vv = *(const bf16x8*)(v + sbase + (int64_t)(k0 + r) * D + col);
+      }
+      *(bf16x8*)(Ks + r * D + col) = kv;
+      *(bf16x8*)(Vs + r * D + col) = vv;
+    }
+    if (MASK && tid < KT) Ms[tid] = (k0 + tid < N) ? mask[((int64_t)b * N + i) * N + k0 + tid] : (uint8_t)1;
+    __syncthreads();
+
+    f32x16 s[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; tt++) {
+      const float* bt = btile + (int64_t)(kt * 2 + tt) * 1024;
+#pragma unroll
+      for (int R = 0; R < 4; R++) {
+        const f32x4 bv = *(const f32x4*)(bt + ((R * 2 + g) * 32 + ln) * 4);
+        s[tt][R * 4 + 0] = bv[0]; s[tt][R * 4 + 1] = bv[1];
+        s[tt][R * 4 + 2] = bv[2]; s[tt][R * 4 + 3] = bv[3];
+      }
+#pragma unroll
+      for (int cc = 0; cc < NC; cc++) {
+        const bf16x8 a = *(const bf16x8*)(Ks + (tt * 32 + ln) * D + cc * 16 + g * 8);
+        s[tt] = mfma32(a, qf[cc], s[tt]);
+      }
+      if (MASK) {
+#pragma unroll
+        for (int R = 0; R < 4; R++) {
+#pragma unroll
+          for (int e = 0; e < 4; e++)
+            if (!Ms[tt * 32 + R * 8 + g * 4 + e]) s[tt][R * 4 + e] += mneg;
+        }
+      }
+    }
+    // running max over this lane's 32 scores, then across the lane pair (l, l^32)
+    float mx = s[0][0];
+#pragma unroll
+    for (int r = 1; r < 16; r++) mx = fmaxf(mx, s[0][r]);
+#pragma unroll
+    for (int r = 0; r < 16; r++) mx = fmaxf(mx, s[1][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float scale = __builtin_amdgcn_exp2f((m_run - m_new) * c1);
+    const float nm = m_new * c1;
+    m_run = m_new;
+    float p[2][16];
+    float lsum = 0.0f;
+#pragma unroll
+    for (int tt = 0; tt < 2; tt++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        p[tt][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[tt][r], c1, -nm));
+        lsum += p[tt][r];
+      }
+    l_run = l_run * scale + lsum;
+#pragma unroll
+    for (int r = 0; r < 16; r++) acc_o[r] *= scale;
+
+    // O^T (channels x queries) += V^T P^T; lane group (l/16) selects channel half and key run
+    const int G16 = l >> 4, chalf = G16 & 1;
+#pragma unroll
+    for (int tt = 0; tt < 2; tt++)
+#pragma unroll
+      for (int m2 = 0; m2 < 2; m2++) {
+        const bf16x8 pb = pack8(&p[tt][m2 * 8]);
+        const int r0 = tt * 32 + m2 * 16 + g * 4;
+        bf16x8 a;
+        if (D == 32 || chalf == 0) {
+          a = cat8(tr16(Vs, D, r0, chalf * 16), tr16(Vs, D, r0 + 8, chalf * 16));
+        } else {
+          a = zero8();
+        }
+        acc_o = mfma32(a, pb, acc_o);
+      }
+    __syncthreads();
+  }
+
+  // epilogue: normalise, round, residual, logsumexp
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = 1.0f / l_tot;
+  if (jok) {
+    bf16* orow = o + sbase + (int64_t)j * D;
+    bf16* rrow = res ? res + sbase + (int64_t)j * D : nullptr;
+#pragma unroll
+    for (int R = 0; R < D / 8; R++) {
+      bf16x4 ob, rb;
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const float f = acc_o[R * 4 + e] * inv;
+        const bf16 fb = (bf16)f;
+        ob[e] = fb;
+        rb[e] = (bf16)(f - (float)fb);
+      }
+      const int c = R * 8 + g * 4;
+      *(bf16x4*)(orow + c) = ob;
+      if (rrow) *(bf16x4*)(rrow + c) = rb;
+    }
+    if (g == 0) lse[(((int64_t)b * N + i) * H + h) * N + j] = m_run * alpha + logf(l_tot);
+  }
+}
+
+// ------------------------------------------------------------------ backward: correction D
+// D[b,i,h,j] = sum_c dO * (o + residual) in FP32 (or dO * o without a residual).
+template <int D>
+__global__ __launch_bounds__(256)
+void bwd_pre_kernel(const bf16* __restrict__ dO, const bf16* __restrict__ o, const bf16* __restrict__ res,
+                    float* __restrict__ Dout, int64_t rows) {
+  const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= rows) return;
+  float acc = 0.0f;
+#pragma unroll
+  for (int c8 = 0; c8 < D / 8; c8++) {
+    const bf16x8 a = *(const bf16x8*)(dO + r * D + c8 * 8);
+    const bf16x8 ov = *(const bf16x8*)(o + r * D + c8 * 8);
+    if (res) {
+      const bf16x8 rv = *(const bf16x8*)(res + r * D + c8 * 8);
+#pragma unroll
+      for (int e = 0; e < 8; e++) acc = __builtin_fmaf((float)a[e], (float)ov[e] + (float)rv[e], acc);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; e++) acc = __builtin_fmaf((float)a[e], (float)ov[e], acc);
+    }
+  }
+  Dout[r] = acc;
+}
+
+// ------------------------------------------------------------------ backward: main
+// One work-group = 8 waves = one block of 64 keys of head h, for a group of G slices.
+// wave w: key half kh = w&1 (32 keys), query lane p = w>>1.  Per slice the queries are
+// walked in steps of 128 (4 tiles of 32, tile p to query lane p).  Each wave keeps the
+// pair-bias gradient of its (query tiles x 32 keys) in registers across the slice group
+// ("face"), so dS is summed over slices on chip and written once per group.
+constexpr int kBwdMaxSteps = 6;  // 6 steps x 128 queries = TRI_ATTN_MAX_N
+
+template <int D, bool MASK>
+__global__ __launch_bounds__(512, 1)
+void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+                const bf16* __restrict__ dO, const float* __restrict__ biasT, const uint8_t* __restrict__ mask,
+                const float* __restrict__ lse, const float* __restrict__ Dg,
+                float* __restrict__ dqp, float* __restrict__ dbp, bf16* __restrict__ dk, bf16* __restrict__ dv,
+                int B, int N, int H, int G, int ngroups, float alpha) {
+  constexpr int NC = D / 16;
+  constexpr int LDT = 128 + 8;  // dS^T row stride (elements), padded
+  constexpr int NR = D / 2;     // accumulator registers of dK^T / dV^T holding channels c < D
+  __shared__ __attribute__((aligned(16))) bf16 Ks_[64 * D];
+  __shared__ __attribute__((aligned(16))) bf16 Vs_[64 * D];
+  __shared__ __attribute__((aligned(16))) bf16 Qs_[128 * D];
+  __shared__ __attribute__((aligned(16))) bf16 dOs_[128 * D];
+  __shared__ __attribute__((aligned(16))) float lseS_[128];
+  __shared__ __attribute__((aligned(16))) float DS_[128];
+  __shared__ __attribute__((aligned(16))) bf16 dST_[64 * LDT];
+  __shared__ __attribute__((aligned(16))) float red_[8 * 2 * NR * 64];
+  lbf16* Ks = (lbf16*)Ks_;
+  lbf16* Vs = (lbf16*)Vs_;
+  lbf16* Qs = (lbf16*)Qs_;
+  lbf16* dOs = (lbf16*)dOs_;
+  lf32* lseS = (lf32*)lseS_;
+  lf32* DS = (lf32*)DS_;
+  lbf16* dST = (lbf16*)dST_;
+  lf32* red = (lf32*)red_;
+
+  const int KB = (N + 63) / 64;
+  const int64_t ntiles = (int64_t)B * H * ngroups * KB;
+  const int64_t tile = xcd_tile(ntiles);
+  if (tile >= ntiles) return;
+  const int kb = (int)(tile % KB);
+  int64_t rest = tile / KB;
+  const int grp = (int)(rest % ngroups); rest /= ngroups;
+  const int h = (int)(rest % H);
+  const int b = (int)(rest / H);
+  const int i_begin = grp * G, i_end = min(N, i_begin + G);
+
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 5, ln = l & 31;
+  const int kh = w & 1, p = w >> 1;
+  const int G16 = l >> 4, chalf = G16 & 1;
+  const int kl = kh * 32 + ln;          // key within the block
+  const int kg = kb * 64 + kl;          // global key of this lane
+  const bool kok = kg < N;
+  const int Kp = (int)round_up(N, 64), Jp = (int)round_up(N, 128);
+  const float* bT = biasT + ((int64_t)(b * H + h) * (Kp / 32) + (kb * 2 + kh)) * (int64_t)(Jp / 32) * 1024;
+  const float c1 = alpha * kLog2e;
+  const float mneg = kMaskNeg / alpha;
+  const int64_t slice_elems = (int64_t)N * D;
+  const int64_t dq_stride = (int64_t)B * N * H * slice_elems;  // one full dq partial
+
+  // per-lane LDS bases (element offsets); loop-varying parts are compile-time immediates
+  const int trl_d = tr_lane(D), trl_t = tr_lane(LDT);
+  // dV^T/dK^T A operands: rows (queries) p*32 + 4g (+16 m2, +8), channels 16*chalf
+  const int base_qo = (p * 32 + 4 * g) * D + (D == 32 ? 16 * chalf : 0) + trl_d;
+  // dQ^T tiles of this wave: channel tile ct = u, query sub-tile js = w&1 of query tile jt = w>>1
+  const int base_kT = 8 * G16 * D + trl_d;
+  const int base_sT = 8 * G16 * LDT + (w >> 1) * 32 + (w & 1) * 16 + trl_t;
+  const int base_red_w = w * (2 * NR * 64) + l;
+  const int base_red_r = kh * (2 * NR * 64) + p * ((2 * NR) / 4) * 64 + l;
+
+  f32x16 face[kBwdMaxSteps];
+#pragma unroll
+  for (int s = 0; s < kBwdMaxSteps; s++) face[s] = f32x16{};
+
+  for (int i = i_begin; i < i_end; i++) {
+    const int64_t sbase = (((int64_t)b * N + i) * H + h) * slice_elems;
+    const int64_t rbase = (((int64_t)b * N + i) * H + h) * (int64_t)N;
+    // uniform per-slice bases; lane offsets below are 32-bit
+    const bf16* ks = k + sbase + (int64_t)kb * 64 * D;
+    const bf16* vs = v + sbase + (int64_t)kb * 64 * D;
+    const bf16* qsl = q + sbase;
+    const bf16* dos = dO + sbase;
+    const float* lsl = lse + rbase;
+    const float* dsl = Dg + rbase;
+    float* dqs = dqp + (int64_t)kb * dq_stride + sbase;
+    // K and V blocks into LDS (zero beyond N): K/V rows feed S and dP, K^T feeds dQ
+    for (int c = tid; c < 64 * D / 8; c += 512) {
+      const int r = c / (D / 8), col = (c % (D / 8)) * 8;
+      bf16x8 kv = zero8(), vv = zero8();
+      if (kb * 64 + r < N) {
+        kv = *(const bf16x8*)(ks + r * D + col);
+        vv = *(const bf16x8*)(vs + r * D + col);
+      }
+      *(lbf16x8*)(Ks + r * D + col) = kv;
+      *(lbf16x8*)(Vs + r * D + col) = vv;
+    }
+    float madd = 0.0f;
+    if (MASK && kok && !mask[((int64_t)b * N + i) * N + kg]) madd = mneg;
+    f32x16 dkT = {}, dvT = {};
+
+    const int nsteps = (N + 127) / 128;
+#pragma unroll 1
+    for (int s = 0; s < nsteps; s++) {
+      const int j0 = s * 128;
+      __syncthreads();  // previous users of Qs/dOs/dST/lseS are done; K/V staged
+      for (int c = tid; c < 128 * D / 8; c += 512) {
+        const int r = c / (D / 8), col = (c % (D / 8)) * 8;
+        bf16x8 qv = zero8(), ov = zero8();
+        if (j0 + r < N) {
+          qv = *(const bf16x8*)(qsl + (j0 + r) * D + col);
+          ov = *(const bf16x8*)(dos + (j0 + r) * D + col);
+        }
+        *(lbf16x8*)(Qs + r * D + col) = qv;
+        *(lbf16x8*)(dOs + r * D + col) = ov;
+      }
+      if (tid < 128) lseS[tid] = (j0 + tid < N) ? lsl[j0 + tid] * kLog2e : 0.0f;
+      else if (tid < 256) DS[tid - 128] = (j0 + tid - 128 < N) ? dsl[j0 + tid - 128] : 0.0f;
+      __syncthreads();
+
+      // S = bias/alpha + Q K^T  and  dP = dO V^T   (rows: 32 queries, cols: 32 keys)
+      f32x16 sacc, dp = {};
+      const float* bt = bT + (int64_t)(s * 4 + p) * 1024;
+#pragma unroll
+      for (int R = 0; R < 4; R++) {
+        const f32x4 bv = *(const f32x4*)(bt + ((R * 2 + g) * 32 + ln) * 4);
+        sacc[R * 4 + 0] = bv[0]; sacc[R * 4 + 1] = bv[1];
+        sacc[R * 4 + 2] = bv[2]; sacc[R * 4 + 3] = bv[3];
+      }
+#pragma unroll
+      for (int cc = 0; cc < NC; cc++) {
+        const bf16x8 aq = *(const lbf16x8*)(Qs + (p * 32 + ln) * D + cc * 16 + g * 8);
+        const bf16x8 kf = *(const lbf16x8*)(Ks + kl * D + cc * 16 + g * 8);
+        sacc = mfma32(aq, kf, sacc);
+        const bf16x8 ao = *(const lbf16x8*)(dOs + (p * 32 + ln) * D + cc * 16 + g * 8);
+        const bf16x8 vf = *(const lbf16x8*)(Vs + kl * D + cc * 16 + g * 8);
+        dp = mfma32(ao, vf, dp);
+      }
+      float P[16], dS[16];
+#pragma unroll
+      for (int R = 0; R < 4; R++) {
+        const f32x4 lv = *(const lf32x4*)(lseS + p * 32 + R * 8 + g * 4);
+        const f32x4 dd = *(const lf32x4*)(DS + p * 32 + R * 8 + g * 4);
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          const int r = R * 4 + e;
+          float x = sacc[r];
+          if (MASK) x += madd;
+          P[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(x, c1, -lv[e]));
+          dS[r] = P[r] * (dp[r] - dd[e]);
+        }
+      }
+      // the face slot is selected by a uniform switch so that its registers stay statically indexed
+      switch (s) {
+#define TRI_FACE_ADD(S_)                                                  \
+  case S_:                                                                \
+    _Pragma("unroll") for (int r = 0; r < 16; r++) face[S_][r] += dS[r]; \
+    break;
+        TRI_FACE_ADD(0) TRI_FACE_ADD(1) TRI_FACE_ADD(2) TRI_FACE_ADD(3) TRI_FACE_ADD(4) TRI_FACE_ADD(5)
+#undef TRI_FACE_ADD
+        default: break;
+      }
+      static_assert(kBwdMaxSteps == 6, "face switch covers 6 slots");
+
+      // dV^T += dO^T P ; dK^T += Q^T dS   (rows: channels, cols: keys)
+#pragma unroll
+      for (int m2 = 0; m2 < 2; m2++) {
+        const bf16x8 pb = pack8(&P[m2 * 8]);
+        const bf16x8 sb = pack8(&dS[m2 * 8]);
+        bf16x8 ao, aq;
+        if (D == 32 || chalf == 0) {
+          ao = cat8(tr16p(dOs + base_qo + m2 * 16 * D), tr16p(dOs + base_qo + (m2 * 16 + 8) * D));
+          aq = cat8(tr16p(Qs + base_qo + m2 * 16 * D), tr16p(Qs + base_qo + (m2 * 16 + 8) * D));
+        } else {
+          ao = zero8();
+          aq = zero8();
+        }
+        dvT = mfma32(ao, pb, dvT);
+        dkT = mfma32(aq, sb, dkT);
+      }
+      // dS^T (keys x queries) to LDS for the dQ product
+#pragma unroll
+      for (int R = 0; R < 4; R++) {
+        bf16x4 t4;
+#pragma unroll
+        for (int e = 0; e < 4; e++) t4[e] = (bf16)dS[R * 4 + e];
+        *(lbf16x4*)(dST + kl * LDT + p * 32 + R * 8 + g * 4) = t4;
+      }
+      __syncthreads();
+      // dQ^T tiles (16 channels x 16 queries) over the 64 keys of this block
+      const int jj = j0 + (w >> 1) * 32 + (w & 1) * 16 + (l & 15);
+#pragma unroll
+      for (int u = 0; u < NC; u++) {
+        f32x4 c = {};
+#pragma unroll
+        for (int kk = 0; kk < 64; kk += 32) {
+          const bf16x8 a = cat8(tr16p(Ks + base_kT + kk * D + u * 16), tr16p(Ks + base_kT + (kk + 4) * D + u * 16));
+          const bf16x8 bb = cat8(tr16p(dST + base_sT + kk * LDT), tr16p(dST + base_sT + (kk + 4) * LDT));
+          c = mfma16(a, bb, c);
+        }
+        if (jj < N) *(f32x4*)(dqs + jj * D + u * 16 + 4 * G16) = c;
+      }
+    }
+    // reduce dK^T, dV^T over the 4 query lanes in fixed order; query lane p finishes a quarter
+#pragma unroll
+    for (int r = 0; r < NR; r++) {
+      red[base_red_w + r * 64] = dkT[r];
+      red[base_red_w + (NR + r) * 64] = dvT[r];
+    }
+    __syncthreads();
+    {
+      constexpr int PER = (2 * NR) / 4;  // registers finished by each query lane
+#pragma unroll
+      for (int u = 0; u < PER; u++) {
+        float sum = red[base_red_r + u * 64];
+        sum += red[base_red_r + 1 * (4 * NR * 64) + u * 64];
+        sum += red[base_red_r + 2 * (4 * NR * 64) + u * 64];
+        sum += red[base_red_r + 3 * (4 * NR * 64) + u * 64];
+        const int rr = p * PER + u;  // 0 .. 2*NR-1: dK^T registers first, then dV^T
+        const bool isv = rr >= NR;
+        const int r = isv ? rr - NR : rr;
+        const int c = (r >> 2) * 8 + g * 4 + (r & 3);
+        if (kok) {
+          bf16* dst = (isv ? dv : dk) + sbase;
+          dst[kg * D + c] = (bf16)(isv ? sum : sum * alpha);
+        }
+      }
+    }
+  }
+  // write this group's pair-bias gradient partial: dbp[grp][b][h][j][k]
+  float* dst = dbp + (((int64_t)grp * B + b) * H + h) * (int64_t)N * N;
+#pragma unroll
+  for (int s = 0; s < kBwdMaxSteps; s++) {
+    if (s * 128 < N) {
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const int jj = s * 128 + p * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
+        if (jj < N && kok) dst[(int64_t)jj * N + kg] = face[s][r];
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ backward: ordered sums
+// dq = bf16(alpha * sum_kb dqp[kb]) with kb ascending; dbias = sum_g dbp[g] with g ascending.
+__global__ __launch_bounds__(256)
+void reduce_dq_kernel(const float* __restrict__ dqp, bf16* __restrict__ dq, int KB, int64_t n4, float alpha) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= n4) return;
+  f32x4 s = *(const f32x4*)(dqp + t * 4);
+  for (int kb = 1; kb < KB; kb++) {
+    const f32x4 x = *(const f32x4*)(dqp + (int64_t)kb * n4 * 4 + t * 4);
+    s += x;
+  }
+  bf16x4 r;
+#pragma unroll
+  for (int e = 0; e < 4; e++) r[e] = (bf16)(s[e] * alpha);
+  *(bf16x4*)(dq + t * 4) = r;
+}
+
+__global__ __launch_bounds__(256)
+void reduce_dbias_kernel(const float* __restrict__ dbp, float* __restrict__ dbias, int ngroups, int64_t n) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= n) return;
+  float s = dbp[t];
+  for (int g = 1; g < ngroups; g++) s += dbp[(int64_t)g * n + t];
+  dbias[t] = s;
+}
+
+// ------------------------------------------------------------------ host side
+
+struct Plan {
+  int64_t B, N, H, D;
+  int64_t Kp, Jp;           // padded key / query extents of the prepared bias
+  int64_t KB;               // 64-key blocks
+  int64_t ngroups, G;       // slice groups of the backward and slices per group
+  int64_t elems;            // B*N*H*N*D
+  int64_t rows;             // B*N*H*N
+  int64_t bias_f32_bytes;   // prepared bias (either layout)
+  int64_t off_D, off_dqp, off_dbp, bwd_bytes;
+};
+
+constexpr int64_t kAlign = 256;
+
+bool shape_ok(int64_t B, int64_t N, int64_t H, int64_t D) {
+  return B >= 1 && N >= 1 && H >= 1 && (D == 16 || D == 32) && N <= TRI_ATTN_MAX_N && B <= (1 << 20) &&
+         H <= (1 << 12);
+}
+
+Plan make_plan(int64_t B, int64_t N, int64_t H, int64_t D) {
+  Plan p{};
+  p.B = B; p.N = N; p.H = H; p.D = D;
+  p.Kp = round_up(N, 64);
+  p.Jp = round_up(N, 128);
+  p.KB = (N + 63) / 64;
+  // enough (b, h, key block, slice group) work-groups for ~3 per CU, with as few groups
+  // (pair-bias partials) as that allows
+  const int64_t per_group = B * H * p.KB;
+  int64_t groups = (768 + per_group - 1) / per_group;
+  if (groups < 1) groups = 1;
+  if (groups > N) groups = N;
+  p.G = (N + groups - 1) / groups;
+  p.ngroups = (N + p.G - 1) / p.G;
+  p.elems = B * N * H * N * D;
+  p.rows = B * N * H * N;
+  p.bias_f32_bytes = round_up(B * H * p.Kp * p.Jp * 4, kAlign);
+  p.off_D = p.bias_f32_bytes;
+  p.off_dqp = p.off_D + round_up(p.rows * 4, kAlign);
+  p.off_dbp = p.off_dqp + round_up(p.KB * p.elems * 4, kAlign);
+  p.bwd_bytes = p.off_dbp + round_up(p.ngroups * B * H * N * N * 4, kAlign);
+  return p;
+}
+
+bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+struct Range { const void* p; int64_t n; bool out; };
+
+bool overlaps(const Range* r, int n) {
+  for (int a = 0; a < n; a++) {
+    if (!r[a].p || r[a].n <= 0) continue;
+    for (int c = a + 1; c < n; c++) {
+      if (!r[c].p || r[c].n <= 0) continue;
+      if (!r[a].out && !r[c].out) continue;  // inputs may alias each other
+      const uintptr_t a0 = (uintptr_t)r[a].p, a1 = a0 + (uintptr_t)r[a].n;
+      const uintptr_t c0 = (uintptr_t)r[c].p, c1 = c0 + (uintptr_t)r[c].n;
+      if (a0 < c1 && c0 < a1) return true;
+    }
+  }
+  return false;
+}
+
+unsigned grid_xcd(int64_t ntiles) { return (unsigned)(round_up(ntiles, kXcd)); }
+
+template <int D>
+tri_attn_status launch_fwd(unsigned stages, const Plan& P, const void* q, const void* k, const void* v, const void* bias,
+                           const uint8_t* mask, void* o, float* lse, void* res, void* ws, hipStream_t st) {
+  const float alpha = 1.0f / sqrtf((float)D);
+  float* biasF = (float*)ws;
+  const int64_t nb = P.B * P.H * P.Jp * P.Kp;
+  if (stages & TRI_ATTN_STAGE_PREP)
+    hipLaunchKernelGGL(bias_prep_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, st, (const bf16*)bias,
+                       biasF, (int)P.N, (int)P.Jp, (int)P.Kp, true, 1.0f / alpha, nb);
+  const int64_t ntiles = P.B * P.H * P.N * ((P.N + 127) / 128);
+  if (!(stages & TRI_ATTN_STAGE_MAIN)) {
+  } else if (mask)
+    hipLaunchKernelGGL((fwd_kernel<D, true>), dim3(grid_xcd(ntiles)), dim3(256), 0, st, (const bf16*)q,
+                       (const bf16*)k, (const bf16*)v, biasF, mask, (bf16*)o, lse, (bf16*)res, (int)P.B, (int)P.N,
+                       (int)P.H, alpha);
+  else
+    hipLaunchKernelGGL((fwd_kernel<D, false>), dim3(grid_xcd(ntiles)), dim3(256), 0, st, (const bf16*)q,
+                       (const bf16*)k, (const bf16*)v, biasF, mask, (bf16*)o, lse, (bf16*)res, (int)P.B, (int)P.N,
+                       (int)P.H, alpha);
+  return hipGetLastError() == hipSuccess ? TRI_ATTN_SUCCESS : TRI_ATTN_ERROR_LAUNCH;
+}
+
+template <int D>
+tri_attn_status launch_bwd(unsigned stages, const Plan& P, const void* q, const void* k, const void* v, const void* bias,
+                           const uint8_t* mask, const void* o, const float* lse, const void* res, const void* dO,
+                           void* dq, void* dk, void* dv, float* dbias, void* ws, hipStream_t st) {
+  const float alpha = 1.0f / sqrtf((float)D);
+  char* base = (char*)ws;
+  float* biasT = (float*)base;
+  float* Dg = (float*)(base + P.off_D);
+  float* dqp = (float*)(base + P.off_dqp);
+  float* dbp = (float*)(base + P.off_dbp);
+  const int64_t nb = P.B * P.H * P.Kp * P.Jp;
+  if (stages & TRI_ATTN_STAGE_PREP) {
+    hipLaunchKernelGGL(bias_prep_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, st, (const bf16*)bias,
+                       biasT, (int)P.N, (int)P.Kp, (int)P.Jp, false, 1.0f / alpha, nb);
+    hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3((unsigned)((P.rows + 255) / 256)), dim3(256), 0, st,
+                       (const bf16*)dO, (const bf16*)o, (const bf16*)res, Dg, P.rows);
+  }
+  const int64_t ntiles = P.B * P.H * P.ngroups * P.KB;
+  if (!(stages & TRI_ATTN_STAGE_MAIN)) {
+  } else if (mask)
+    hipLaunchKernelGGL((bwd_kernel<D, true>), dim3(grid_xcd(ntiles)), dim3(512), 0, st, (const bf16*)q,
+                       (const bf16*)k, (const bf16*)v, (const bf16*)dO, biasT, mask, lse, Dg, dqp, dbp, (bf16*)dk,
+                       (bf16*)dv, (int)P.B, (int)P.N, (int)P.H, (int)P.G, (int)P.ngroups, alpha);
+  else
+    hipLaunchKernelGGL((bwd_kernel<D, false>), dim3(grid_xcd(ntiles)), dim3(512), 0, st, (const bf16*)q,
+                       (const bf16*)k, (const bf16*)v, (const bf16*)dO, biasT, mask, lse, Dg, dqp, dbp, (bf16*)dk,
+                       (bf16*)dv, (int)P.B, (int)P.N, (int)P.H, (int)P.G, (int)P.ngroups, alpha);
+  if (stages & TRI_ATTN_STAGE_FINAL) {
+    const int64_t n4 = P.elems / 4;
+    hipLaunchKernelGGL(reduce_dq_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, dqp, (bf16*)dq,
+                       (int)P.KB, n4, alpha);
+    const int64_t nbias = P.B * P.H * P.N * P.N;
+    hipLaunchKernelGGL(reduce_dbias_kernel, dim3((unsigned)((nbias + 255) / 256)), dim3(256), 0, st, dbp, dbias,
+                       (int)P.ngroups, nbias);
+  }
+  return hipGetLastError() == hipSuccess ? TRI_ATTN_SUCCESS : TRI_ATTN_ERROR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tri_attn_status_string(int status) {
+  switch (status) {
+    case TRI_ATTN_SUCCESS: return "TRI_ATTN_SUCCESS";
+    case TRI_ATTN_ERROR_INVALID_VALUE: return "TRI_ATTN_ERROR_INVALID_VALUE";
+    case TRI_ATTN_ERROR_UNSUPPORTED: return "TRI_ATTN_ERROR_UNSUPPORTED";
+    case TRI_ATTN_ERROR_MISALIGNED: return "TRI_ATTN_ERROR_MISALIGNED";
+    case TRI_ATTN_ERROR_WORKSPACE: return "TRI_ATTN_ERROR_WORKSPACE";
+    case TRI_ATTN_ERROR_LAUNCH: return "TRI_ATTN_ERROR_LAUNCH";
+    default: return "TRI_ATTN_UNKNOWN_STATUS";
+  }
+}
+
+size_t tri_attn_fwd_workspace_bytes(int64_t B, int64_t N, int64_t H, int64_t D) {
+  if (!shape_ok(B, N, H, D)) return 0;
+  return (size_t)make_plan(B, N, H, D).bias_f32_bytes;
+}
+
+size_t tri_attn_bwd_workspace_bytes(int64_t B, int64_t N, int64_t H, int64_t D) {
+  if (!shape_ok(B, N, H, D)) return 0;
+  return (size_t)make_plan(B, N, H, D).bwd_bytes;
+}
+
+tri_attn_status tri_attn_fwd_stages(unsigned stages, int64_t B, int64_t N, int64_t H, int64_t D, const void* q,
+                                    const void* k, const void* v, const void* bias, const uint8_t* key_mask, void* o,
+                                    float* lse, void* residual, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
+  if (stages & ~TRI_ATTN_STAGE_ALL) return TRI_ATTN_ERROR_INVALID_VALUE;
+  if (B < 1 || N < 1 || H < 1) return TRI_ATTN_ERROR_INVALID_VALUE;
+  if (!shape_ok(B, N, H, D)) return TRI_ATTN_ERROR_UNSUPPORTED;
+  if (!q || !k || !v || !bias || !o || !lse) return TRI_ATTN_ERROR_INVALID_VALUE;
+  const Plan P = make_plan(B, N, H, D);
+  const int64_t tb = P.elems * 2, bb = B * H * N * N * 2, lb = P.rows * 4, mb = B * N * N;
+  const Range rs[] = {{q, tb, false}, {k, tb, false}, {v, tb, false}, {bias, bb, false}, {key_mask, mb, false},
+                      {o, tb, true}, {lse, lb, true}, {residual, tb, true}, {workspace, (int64_t)workspace_bytes, true}};
+  if (overlaps(rs, 9)) return TRI_ATTN_ERROR_INVALID_VALUE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(bias) || !aligned16(o) || !aligned16(lse) ||
+      (residual && !aligned16(residual)) || (workspace && !aligned16(workspace)))
+    return TRI_ATTN_ERROR_MISALIGNED;
+  if (!workspace || workspace_bytes < (size_t)P.bias_f32_bytes) return TRI_ATTN_ERROR_WORKSPACE;
+  return D == 16 ? launch_fwd<16>(stages, P, q, k, v, bias, key_mask, o, lse, residual, workspace, stream)
+                 : launch_fwd<32>(stages, P, q, k, v, bias, key_mask, o, lse, residual, workspace, stream);
+}
+
+tri_attn_status tri_attn_fwd(int64_t B, int64_t N, int64_t H, int64_t D, const void* q, const void* k, const void* v,
+                             const void* bias, const uint8_t* key_mask, void* o, float* lse, void* residual,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return tri_attn_fwd_stages(TRI_ATTN_STAGE_ALL, B, N, H, D, q, k, v, bias, key_mask, o, lse, residual, workspace,
+                             workspace_bytes, stream);
+}
+
+tri_attn_status tri_attn_bwd_stages(unsigned stages, int64_t B, int64_t N, int64_t H, int64_t D, const void* q,
+                                    const void* k, const void* v, const void* bias, const uint8_t* key_mask,
+                                    const void* o, const float* lse, const void* residual, const void* dO, void* dq,
+                                    void* dk, void* dv, float* dbias, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
+  if (stages & ~TRI_ATTN_STAGE_ALL) return TRI_ATTN_ERROR_INVALID_VALUE;
+  if (B < 1 || N < 1 || H < 1) return TRI_ATTN_ERROR_INVALID_VALUE;
+  if (!shape_ok(B, N, H, D)) return TRI_ATTN_ERROR_UNSUPPORTED;
+  if (!q || !k || !v || !bias || !o || !lse || !dO || !dq || !dk || !dv || !dbias) return TRI_ATTN_ERROR_INVALID_VALUE;
+  const Plan P = make_plan(B, N, H, D);
+  const int64_t tb = P.elems * 2, bb = B * H * N * N * 2, lb = P.rows * 4, mb = B * N * N, db = B * H * N * N * 4;
+  const Range rs[] = {{q, tb, false},  {k, tb, false},  {v, tb, false},   {bias, bb, false},
+                      {key_mask, mb, false}, {o, tb, false}, {lse, lb, false}, {residual, tb, false},
+                      {dO, tb, false}, {dq, tb, true},   {dk, tb, true},    {dv, tb, true},
+                      {dbias, db, true}, {workspace, (int64_t)workspace_bytes, true}};
+  if (overlaps(rs, 14)) return TRI_ATTN_ERROR_INVALID_VALUE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(bias) || !aligned16(o) || !aligned16(lse) ||
+      (residual && !aligned16(residual)) || !aligned16(dO) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
+      !aligned16(dbias) || (workspace && !aligned16(workspace)))
+    return TRI_ATTN_ERROR_MISALIGNED;
+  if (!workspace || workspace_bytes < (size_t)P.bwd_bytes) return TRI_ATTN_ERROR_WORKSPACE;
+  return D == 16 ? launch_bwd<16>(stages, P, q, k, v, bias, key_mask, o, lse, residual, dO, dq, dk, dv, dbias,
+                                  workspace, stream)
+                 : launch_bwd<32>(stages, P, q, k, v, bias, key_mask, o, lse, residual, dO, dq, dk, dv, dbias,
+                                  workspace, stream);
+}
+
+tri_attn_status tri_attn_bwd(int64_t B, int64_t N, int64_t H, int64_t D, const void* q, const void* k, const void* v,
+                             const void* bias, const uint8_t* key_mask, const void* o, const float* lse,
+                             const void* residual, const void* dO, void* dq, void* dk, void* dv, float* dbias,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return tri_attn_bwd_stages(TRI_ATTN_STAGE_ALL, B, N, H, D, q, k, v, bias, key_mask, o, lse, residual, dO, dq, dk,
+                             dv, dbias, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
