@@ -29,6 +29,8 @@
 #include <string.h>
 #include <math.h>
 
+#include <type_traits>
+
 #include "tri_attn.h"
 
 namespace {
@@ -295,20 +297,29 @@ void fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
 }
 
 // ------------------------------------------------------------------ backward: correction D
-// D[b,i,h,j] = sum_c dO * (o + residual) in FP32 (or dO * o without a residual).
+// D[b,i,h,j] = sum_c dO * (o + residual) in FP32 (or dO * o without a residual), written
+// with lse2 = lse * log2(e) into rows padded to Jp floats (16-byte aligned, zero padding),
+// the layout the main kernel streams into LDS.  D/8 adjacent lanes share a row (16 bytes
+// each, so a wave reads contiguous memory); their partial sums combine in a fixed order.
 template <int D>
 __global__ __launch_bounds__(256)
 void bwd_pre_kernel(const bf16* __restrict__ dO, const bf16* __restrict__ o, const bf16* __restrict__ res,
-                    float* __restrict__ Dout, int64_t rows) {
-  const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (r >= rows) return;
+                    const float* __restrict__ lse, float* __restrict__ Dp, float* __restrict__ L2p, int N, int Jp,
+                    int64_t nrows) {
+  constexpr int LPR = D / 8;  // lanes per row
+  // the grid covers nrows * Jp * LPR threads exactly (Jp * LPR is a multiple of 256)
+  const int64_t gt = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t prow = gt / LPR;  // padded row index
+  const int part = (int)(gt % LPR);
+  const int64_t row = prow / Jp;
+  const int j = (int)(prow % Jp);
   float acc = 0.0f;
-#pragma unroll
-  for (int c8 = 0; c8 < D / 8; c8++) {
-    const bf16x8 a = *(const bf16x8*)(dO + r * D + c8 * 8);
-    const bf16x8 ov = *(const bf16x8*)(o + r * D + c8 * 8);
+  if (j < N) {
+    const int64_t off = (row * N + j) * D + part * 8;
+    const bf16x8 a = *(const bf16x8*)(dO + off);
+    const bf16x8 ov = *(const bf16x8*)(o + off);
     if (res) {
-      const bf16x8 rv = *(const bf16x8*)(res + r * D + c8 * 8);
+      const bf16x8 rv = *(const bf16x8*)(res + off);
 #pragma unroll
       for (int e = 0; e < 8; e++) acc = __builtin_fmaf((float)a[e], (float)ov[e] + (float)rv[e], acc);
     } else {
@@ -316,43 +327,63 @@ void bwd_pre_kernel(const bf16* __restrict__ dO, const bf16* __restrict__ o, con
       for (int e = 0; e < 8; e++) acc = __builtin_fmaf((float)a[e], (float)ov[e], acc);
     }
   }
-  Dout[r] = acc;
+  acc += __shfl_xor(acc, 1);
+  if (LPR == 4) acc += __shfl_xor(acc, 2);
+  if (part == 0) {
+    Dp[prow] = acc;
+    L2p[prow] = j < N ? lse[row * N + j] * kLog2e : 0.0f;
+  }
 }
 
 // ------------------------------------------------------------------ backward: main
 // One work-group = 8 waves = one block of 64 keys of head h, for a group of G slices.
-// wave w: key half kh = w&1 (32 keys), query lane p = w>>1.  Per slice the queries are
-// walked in steps of 128 (4 tiles of 32, tile p to query lane p).  Each wave keeps the
-// pair-bias gradient of its (query tiles x 32 keys) in registers across the slice group
-// ("face"), so dS is summed over slices on chip and written once per group.
+// wave w: key half kh = w&1 (32 keys), query lane p = w>>1.  The work items are
+// (slice, 128-query step) pairs; step s of a slice covers queries 128s..128s+127 in four
+// tiles of 32, tile p going to query lane p.  Each wave keeps the pair-bias gradient of
+// its (query tiles x 32 keys) in registers across the slice group ("face"), so dS is
+// summed over slices on chip and written once per group.  The steps of a slice are
+// unrolled at compile time so that every face slot is addressed statically.
+//
+// Software pipeline: while item t is computed, item t+1's Q, dO, bias tiles, lse2 and D
+// (and K, V at a slice boundary) stream from global memory straight into the other half
+// of double-buffered LDS (global_load_lds_dwordx4, no registers involved).  Rows past N
+// are loaded from row N-1: the -inf padding of the prepared bias turns every padded query
+// or key into an exact zero probability, so their contents never matter.
+//
+// Rows of Q, dO, K and V in LDS hold their 16-byte chunks in XOR-swizzled order (chunk c
+// of row r sits in slot c ^ swz(r)), which spreads the row-wise operand reads of a wave
+// over all LDS banks.
 constexpr int kBwdMaxSteps = 6;  // 6 steps x 128 queries = TRI_ATTN_MAX_N
+
+__device__ __forceinline__ void dma16(const void* g, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+}
+
+// chunk swizzle for rows of D bf16 (D/8 chunks of 16 bytes per row)
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  return D == 32 ? ((row >> 2) & 3) : ((row >> 3) & 1);
+}
 
 template <int D, bool MASK>
 __global__ __launch_bounds__(512, 1)
 void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
                 const bf16* __restrict__ dO, const float* __restrict__ biasT, const uint8_t* __restrict__ mask,
-                const float* __restrict__ lse, const float* __restrict__ Dg,
+                const float* __restrict__ L2p, const float* __restrict__ Dp,
                 float* __restrict__ dqp, float* __restrict__ dbp, bf16* __restrict__ dk, bf16* __restrict__ dv,
                 int B, int N, int H, int G, int ngroups, float alpha) {
   constexpr int NC = D / 16;
+  constexpr int CPR = D / 8;    // 16-byte chunks per row
   constexpr int LDT = 128 + 8;  // dS^T row stride (elements), padded
   constexpr int NR = D / 2;     // accumulator registers of dK^T / dV^T holding channels c < D
-  __shared__ __attribute__((aligned(16))) bf16 Ks_[64 * D];
-  __shared__ __attribute__((aligned(16))) bf16 Vs_[64 * D];
-  __shared__ __attribute__((aligned(16))) bf16 Qs_[128 * D];
-  __shared__ __attribute__((aligned(16))) bf16 dOs_[128 * D];
-  __shared__ __attribute__((aligned(16))) float lseS_[128];
-  __shared__ __attribute__((aligned(16))) float DS_[128];
+  __shared__ __attribute__((aligned(16))) bf16 Qs_[2][128 * D];
+  __shared__ __attribute__((aligned(16))) bf16 dOs_[2][128 * D];
+  __shared__ __attribute__((aligned(16))) float bS_[2][8 * 1024];  // bias tiles [kh][p][1024]
+  __shared__ __attribute__((aligned(16))) float lS_[2][128];
+  __shared__ __attribute__((aligned(16))) float DS_[2][128];
+  __shared__ __attribute__((aligned(16))) bf16 Ks_[2][64 * D];
+  __shared__ __attribute__((aligned(16))) bf16 Vs_[2][64 * D];
   __shared__ __attribute__((aligned(16))) bf16 dST_[64 * LDT];
-  __shared__ __attribute__((aligned(16))) float red_[8 * 2 * NR * 64];
-  lbf16* Ks = (lbf16*)Ks_;
-  lbf16* Vs = (lbf16*)Vs_;
-  lbf16* Qs = (lbf16*)Qs_;
-  lbf16* dOs = (lbf16*)dOs_;
-  lf32* lseS = (lf32*)lseS_;
-  lf32* DS = (lf32*)DS_;
-  lbf16* dST = (lbf16*)dST_;
-  lf32* red = (lf32*)red_;
 
   const int KB = (N + 63) / 64;
   const int64_t ntiles = (int64_t)B * H * ngroups * KB;
@@ -372,94 +403,127 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   const int kg = kb * 64 + kl;          // global key of this lane
   const bool kok = kg < N;
   const int Kp = (int)round_up(N, 64), Jp = (int)round_up(N, 128);
-  const float* bT = biasT + ((int64_t)(b * H + h) * (Kp / 32) + (kb * 2 + kh)) * (int64_t)(Jp / 32) * 1024;
+  const float* bT = biasT + ((int64_t)(b * H + h) * (Kp / 32) + kb * 2) * (int64_t)(Jp / 32) * 1024;
   const float c1 = alpha * kLog2e;
   const float mneg = kMaskNeg / alpha;
   const int64_t slice_elems = (int64_t)N * D;
   const int64_t dq_stride = (int64_t)B * N * H * slice_elems;  // one full dq partial
+  const int nsteps = (N + 127) / 128;
 
-  // per-lane LDS bases (element offsets); loop-varying parts are compile-time immediates
-  const int trl_d = tr_lane(D), trl_t = tr_lane(LDT);
-  // dV^T/dK^T A operands: rows (queries) p*32 + 4g (+16 m2, +8), channels 16*chalf
-  const int base_qo = (p * 32 + 4 * g) * D + (D == 32 ? 16 * chalf : 0) + trl_d;
-  // dQ^T tiles of this wave: channel tile ct = u, query sub-tile js = w&1 of query tile jt = w>>1
-  const int base_kT = 8 * G16 * D + trl_d;
-  const int base_sT = 8 * G16 * LDT + (w >> 1) * 32 + (w & 1) * 16 + trl_t;
-  const int base_red_w = w * (2 * NR * 64) + l;
-  const int base_red_r = kh * (2 * NR * 64) + p * ((2 * NR) / 4) * 64 + l;
+
+  // ---- per-lane LDS offsets (elements) of the operand reads
+  // natural row reads: row rr, chunk c -> rr*D + ((c ^ swz(rr)) * 8)
+  // transposed reads of a 4-row group starting at row r0 (swz constant over the group)
+  auto tr_off = [](int lane, int r0, int c0) {  // element offset of this lane's 8 bytes
+    const int t16 = lane & 15;
+    const int rr = r0 + (t16 >> 2), col = c0 + 4 * (t16 & 3);
+    return rr * D + ((((col >> 3) ^ swz<D>(rr)) << 3) | (col & 7));
+  };
+
+  // issue the loads of work item (ii, ss) into LDS buffer `buf`; each lane fetches the global
+  // chunk that belongs in its LDS slot (swizzled for Q, dO, K, V).  Bases are uniform, lane
+  // offsets 32-bit.
+  auto prefetch = [&](int ii, int ss, int buf) {
+    int tx = tid;
+    asm volatile("" : "+v"(tx));  // keep the per-lane address math local to this call
+    const int j0 = ss * 128;
+    const int64_t sl = ((int64_t)b * N + ii) * H + h;  // slice-head row index
+    const bf16* qb = q + sl * slice_elems;
+    const bf16* ob = dO + sl * slice_elems;
+    if (tx < 128 * CPR) {
+      const int pr_row = tx / CPR;
+      const unsigned off = (unsigned)(min(j0 + pr_row, N - 1) * D + ((tx % CPR) ^ swz<D>(pr_row)) * 8);
+      dma16(qb + off, &Qs_[buf][w * 512]);
+      dma16(ob + off, &dOs_[buf][w * 512]);
+    }
+    const float* bts = bT + ss * 4096;
+#pragma unroll
+    for (int m = 0; m < 4; m++) {
+      const unsigned f = (unsigned)(tx + 512 * m) * 4u;
+      dma16(bts + ((f >> 12) * (unsigned)(Jp / 32) * 1024u + (f & 4095u)), &bS_[buf][(w * 64 + 512 * m) * 4]);
+    }
+    const float* l2b = L2p + sl * Jp + j0;
+    const float* db = Dp + sl * Jp + j0;
+    if (w == 0 && l < 32) dma16(l2b + 4 * tx, &lS_[buf][0]);
+    if (w == 1 && l < 32) dma16(db + 4 * (tx - 64), &DS_[buf][0]);
+    if (ss == 0) {  // first step of a slice: its K and V blocks
+      constexpr int KC = 64 * CPR;  // 16-byte chunks per block
+      const int kvb = (ii - i_begin) & 1;
+      const int kv_t = tx < 256 ? tx : tx - 256;  // K (waves 0-3) / V (waves 4-7)
+      const int kv_row = kv_t / CPR;
+      const unsigned off = (unsigned)(min(kb * 64 + kv_row, N - 1) * D + ((kv_t % CPR) ^ swz<D>(kv_row)) * 8);
+      if (tx < KC) dma16(k + sl * slice_elems + off, &Ks_[kvb][w * 512]);
+      else if (tx >= 256 && tx < 256 + KC) dma16(v + sl * slice_elems + off, &Vs_[kvb][(w - 4) * 512]);
+    }
+  };
 
   f32x16 face[kBwdMaxSteps];
 #pragma unroll
   for (int s = 0; s < kBwdMaxSteps; s++) face[s] = f32x16{};
 
+  prefetch(i_begin, 0, 0);
+  int cur = 0;
   for (int i = i_begin; i < i_end; i++) {
+    const int kvb = (i - i_begin) & 1;
     const int64_t sbase = (((int64_t)b * N + i) * H + h) * slice_elems;
-    const int64_t rbase = (((int64_t)b * N + i) * H + h) * (int64_t)N;
-    // uniform per-slice bases; lane offsets below are 32-bit
-    const bf16* ks = k + sbase + (int64_t)kb * 64 * D;
-    const bf16* vs = v + sbase + (int64_t)kb * 64 * D;
-    const bf16* qsl = q + sbase;
-    const bf16* dos = dO + sbase;
-    const float* lsl = lse + rbase;
-    const float* dsl = Dg + rbase;
-    float* dqs = dqp + (int64_t)kb * dq_stride + sbase;
-    // K and V blocks into LDS (zero beyond N): K/V rows feed S and dP, K^T feeds dQ
-    for (int c = tid; c < 64 * D / 8; c += 512) {
-      const int r = c / (D / 8), col = (c % (D / 8)) * 8;
-      bf16x8 kv = zero8(), vv = zero8();
-      if (kb * 64 + r < N) {
-        kv = *(const bf16x8*)(ks + r * D + col);
-        vv = *(const bf16x8*)(vs + r * D + col);
-      }
-      *(lbf16x8*)(Ks + r * D + col) = kv;
-      *(lbf16x8*)(Vs + r * D + col) = vv;
-    }
     float madd = 0.0f;
-    if (MASK && kok && !mask[((int64_t)b * N + i) * N + kg]) madd = mneg;
     f32x16 dkT = {}, dvT = {};
 
-    const int nsteps = (N + 127) / 128;
-#pragma unroll 1
-    for (int s = 0; s < nsteps; s++) {
+    auto step = [&](auto S_) {
+      constexpr int s = decltype(S_)::value;
       const int j0 = s * 128;
-      __syncthreads();  // previous users of Qs/dOs/dST/lseS are done; K/V staged
-      for (int c = tid; c < 128 * D / 8; c += 512) {
-        const int r = c / (D / 8), col = (c % (D / 8)) * 8;
-        bf16x8 qv = zero8(), ov = zero8();
-        if (j0 + r < N) {
-          qv = *(const bf16x8*)(qsl + (j0 + r) * D + col);
-          ov = *(const bf16x8*)(dos + (j0 + r) * D + col);
-        }
-        *(lbf16x8*)(Qs + r * D + col) = qv;
-        *(lbf16x8*)(dOs + r * D + col) = ov;
+      // The lane index is made opaque at every unrolled step, so that addresses derived from
+      // it are rebuilt locally instead of being held live across all six steps.
+      int lx = l;
+      asm volatile("" : "+v"(lx));
+      const int g = lx >> 5, ln = lx & 31, G16 = lx >> 4, chalf = G16 & 1;
+      const int kl = kh * 32 + ln, rq = p * 32 + ln, rk = kl;
+      // item (i, s) was issued before the previous item's dq stores (and, at a slice
+      // boundary, before the previous slice's dk/dv stores, where everything is drained)
+      if (s == 0) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        if (MASK) madd = (kok && !mask[((int64_t)b * N + i) * N + kg]) ? mneg : 0.0f;
+      } else if (NC == 2) {
+        __builtin_amdgcn_s_waitcnt(0x0F72);  // vmcnt(2): the two dq stores may be in flight
+      } else {
+        __builtin_amdgcn_s_waitcnt(0x0F71);  // vmcnt(1)
       }
-      if (tid < 128) lseS[tid] = (j0 + tid < N) ? lsl[j0 + tid] * kLog2e : 0.0f;
-      else if (tid < 256) DS[tid - 128] = (j0 + tid - 128 < N) ? dsl[j0 + tid - 128] : 0.0f;
-      __syncthreads();
+      __syncthreads();  // item (i, s) is in LDS everywhere; the other buffers and dS^T are free
+      if (s + 1 < nsteps) prefetch(i, s + 1, cur ^ 1);
+      else if (i + 1 < i_end) prefetch(i + 1, 0, cur ^ 1);
+
+      const lbf16* Qs = (const lbf16*)Qs_[cur];
+      const lbf16* dOs = (const lbf16*)dOs_[cur];
+      const lbf16* Ks = (const lbf16*)Ks_[kvb];
+      const lbf16* Vs = (const lbf16*)Vs_[kvb];
+      const lf32* bS = (const lf32*)bS_[cur] + (kh * 4 + p) * 1024;
+      const lf32* lS = (const lf32*)lS_[cur];
+      const lf32* DSv = (const lf32*)DS_[cur];
+      lbf16* dST = (lbf16*)dST_;
 
       // S = bias/alpha + Q K^T  and  dP = dO V^T   (rows: 32 queries, cols: 32 keys)
       f32x16 sacc, dp = {};
-      const float* bt = bT + (int64_t)(s * 4 + p) * 1024;
 #pragma unroll
       for (int R = 0; R < 4; R++) {
-        const f32x4 bv = *(const f32x4*)(bt + ((R * 2 + g) * 32 + ln) * 4);
+        const f32x4 bv = *(const lf32x4*)(bS + ((R * 2 + g) * 32 + ln) * 4);
         sacc[R * 4 + 0] = bv[0]; sacc[R * 4 + 1] = bv[1];
         sacc[R * 4 + 2] = bv[2]; sacc[R * 4 + 3] = bv[3];
       }
 #pragma unroll
       for (int cc = 0; cc < NC; cc++) {
-        const bf16x8 aq = *(const lbf16x8*)(Qs + (p * 32 + ln) * D + cc * 16 + g * 8);
-        const bf16x8 kf = *(const lbf16x8*)(Ks + kl * D + cc * 16 + g * 8);
+        const int cq = ((cc * 2 + g) ^ swz<D>(rq)) * 8, ck = ((cc * 2 + g) ^ swz<D>(rk)) * 8;
+        const bf16x8 aq = *(const lbf16x8*)(Qs + rq * D + cq);
+        const bf16x8 kf = *(const lbf16x8*)(Ks + rk * D + ck);
         sacc = mfma32(aq, kf, sacc);
-        const bf16x8 ao = *(const lbf16x8*)(dOs + (p * 32 + ln) * D + cc * 16 + g * 8);
-        const bf16x8 vf = *(const lbf16x8*)(Vs + kl * D + cc * 16 + g * 8);
+        const bf16x8 ao = *(const lbf16x8*)(dOs + rq * D + cq);
+        const bf16x8 vf = *(const lbf16x8*)(Vs + rk * D + ck);
         dp = mfma32(ao, vf, dp);
       }
       float P[16], dS[16];
 #pragma unroll
       for (int R = 0; R < 4; R++) {
-        const f32x4 lv = *(const lf32x4*)(lseS + p * 32 + R * 8 + g * 4);
-        const f32x4 dd = *(const lf32x4*)(DS + p * 32 + R * 8 + g * 4);
+        const f32x4 lv = *(const lf32x4*)(lS + p * 32 + R * 8 + g * 4);
+        const f32x4 dd = *(const lf32x4*)(DSv + p * 32 + R * 8 + g * 4);
 #pragma unroll
         for (int e = 0; e < 4; e++) {
           const int r = R * 4 + e;
@@ -469,31 +533,20 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
           dS[r] = P[r] * (dp[r] - dd[e]);
         }
       }
-      // the face slot is selected by a uniform switch so that its registers stay statically indexed
-      switch (s) {
-#define TRI_FACE_ADD(S_)                                                  \
-  case S_:                                                                \
-    _Pragma("unroll") for (int r = 0; r < 16; r++) face[S_][r] += dS[r]; \
-    break;
-        TRI_FACE_ADD(0) TRI_FACE_ADD(1) TRI_FACE_ADD(2) TRI_FACE_ADD(3) TRI_FACE_ADD(4) TRI_FACE_ADD(5)
-#undef TRI_FACE_ADD
-        default: break;
-      }
-      static_assert(kBwdMaxSteps == 6, "face switch covers 6 slots");
+#pragma unroll
+      for (int r = 0; r < 16; r++) face[s][r] += dS[r];
 
       // dV^T += dO^T P ; dK^T += Q^T dS   (rows: channels, cols: keys)
 #pragma unroll
       for (int m2 = 0; m2 < 2; m2++) {
         const bf16x8 pb = pack8(&P[m2 * 8]);
         const bf16x8 sb = pack8(&dS[m2 * 8]);
-        bf16x8 ao, aq;
-        if (D == 32 || chalf == 0) {
-          ao = cat8(tr16p(dOs + base_qo + m2 * 16 * D), tr16p(dOs + base_qo + (m2 * 16 + 8) * D));
-          aq = cat8(tr16p(Qs + base_qo + m2 * 16 * D), tr16p(Qs + base_qo + (m2 * 16 + 8) * D));
-        } else {
-          ao = zero8();
-          aq = zero8();
-        }
+        // at D = 16 the upper 16 channel rows of the 32x32 product repeat the lower ones;
+        // those accumulator rows are never stored
+        const int r0 = p * 32 + m2 * 16 + 4 * g, c0 = D == 32 ? 16 * chalf : 0;
+        const int o1 = tr_off(lx, r0, c0), o2 = tr_off(lx, r0 + 8, c0);
+        const bf16x8 ao = cat8(tr16p(dOs + o1), tr16p(dOs + o2));
+        const bf16x8 aq = cat8(tr16p(Qs + o1), tr16p(Qs + o2));
         dvT = mfma32(ao, pb, dvT);
         dkT = mfma32(aq, sb, dkT);
       }
@@ -505,43 +558,77 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
         for (int e = 0; e < 4; e++) t4[e] = (bf16)dS[R * 4 + e];
         *(lbf16x4*)(dST + kl * LDT + p * 32 + R * 8 + g * 4) = t4;
       }
-      __syncthreads();
+      __syncthreads();  // dS^T complete
       // dQ^T tiles (16 channels x 16 queries) over the 64 keys of this block
-      const int jj = j0 + (w >> 1) * 32 + (w & 1) * 16 + (l & 15);
+      {
+        float* dqs = dqp + (int64_t)kb * dq_stride + sbase;
+        const int jj = j0 + (w >> 1) * 32 + (w & 1) * 16 + (lx & 15);
+        const int sT = 8 * G16 * LDT + (w >> 1) * 32 + (w & 1) * 16 + tr_lane(LDT);
 #pragma unroll
-      for (int u = 0; u < NC; u++) {
-        f32x4 c = {};
+        for (int u = 0; u < NC; u++) {
+          f32x4 c = {};
 #pragma unroll
-        for (int kk = 0; kk < 64; kk += 32) {
-          const bf16x8 a = cat8(tr16p(Ks + base_kT + kk * D + u * 16), tr16p(Ks + base_kT + (kk + 4) * D + u * 16));
-          const bf16x8 bb = cat8(tr16p(dST + base_sT + kk * LDT), tr16p(dST + base_sT + (kk + 4) * LDT));
-          c = mfma16(a, bb, c);
+          for (int kk = 0; kk < 64; kk += 32) {
+            const bf16x8 a = cat8(tr16p(Ks + tr_off(lx, kk + 8 * G16, u * 16)), tr16p(Ks + tr_off(lx, kk + 8 * G16 + 4, u * 16)));
+            const bf16x8 bb = cat8(tr16p(dST + sT + kk * LDT), tr16p(dST + sT + (kk + 4) * LDT));
+            c = mfma16(a, bb, c);
+          }
+          if (jj < N) *(f32x4*)(dqs + jj * D + u * 16 + 4 * G16) = c;
         }
-        if (jj < N) *(f32x4*)(dqs + jj * D + u * 16 + 4 * G16) = c;
+      }
+      cur ^= 1;
+    };
+
+    step(std::integral_constant<int, 0>{});
+    if (nsteps > 1) step(std::integral_constant<int, 1>{});
+    if (nsteps > 2) step(std::integral_constant<int, 2>{});
+    if (nsteps > 3) step(std::integral_constant<int, 3>{});
+    if (nsteps > 4) step(std::integral_constant<int, 4>{});
+    if (nsteps > 5) step(std::integral_constant<int, 5>{});
+    static_assert(kBwdMaxSteps == 6, "six unrolled steps");
+
+    // end of slice i: dK^T, dV^T summed over the four query lanes as (p0 + p1) + (p2 + p3),
+    // in the bias buffer of the last item (no longer read; the prefetch targets the other one)
+    lf32* red = (lf32*)bS_[cur ^ 1];
+    const int slot_w = (kh * 2 + (p >> 1)) * (2 * NR * 64) + l;
+    if (p & 1) {
+#pragma unroll
+      for (int r = 0; r < NR; r++) {
+        red[slot_w + r * 64] = dkT[r];
+        red[slot_w + (NR + r) * 64] = dvT[r];
       }
     }
-    // reduce dK^T, dV^T over the 4 query lanes in fixed order; query lane p finishes a quarter
+    __syncthreads();
+    if (!(p & 1)) {
 #pragma unroll
-    for (int r = 0; r < NR; r++) {
-      red[base_red_w + r * 64] = dkT[r];
-      red[base_red_w + (NR + r) * 64] = dvT[r];
+      for (int r = 0; r < NR; r++) {
+        dkT[r] += red[slot_w + r * 64];
+        dvT[r] += red[slot_w + (NR + r) * 64];
+      }
+    }
+    if (p == 2) {  // (p2 + p3) into its own slot, which only this wave read
+#pragma unroll
+      for (int r = 0; r < NR; r++) {
+        red[slot_w + r * 64] = dkT[r];
+        red[slot_w + (NR + r) * 64] = dvT[r];
+      }
     }
     __syncthreads();
-    {
-      constexpr int PER = (2 * NR) / 4;  // registers finished by each query lane
+    if (p == 0) {
+      const int slot2 = (kh * 2 + 1) * (2 * NR * 64) + l;
 #pragma unroll
-      for (int u = 0; u < PER; u++) {
-        float sum = red[base_red_r + u * 64];
-        sum += red[base_red_r + 1 * (4 * NR * 64) + u * 64];
-        sum += red[base_red_r + 2 * (4 * NR * 64) + u * 64];
-        sum += red[base_red_r + 3 * (4 * NR * 64) + u * 64];
-        const int rr = p * PER + u;  // 0 .. 2*NR-1: dK^T registers first, then dV^T
-        const bool isv = rr >= NR;
-        const int r = isv ? rr - NR : rr;
-        const int c = (r >> 2) * 8 + g * 4 + (r & 3);
+      for (int R = 0; R < NR / 4; R++) {
+        bf16x4 ok4, ov4;
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          const int r = R * 4 + e;
+          ok4[e] = (bf16)((dkT[r] + red[slot2 + r * 64]) * alpha);
+          ov4[e] = (bf16)(dvT[r] + red[slot2 + (NR + r) * 64]);
+        }
         if (kok) {
-          bf16* dst = (isv ? dv : dk) + sbase;
-          dst[kg * D + c] = (bf16)(isv ? sum : sum * alpha);
+          const int c = R * 8 + g * 4;
+          *(bf16x4*)(dk + sbase + (int64_t)kg * D + c) = ok4;
+          *(bf16x4*)(dv + sbase + (int64_t)kg * D + c) = ov4;
         }
       }
     }
@@ -550,7 +637,7 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   float* dst = dbp + (((int64_t)grp * B + b) * H + h) * (int64_t)N * N;
 #pragma unroll
   for (int s = 0; s < kBwdMaxSteps; s++) {
-    if (s * 128 < N) {
+    if (s < nsteps) {
 #pragma unroll
       for (int r = 0; r < 16; r++) {
         const int jj = s * 128 + p * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
@@ -596,7 +683,7 @@ struct Plan {
   int64_t elems;            // B*N*H*N*D
   int64_t rows;             // B*N*H*N
   int64_t bias_f32_bytes;   // prepared bias (either layout)
-  int64_t off_D, off_dqp, off_dbp, bwd_bytes;
+  int64_t off_D, off_L2, off_dqp, off_dbp, bwd_bytes;
 };
 
 constexpr int64_t kAlign = 256;
@@ -624,7 +711,8 @@ Plan make_plan(int64_t B, int64_t N, int64_t H, int64_t D) {
   p.rows = B * N * H * N;
   p.bias_f32_bytes = round_up(B * H * p.Kp * p.Jp * 4, kAlign);
   p.off_D = p.bias_f32_bytes;
-  p.off_dqp = p.off_D + round_up(p.rows * 4, kAlign);
+  p.off_L2 = p.off_D + round_up(B * N * H * p.Jp * 4, kAlign);
+  p.off_dqp = p.off_L2 + round_up(B * N * H * p.Jp * 4, kAlign);
   p.off_dbp = p.off_dqp + round_up(p.KB * p.elems * 4, kAlign);
   p.bwd_bytes = p.off_dbp + round_up(p.ngroups * B * H * N * N * 4, kAlign);
   return p;
@@ -680,24 +768,27 @@ tri_attn_status launch_bwd(unsigned stages, const Plan& P, const void* q, const 
   char* base = (char*)ws;
   float* biasT = (float*)base;
   float* Dg = (float*)(base + P.off_D);
+  float* L2g = (float*)(base + P.off_L2);
   float* dqp = (float*)(base + P.off_dqp);
   float* dbp = (float*)(base + P.off_dbp);
   const int64_t nb = P.B * P.H * P.Kp * P.Jp;
   if (stages & TRI_ATTN_STAGE_PREP) {
     hipLaunchKernelGGL(bias_prep_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, st, (const bf16*)bias,
                        biasT, (int)P.N, (int)P.Kp, (int)P.Jp, false, 1.0f / alpha, nb);
-    hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3((unsigned)((P.rows + 255) / 256)), dim3(256), 0, st,
-                       (const bf16*)dO, (const bf16*)o, (const bf16*)res, Dg, P.rows);
+    const int64_t nrows = P.B * P.N * P.H;
+    hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3((unsigned)(nrows * P.Jp * (D / 8) / 256)), dim3(256), 0, st,
+                       (const bf16*)dO, (const bf16*)o, (const bf16*)res, lse, Dg, L2g, (int)P.N, (int)P.Jp,
+                       nrows);
   }
   const int64_t ntiles = P.B * P.H * P.ngroups * P.KB;
   if (!(stages & TRI_ATTN_STAGE_MAIN)) {
   } else if (mask)
     hipLaunchKernelGGL((bwd_kernel<D, true>), dim3(grid_xcd(ntiles)), dim3(512), 0, st, (const bf16*)q,
-                       (const bf16*)k, (const bf16*)v, (const bf16*)dO, biasT, mask, lse, Dg, dqp, dbp, (bf16*)dk,
+                       (const bf16*)k, (const bf16*)v, (const bf16*)dO, biasT, mask, L2g, Dg, dqp, dbp, (bf16*)dk,
                        (bf16*)dv, (int)P.B, (int)P.N, (int)P.H, (int)P.G, (int)P.ngroups, alpha);
   else
     hipLaunchKernelGGL((bwd_kernel<D, false>), dim3(grid_xcd(ntiles)), dim3(512), 0, st, (const bf16*)q,
-                       (const bf16*)k, (const bf16*)v, (const bf16*)dO, biasT, mask, lse, Dg, dqp, dbp, (bf16*)dk,
+                       (const bf16*)k, (const bf16*)v, (const bf16*)dO, biasT, mask, L2g, Dg, dqp, dbp, (bf16*)dk,
                        (bf16*)dv, (int)P.B, (int)P.N, (int)P.H, (int)P.G, (int)P.ngroups, alpha);
   if (stages & TRI_ATTN_STAGE_FINAL) {
     const int64_t n4 = P.elems / 4;
