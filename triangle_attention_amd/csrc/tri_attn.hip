@@ -396,7 +396,9 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   const int b = (int)(rest / H);
   const int i_begin = grp * G, i_end = min(N, i_begin + G);
 
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 5, ln = l & 31;
+  // the wave index is uniform; readfirstlane lets the compiler keep everything derived
+  // from it (LDS destinations, tile offsets) in scalar registers
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, g = l >> 5, ln = l & 31;
   const int kh = w & 1, p = w >> 1;
   const int G16 = l >> 4, chalf = G16 & 1;
   const int kl = kh * 32 + ln;          // key within the block

@@ -1,0 +1,61 @@
+"""Small workloads for hardware-counter runs under rocprofv3.
+
+  python3 -m triangle_attention_amd.profile_drv attn [workload] [reps]
+      forward + backward of a synthetic workload through the C ABI, `reps` times
+  python3 -m triangle_attention_amd.profile_drv copy [mib] [reps]
+      a plain device-to-device copy of `mib` MiB (torch's copy kernel), used to
+      calibrate FETCH_SIZE / WRITE_SIZE against a known byte count
+"""
+from __future__ import annotations
+
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def _attn(name: str, reps: int):
+    import numpy as np
+    import torch
+
+    import triangle_attention_amd as ta
+    from tri_synth import WORKLOADS, workload_inputs
+
+    w = WORKLOADS[name]
+    inp = workload_inputs(w)
+
+    def dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+    q, k, v, bias, dO = (dev(inp[n]) for n in ("q", "k", "v", "bias", "dO"))
+    m = None if inp["key_mask"] is None else torch.from_numpy(inp["key_mask"]).cuda()
+    for _ in range(reps):
+        o, lse, res = ta.forward(q, k, v, bias, m)
+        ta.backward(q, k, v, bias, m, o, lse, res, dO)
+    torch.cuda.synchronize()
+    print(f"attn {name} x{reps} done", flush=True)
+
+
+def _copy(mib: int, reps: int):
+    import torch
+
+    a = torch.zeros(mib << 18, dtype=torch.float32, device="cuda")  # mib MiB
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(f"copy {mib} MiB x{reps} done", flush=True)
+
+
+def main(argv):
+    what = argv[1] if len(argv) > 1 else "attn"
+    if what == "copy":
+        _copy(int(argv[2]) if len(argv) > 2 else 256, int(argv[3]) if len(argv) > 3 else 3)
+    else:
+        _attn(argv[2] if len(argv) > 2 else "n768_h4_d32", int(argv[3]) if len(argv) > 3 else 3)
+
+
+if __name__ == "__main__":
+    main(sys.argv)
