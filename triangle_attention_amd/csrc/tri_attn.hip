@@ -116,33 +116,48 @@ __host__ __device__ __forceinline__ int64_t ctile_off(int m, int n) {
 }
 
 // ------------------------------------------------------------------ bias preparation
-// biasF: forward operand, tiles indexed (b,h, jb, kb), element (row m = key k%32,
-// column n = query j%32); value bias[b,h,j,k]/alpha, -inf for k >= N.
-// biasT: backward operand, tiles (b,h, kb, jb), element (row m = query, column n = key);
-// value bias[b,h,j,k]/alpha, -inf if j >= N or k >= N.
-__global__ void bias_prep_kernel(const bf16* __restrict__ bias, float* __restrict__ out, int N,
-                                 int Rp, int Cp, bool fwd, float inv_alpha, int64_t total) {
+// biasF: forward operand, 32x32 tiles indexed (b,h, query block, key block), element
+// (row m = key k%32, column n = query j%32) in accumulator order; value bias[b,h,j,k]/alpha,
+// -inf for k >= N, 0 for padded queries j >= N.
+__global__ void bias_prep_fwd_kernel(const bf16* __restrict__ bias, float* __restrict__ out, int N, int Jp, int Kp,
+                                     float inv_alpha, int64_t total) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= total) return;
-  // decode idx -> (bh, rb, cb, in-tile offset); tiles are 32x32 over (row block rb, col block cb)
   const int64_t tile = idx >> 10;
   const int off = (int)(idx & 1023);
   const int e = off & 3, n = (off >> 2) & 31, Rg = off >> 7;  // Rg = R*2+g
   const int m = (Rg >> 1) * 8 + (Rg & 1) * 4 + e;
-  const int ncb = Cp / 32, nrb = Rp / 32;
+  const int ncb = Kp / 32, nrb = Jp / 32;
   const int cb = (int)(tile % ncb);
   const int rb = (int)((tile / ncb) % nrb);
   const int64_t bh = tile / ((int64_t)ncb * nrb);
-  // forward tiles: rows = query blocks (rb), inside a tile row m = key, column n = query
-  // backward tiles: rows = key blocks (rb), inside a tile row m = query, column n = key
-  int j, k;
-  if (fwd) { j = rb * 32 + n; k = cb * 32 + m; }
-  else     { k = rb * 32 + n; j = cb * 32 + m; }
+  const int j = rb * 32 + n, k = cb * 32 + m;
   float val;
   if (k >= N) val = -INFINITY;
-  else if (j >= N) val = fwd ? 0.0f : -INFINITY;
+  else if (j >= N) val = 0.0f;
   else val = (float)bias[(bh * N + j) * N + k] * inv_alpha;
   out[idx] = val;
+}
+
+// biasB: backward operand, bf16, one contiguous block per (b, h, 64-key block kb) that the
+// backward work-group copies into LDS as is.  Inside a block: 128-query step s, then tile
+// t = 4*kh + p (key half kh, 32-query tile p), then 1024 values in lane order
+// [half hf][lane 32g+n][8]: position 4R'+e of the 8 holds query 128s + 32p + 8(2hf+R') + 4g + e
+// and key 64kb + 32kh + n, i.e. accumulator register 8hf+4R'+e of lane 32g+n of the 32x32
+// score tile.  The value is the bias itself (exact), -inf where j >= N or k >= N.
+__global__ void bias_prep_bwd_kernel(const bf16* __restrict__ bias, bf16* __restrict__ out, int N, int KB, int nsteps,
+                                     int64_t total) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= total) return;
+  const int off = (int)(idx & 1023), t = (int)((idx >> 10) & 7);
+  int64_t rest = idx >> 13;
+  const int s = (int)(rest % nsteps); rest /= nsteps;
+  const int kb = (int)(rest % KB);
+  const int64_t bh = rest / KB;
+  const int e = off & 3, R = ((off >> 9) << 1) | ((off >> 2) & 1), lane = (off >> 3) & 63;
+  const int j = s * 128 + (t & 3) * 32 + R * 8 + (lane >> 5) * 4 + e;
+  const int k = kb * 64 + (t >> 2) * 32 + (lane & 31);
+  out[idx] = (j < N && k < N) ? bias[(bh * N + j) * N + k] : (bf16)(-INFINITY);
 }
 
 // ------------------------------------------------------------------ forward
@@ -344,11 +359,16 @@ void bwd_pre_kernel(const bf16* __restrict__ dO, const bf16* __restrict__ o, con
 // summed over slices on chip and written once per group.  The steps of a slice are
 // unrolled at compile time so that every face slot is addressed statically.
 //
-// Software pipeline: while item t is computed, item t+1's Q, dO, bias tiles, lse2 and D
-// (and K, V at a slice boundary) stream from global memory straight into the other half
-// of double-buffered LDS (global_load_lds_dwordx4, no registers involved).  Rows past N
-// are loaded from row N-1: the -inf padding of the prepared bias turns every padded query
-// or key into an exact zero probability, so their contents never matter.
+// The pair bias is the same for every slice, so the work-group's whole bias column
+// (all queries x its 64 keys, bf16, 96 KiB at N = 768) is loaded into LDS once and stays
+// there for the slice group.
+//
+// Software pipeline: while item t is computed, item t+1's Q, dO, lse2 and D stream from
+// global memory straight into the other half of double-buffered LDS
+// (global_load_lds_dwordx4, no registers involved); the next slice's K and V follow once
+// the last item of a slice has finished reading them.  Rows past N are loaded from row
+// N-1: the -inf padding of the prepared bias turns every padded query or key into an
+// exact zero probability, so their contents never matter.
 //
 // Rows of Q, dO, K and V in LDS hold their 16-byte chunks in XOR-swizzled order (chunk c
 // of row r sits in slot c ^ swz(r)), which spreads the row-wise operand reads of a wave
@@ -368,22 +388,24 @@ __device__ __forceinline__ int swz(int row) {
 template <int D, bool MASK>
 __global__ __launch_bounds__(512, 1)
 void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-                const bf16* __restrict__ dO, const float* __restrict__ biasT, const uint8_t* __restrict__ mask,
+                const bf16* __restrict__ dO, const bf16* __restrict__ biasB, const uint8_t* __restrict__ mask,
                 const float* __restrict__ L2p, const float* __restrict__ Dp,
                 float* __restrict__ dqp, float* __restrict__ dbp, bf16* __restrict__ dk, bf16* __restrict__ dv,
-                int B, int N, int H, int G, int ngroups, float alpha) {
+                int B, int N, int H, int G, int ngroups, float alpha, float inv_alpha) {
   constexpr int NC = D / 16;
   constexpr int CPR = D / 8;    // 16-byte chunks per row
   constexpr int LDT = 128 + 8;  // dS^T row stride (elements), padded
   constexpr int NR = D / 2;     // accumulator registers of dK^T / dV^T holding channels c < D
-  __shared__ __attribute__((aligned(16))) bf16 Qs_[2][128 * D];
-  __shared__ __attribute__((aligned(16))) bf16 dOs_[2][128 * D];
-  __shared__ __attribute__((aligned(16))) float bS_[2][8 * 1024];  // bias tiles [kh][p][1024]
-  __shared__ __attribute__((aligned(16))) float lS_[2][128];
-  __shared__ __attribute__((aligned(16))) float DS_[2][128];
-  __shared__ __attribute__((aligned(16))) bf16 Ks_[2][64 * D];
-  __shared__ __attribute__((aligned(16))) bf16 Vs_[2][64 * D];
-  __shared__ __attribute__((aligned(16))) bf16 dST_[64 * LDT];
+  // LDS map (bytes): bias column | Q,dO of buffer 0 | dS^T | Q,dO of buffer 1 | K, V | lse2, D.
+  // Buffer 0 + dS^T and dS^T + buffer 1 are contiguous: the end-of-slice dK/dV reduction
+  // uses whichever of the two ranges holds no prefetched data.
+  constexpr int kBiasBytes = kBwdMaxSteps * 8 * 1024 * 2;
+  constexpr int kQD = 2 * 128 * D * 2;
+  constexpr int oQD0 = kBiasBytes, oDST = oQD0 + kQD, oQD1 = oDST + 64 * LDT * 2, oK = oQD1 + kQD;
+  constexpr int oV = oK + 64 * D * 2, oL = oV + 64 * D * 2, oDv = oL + 2 * 128 * 4, kLdsBytes = oDv + 2 * 128 * 4;
+  static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+  static_assert(4 * 2 * NR * 64 * 4 <= kQD + 64 * LDT * 2, "dK/dV reduction scratch");
+  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
 
   const int KB = (N + 63) / 64;
   const int64_t ntiles = (int64_t)B * H * ngroups * KB;
@@ -400,18 +422,17 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   // from it (LDS destinations, tile offsets) in scalar registers
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, g = l >> 5, ln = l & 31;
   const int kh = w & 1, p = w >> 1;
-  const int G16 = l >> 4, chalf = G16 & 1;
   const int kl = kh * 32 + ln;          // key within the block
   const int kg = kb * 64 + kl;          // global key of this lane
   const bool kok = kg < N;
-  const int Kp = (int)round_up(N, 64), Jp = (int)round_up(N, 128);
-  const float* bT = biasT + ((int64_t)(b * H + h) * (Kp / 32) + kb * 2) * (int64_t)(Jp / 32) * 1024;
+  const int Jp = (int)round_up(N, 128);
   const float c1 = alpha * kLog2e;
   const float mneg = kMaskNeg / alpha;
   const int64_t slice_elems = (int64_t)N * D;
   const int64_t dq_stride = (int64_t)B * N * H * slice_elems;  // one full dq partial
   const int nsteps = (N + 127) / 128;
 
+  auto qd_off = [](int buf) { return buf ? oQD1 : oQD0; };
 
   // ---- per-lane LDS offsets (elements) of the operand reads
   // natural row reads: row rr, chunk c -> rr*D + ((c ^ swz(rr)) * 8)
@@ -423,50 +444,49 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   };
 
   // issue the loads of work item (ii, ss) into LDS buffer `buf`; each lane fetches the global
-  // chunk that belongs in its LDS slot (swizzled for Q, dO, K, V).  Bases are uniform, lane
+  // chunk that belongs in its LDS slot (swizzled for Q and dO).  Bases are uniform, lane
   // offsets 32-bit.
   auto prefetch = [&](int ii, int ss, int buf) {
     int tx = tid;
     asm volatile("" : "+v"(tx));  // keep the per-lane address math local to this call
     const int j0 = ss * 128;
     const int64_t sl = ((int64_t)b * N + ii) * H + h;  // slice-head row index
-    const bf16* qb = q + sl * slice_elems;
-    const bf16* ob = dO + sl * slice_elems;
     if (tx < 128 * CPR) {
       const int pr_row = tx / CPR;
       const unsigned off = (unsigned)(min(j0 + pr_row, N - 1) * D + ((tx % CPR) ^ swz<D>(pr_row)) * 8);
-      dma16(qb + off, &Qs_[buf][w * 512]);
-      dma16(ob + off, &dOs_[buf][w * 512]);
+      dma16(q + sl * slice_elems + off, lds + qd_off(buf) + w * 1024);
+      dma16(dO + sl * slice_elems + off, lds + qd_off(buf) + 128 * D * 2 + w * 1024);
     }
-    const float* bts = bT + ss * 4096;
-#pragma unroll
-    for (int m = 0; m < 4; m++) {
-      const unsigned f = (unsigned)(tx + 512 * m) * 4u;
-      dma16(bts + ((f >> 12) * (unsigned)(Jp / 32) * 1024u + (f & 4095u)), &bS_[buf][(w * 64 + 512 * m) * 4]);
-    }
-    const float* l2b = L2p + sl * Jp + j0;
-    const float* db = Dp + sl * Jp + j0;
-    if (w == 0 && l < 32) dma16(l2b + 4 * tx, &lS_[buf][0]);
-    if (w == 1 && l < 32) dma16(db + 4 * (tx - 64), &DS_[buf][0]);
-    if (ss == 0) {  // first step of a slice: its K and V blocks
-      constexpr int KC = 64 * CPR;  // 16-byte chunks per block
-      const int kvb = (ii - i_begin) & 1;
-      const int kv_t = tx < 256 ? tx : tx - 256;  // K (waves 0-3) / V (waves 4-7)
-      const int kv_row = kv_t / CPR;
-      const unsigned off = (unsigned)(min(kb * 64 + kv_row, N - 1) * D + ((kv_t % CPR) ^ swz<D>(kv_row)) * 8);
-      if (tx < KC) dma16(k + sl * slice_elems + off, &Ks_[kvb][w * 512]);
-      else if (tx >= 256 && tx < 256 + KC) dma16(v + sl * slice_elems + off, &Vs_[kvb][(w - 4) * 512]);
-    }
+    if (w == 0 && l < 32) dma16(L2p + sl * Jp + j0 + 4 * tx, lds + oL + buf * 512);
+    if (w == 1 && l < 32) dma16(Dp + sl * Jp + j0 + 4 * (tx - 64), lds + oDv + buf * 512);
   };
+  // K and V blocks of slice ii (single buffer: issued once the previous slice is done with it)
+  auto prefetch_kv = [&](int ii) {
+    int tx = tid;
+    asm volatile("" : "+v"(tx));
+    constexpr int KC = 64 * CPR;  // 16-byte chunks per block
+    const int64_t sl = ((int64_t)b * N + ii) * H + h;
+    const int kv_t = tx < 256 ? tx : tx - 256;  // K (waves 0-3) / V (waves 4-7)
+    const int kv_row = kv_t / CPR;
+    const unsigned off = (unsigned)(min(kb * 64 + kv_row, N - 1) * D + ((kv_t % CPR) ^ swz<D>(kv_row)) * 8);
+    if (tx < KC) dma16(k + sl * slice_elems + off, lds + oK + w * 1024);
+    else if (tx >= 256 && tx < 256 + KC) dma16(v + sl * slice_elems + off, lds + oV + (w - 4) * 1024);
+  };
+
+  // the bias column of this work-group: nsteps * 16 KiB, contiguous in the prepared layout
+  {
+    const bf16* src = biasB + ((int64_t)(b * H + h) * KB + kb) * (int64_t)nsteps * 8192;
+    for (int c = w; c < nsteps * 16; c += 8) dma16(src + c * 512 + l * 8, lds + c * 1024);
+  }
 
   f32x16 face[kBwdMaxSteps];
 #pragma unroll
   for (int s = 0; s < kBwdMaxSteps; s++) face[s] = f32x16{};
 
   prefetch(i_begin, 0, 0);
+  prefetch_kv(i_begin);
   int cur = 0;
   for (int i = i_begin; i < i_end; i++) {
-    const int kvb = (i - i_begin) & 1;
     const int64_t sbase = (((int64_t)b * N + i) * H + h) * slice_elems;
     float madd = 0.0f;
     f32x16 dkT = {}, dvT = {};
@@ -481,7 +501,8 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
       const int g = lx >> 5, ln = lx & 31, G16 = lx >> 4, chalf = G16 & 1;
       const int kl = kh * 32 + ln, rq = p * 32 + ln, rk = kl;
       // item (i, s) was issued before the previous item's dq stores (and, at a slice
-      // boundary, before the previous slice's dk/dv stores, where everything is drained)
+      // boundary, before the previous slice's K/V loads and dk/dv stores, where everything
+      // is drained)
       if (s == 0) {
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         if (MASK) madd = (kok && !mask[((int64_t)b * N + i) * N + kg]) ? mneg : 0.0f;
@@ -494,22 +515,24 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
       if (s + 1 < nsteps) prefetch(i, s + 1, cur ^ 1);
       else if (i + 1 < i_end) prefetch(i + 1, 0, cur ^ 1);
 
-      const lbf16* Qs = (const lbf16*)Qs_[cur];
-      const lbf16* dOs = (const lbf16*)dOs_[cur];
-      const lbf16* Ks = (const lbf16*)Ks_[kvb];
-      const lbf16* Vs = (const lbf16*)Vs_[kvb];
-      const lf32* bS = (const lf32*)bS_[cur] + (kh * 4 + p) * 1024;
-      const lf32* lS = (const lf32*)lS_[cur];
-      const lf32* DSv = (const lf32*)DS_[cur];
-      lbf16* dST = (lbf16*)dST_;
+      const lbf16* Qs = (const lbf16*)(lds + qd_off(cur));
+      const lbf16* dOs = (const lbf16*)(lds + qd_off(cur) + 128 * D * 2);
+      const lbf16* Ks = (const lbf16*)(lds + oK);
+      const lbf16* Vs = (const lbf16*)(lds + oV);
+      const lbf16* bS = (const lbf16*)lds + ((s * 2 + kh) * 4 + p) * 1024 + lx * 8;
+      const lf32* lS = (const lf32*)(lds + oL) + cur * 128;
+      const lf32* DSv = (const lf32*)(lds + oDv) + cur * 128;
+      lbf16* dST = (lbf16*)(lds + oDST);
 
       // S = bias/alpha + Q K^T  and  dP = dO V^T   (rows: 32 queries, cols: 32 keys)
       f32x16 sacc, dp = {};
+      {
+        const bf16x8 b0 = *(const lbf16x8*)bS, b1 = *(const lbf16x8*)(bS + 512);
 #pragma unroll
-      for (int R = 0; R < 4; R++) {
-        const f32x4 bv = *(const lf32x4*)(bS + ((R * 2 + g) * 32 + ln) * 4);
-        sacc[R * 4 + 0] = bv[0]; sacc[R * 4 + 1] = bv[1];
-        sacc[R * 4 + 2] = bv[2]; sacc[R * 4 + 3] = bv[3];
+        for (int r = 0; r < 8; r++) {
+          sacc[r] = (float)b0[r] * inv_alpha;
+          sacc[r + 8] = (float)b1[r] * inv_alpha;
+        }
       }
 #pragma unroll
       for (int cc = 0; cc < NC; cc++) {
@@ -589,9 +612,13 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
     if (nsteps > 5) step(std::integral_constant<int, 5>{});
     static_assert(kBwdMaxSteps == 6, "six unrolled steps");
 
+    __syncthreads();  // every wave is past the last dQ product: K, V and dS^T are free
+    if (i + 1 < i_end) prefetch_kv(i + 1);
+
     // end of slice i: dK^T, dV^T summed over the four query lanes as (p0 + p1) + (p2 + p3),
-    // in the bias buffer of the last item (no longer read; the prefetch targets the other one)
-    lf32* red = (lf32*)bS_[cur ^ 1];
+    // in the Q/dO buffer of the last item and the dS^T area next to it (the prefetch of the
+    // next slice's first item targets the other buffer)
+    lf32* red = (lf32*)(lds + (cur ? oQD0 : oDST));
     const int slot_w = (kh * 2 + (p >> 1)) * (2 * NR * 64) + l;
     if (p & 1) {
 #pragma unroll
@@ -651,28 +678,46 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
 
 // ------------------------------------------------------------------ backward: ordered sums
 // dq = bf16(alpha * sum_kb dqp[kb]) with kb ascending; dbias = sum_g dbp[g] with g ascending.
+// All loads of a thread are issued before the sum (indexes past the last partial re-read it
+// and are not added), so the kernels stream at memory speed instead of one latency per term.
 __global__ __launch_bounds__(256)
 void reduce_dq_kernel(const float* __restrict__ dqp, bf16* __restrict__ dq, int KB, int64_t n4, float alpha) {
+  constexpr int kMaxKB = TRI_ATTN_MAX_N / 64;
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= n4) return;
-  f32x4 s = *(const f32x4*)(dqp + t * 4);
-  for (int kb = 1; kb < KB; kb++) {
-    const f32x4 x = *(const f32x4*)(dqp + (int64_t)kb * n4 * 4 + t * 4);
-    s += x;
-  }
+  f32x4 x[kMaxKB];
+#pragma unroll
+  for (int kb = 0; kb < kMaxKB; kb++) x[kb] = *(const f32x4*)(dqp + ((int64_t)min(kb, KB - 1) * n4 + t) * 4);
+  f32x4 s = x[0];
+#pragma unroll
+  for (int kb = 1; kb < kMaxKB; kb++)
+    if (kb < KB) s += x[kb];
   bf16x4 r;
 #pragma unroll
   for (int e = 0; e < 4; e++) r[e] = (bf16)(s[e] * alpha);
   *(bf16x4*)(dq + t * 4) = r;
 }
 
+// VEC: four adjacent elements per thread (n divisible by 4, so every partial stays 16-byte aligned)
+template <bool VEC>
 __global__ __launch_bounds__(256)
 void reduce_dbias_kernel(const float* __restrict__ dbp, float* __restrict__ dbias, int ngroups, int64_t n) {
+  typedef typename std::conditional<VEC, f32x4, float>::type T;
+  constexpr int W = VEC ? 4 : 1, U = 8;
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= n) return;
-  float s = dbp[t];
-  for (int g = 1; g < ngroups; g++) s += dbp[(int64_t)g * n + t];
-  dbias[t] = s;
+  if (t * W >= n) return;
+  T s = {};
+  for (int g0 = 0; g0 < ngroups; g0 += U) {
+    T x[U];
+#pragma unroll
+    for (int u = 0; u < U; u++) x[u] = *(const T*)(dbp + (int64_t)min(g0 + u, ngroups - 1) * n + t * W);
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      if (g0 + u == 0) s = x[u];
+      else if (g0 + u < ngroups) s += x[u];
+    }
+  }
+  *(T*)(dbias + t * W) = s;
 }
 
 // ------------------------------------------------------------------ host side
@@ -684,7 +729,8 @@ struct Plan {
   int64_t ngroups, G;       // slice groups of the backward and slices per group
   int64_t elems;            // B*N*H*N*D
   int64_t rows;             // B*N*H*N
-  int64_t bias_f32_bytes;   // prepared bias (either layout)
+  int64_t bias_f32_bytes;   // prepared forward bias (FP32 tiles)
+  int64_t bias_b16_bytes;   // prepared backward bias (bf16 column blocks)
   int64_t off_D, off_L2, off_dqp, off_dbp, bwd_bytes;
 };
 
@@ -712,7 +758,8 @@ Plan make_plan(int64_t B, int64_t N, int64_t H, int64_t D) {
   p.elems = B * N * H * N * D;
   p.rows = B * N * H * N;
   p.bias_f32_bytes = round_up(B * H * p.Kp * p.Jp * 4, kAlign);
-  p.off_D = p.bias_f32_bytes;
+  p.bias_b16_bytes = round_up(B * H * p.Kp * p.Jp * 2, kAlign);
+  p.off_D = p.bias_b16_bytes;
   p.off_L2 = p.off_D + round_up(B * N * H * p.Jp * 4, kAlign);
   p.off_dqp = p.off_L2 + round_up(B * N * H * p.Jp * 4, kAlign);
   p.off_dbp = p.off_dqp + round_up(p.KB * p.elems * 4, kAlign);
@@ -747,8 +794,8 @@ tri_attn_status launch_fwd(unsigned stages, const Plan& P, const void* q, const 
   float* biasF = (float*)ws;
   const int64_t nb = P.B * P.H * P.Jp * P.Kp;
   if (stages & TRI_ATTN_STAGE_PREP)
-    hipLaunchKernelGGL(bias_prep_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, st, (const bf16*)bias,
-                       biasF, (int)P.N, (int)P.Jp, (int)P.Kp, true, 1.0f / alpha, nb);
+    hipLaunchKernelGGL(bias_prep_fwd_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, st,
+                       (const bf16*)bias, biasF, (int)P.N, (int)P.Jp, (int)P.Kp, 1.0f / alpha, nb);
   const int64_t ntiles = P.B * P.H * P.N * ((P.N + 127) / 128);
   if (!(stages & TRI_ATTN_STAGE_MAIN)) {
   } else if (mask)
@@ -768,15 +815,15 @@ tri_attn_status launch_bwd(unsigned stages, const Plan& P, const void* q, const 
                            void* dq, void* dk, void* dv, float* dbias, void* ws, hipStream_t st) {
   const float alpha = 1.0f / sqrtf((float)D);
   char* base = (char*)ws;
-  float* biasT = (float*)base;
+  bf16* biasB = (bf16*)base;
   float* Dg = (float*)(base + P.off_D);
   float* L2g = (float*)(base + P.off_L2);
   float* dqp = (float*)(base + P.off_dqp);
   float* dbp = (float*)(base + P.off_dbp);
   const int64_t nb = P.B * P.H * P.Kp * P.Jp;
   if (stages & TRI_ATTN_STAGE_PREP) {
-    hipLaunchKernelGGL(bias_prep_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, st, (const bf16*)bias,
-                       biasT, (int)P.N, (int)P.Kp, (int)P.Jp, false, 1.0f / alpha, nb);
+    hipLaunchKernelGGL(bias_prep_bwd_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, st,
+                       (const bf16*)bias, biasB, (int)P.N, (int)P.KB, (int)(P.Jp / 128), nb);
     const int64_t nrows = P.B * P.N * P.H;
     hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3((unsigned)(nrows * P.Jp * (D / 8) / 256)), dim3(256), 0, st,
                        (const bf16*)dO, (const bf16*)o, (const bf16*)res, lse, Dg, L2g, (int)P.N, (int)P.Jp,
@@ -786,19 +833,23 @@ tri_attn_status launch_bwd(unsigned stages, const Plan& P, const void* q, const 
   if (!(stages & TRI_ATTN_STAGE_MAIN)) {
   } else if (mask)
     hipLaunchKernelGGL((bwd_kernel<D, true>), dim3(grid_xcd(ntiles)), dim3(512), 0, st, (const bf16*)q,
-                       (const bf16*)k, (const bf16*)v, (const bf16*)dO, biasT, mask, L2g, Dg, dqp, dbp, (bf16*)dk,
-                       (bf16*)dv, (int)P.B, (int)P.N, (int)P.H, (int)P.G, (int)P.ngroups, alpha);
+                       (const bf16*)k, (const bf16*)v, (const bf16*)dO, biasB, mask, L2g, Dg, dqp, dbp, (bf16*)dk,
+                       (bf16*)dv, (int)P.B, (int)P.N, (int)P.H, (int)P.G, (int)P.ngroups, alpha, 1.0f / alpha);
   else
     hipLaunchKernelGGL((bwd_kernel<D, false>), dim3(grid_xcd(ntiles)), dim3(512), 0, st, (const bf16*)q,
-                       (const bf16*)k, (const bf16*)v, (const bf16*)dO, biasT, mask, L2g, Dg, dqp, dbp, (bf16*)dk,
-                       (bf16*)dv, (int)P.B, (int)P.N, (int)P.H, (int)P.G, (int)P.ngroups, alpha);
+                       (const bf16*)k, (const bf16*)v, (const bf16*)dO, biasB, mask, L2g, Dg, dqp, dbp, (bf16*)dk,
+                       (bf16*)dv, (int)P.B, (int)P.N, (int)P.H, (int)P.G, (int)P.ngroups, alpha, 1.0f / alpha);
   if (stages & TRI_ATTN_STAGE_FINAL) {
     const int64_t n4 = P.elems / 4;
     hipLaunchKernelGGL(reduce_dq_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, dqp, (bf16*)dq,
                        (int)P.KB, n4, alpha);
     const int64_t nbias = P.B * P.H * P.N * P.N;
-    hipLaunchKernelGGL(reduce_dbias_kernel, dim3((unsigned)((nbias + 255) / 256)), dim3(256), 0, st, dbp, dbias,
-                       (int)P.ngroups, nbias);
+    if (nbias % 4 == 0)
+      hipLaunchKernelGGL(reduce_dbias_kernel<true>, dim3((unsigned)((nbias / 4 + 255) / 256)), dim3(256), 0, st, dbp,
+                         dbias, (int)P.ngroups, nbias);
+    else
+      hipLaunchKernelGGL(reduce_dbias_kernel<false>, dim3((unsigned)((nbias + 255) / 256)), dim3(256), 0, st, dbp,
+                         dbias, (int)P.ngroups, nbias);
   }
   return hipGetLastError() == hipSuccess ? TRI_ATTN_SUCCESS : TRI_ATTN_ERROR_LAUNCH;
 }
