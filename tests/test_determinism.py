@@ -39,6 +39,13 @@ def test_five_calls_bitwise_wide_bias_768():
     _five_calls_identical(workload_inputs(WORKLOADS["n768_h4_d16_bias4"]))
 
 
+@pytest.mark.parametrize("name", ["n768_h4_d32", "n640_h4_d16_mask64"])
+def test_five_calls_bitwise_full_size(name):
+    # the other full-size workloads (both head dimensions, with and without the key mask):
+    # every store of the dq partials is exercised at the benchmark's launch configuration
+    _five_calls_identical(workload_inputs(WORKLOADS[name]))
+
+
 def test_compensation_ablation_small():
     """dv does not depend on the correction D, so it is bitwise identical with and without the
     residual; the gradients that do (dq, dk, dbias) are reported against FP64 both ways."""

@@ -364,11 +364,11 @@ void bwd_pre_kernel(const bf16* __restrict__ dO, const bf16* __restrict__ o, con
 // there for the slice group.
 //
 // Software pipeline: while item t is computed, item t+1's Q, dO, lse2 and D stream from
-// global memory straight into the other half of double-buffered LDS
-// (global_load_lds_dwordx4, no registers involved); the next slice's K and V follow once
-// the last item of a slice has finished reading them.  Rows past N are loaded from row
-// N-1: the -inf padding of the prepared bias turns every padded query or key into an
-// exact zero probability, so their contents never matter.
+// global memory straight into the other half of double-buffered LDS (buffer loads to LDS,
+// no registers involved); the next slice's K and V follow once the last item of a slice
+// has finished reading them.  Rows past N read as zeros through the buffer range check,
+// and the -inf padding of the prepared bias turns every padded query or key into an exact
+// zero probability.
 //
 // Rows of Q, dO, K and V in LDS hold their 16-byte chunks in XOR-swizzled order (chunk c
 // of row r sits in slot c ^ swz(r)), which spreads the row-wise operand reads of a wave
@@ -377,6 +377,20 @@ constexpr int kBwdMaxSteps = 6;  // 6 steps x 128 queries = TRI_ATTN_MAX_N
 
 __device__ __forceinline__ void dma16(const void* g, void* lds_wave_base) {
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+}
+
+// Raw buffer resource over [base, base + bytes): loads past the end return zeros, which is how
+// rows beyond N are read below.  (Only loads go through buffer resources: the compiler's
+// wait-state rule for the store-data hazard of wide buffer stores does not cover the form
+// with a register scalar offset on gfx950, where such stores were seen to write
+// overwritten data.  Global stores get the wait states.)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+// 16 bytes per lane from a buffer straight into LDS: lane l's bytes land at lds_wave_base + 16 l
+__device__ __forceinline__ void dma16b(__amdgpu_buffer_rsrc_t r, unsigned voff, int soff, void* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave_base, 16, voff, soff,
+                                           0, 0);
 }
 
 // chunk swizzle for rows of D bf16 (D/8 chunks of 16 bytes per row)
@@ -443,34 +457,32 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
     return rr * D + ((((col >> 3) ^ swz<D>(rr)) << 3) | (col & 7));
   };
 
-  // issue the loads of work item (ii, ss) into LDS buffer `buf`; each lane fetches the global
-  // chunk that belongs in its LDS slot (swizzled for Q and dO).  Bases are uniform, lane
-  // offsets 32-bit.
+  // Per-lane byte offsets of the streamed loads, fixed for the whole work-group; slice and
+  // step enter through the buffer base and the scalar offset.  Q and dO land swizzled.
+  const unsigned qd_vo = (unsigned)(((tid / CPR) * D + ((tid % CPR) ^ swz<D>(tid / CPR)) * 8) * 2);
+  const int kv_t = tid & 255;  // K (waves 0-3) / V (waves 4-7)
+  const unsigned kv_vo = (unsigned)(((kb * 64 + kv_t / CPR) * D + ((kv_t % CPR) ^ swz<D>(kv_t / CPR)) * 8) * 2);
+  const unsigned row_vo = (unsigned)(l & 31) * 16u;
+  const unsigned dq_vo = (unsigned)((((w >> 1) * 32 + (w & 1) * 16 + (l & 15)) * D + 4 * (l >> 4)) * 4);
+
+  // issue the loads of work item (ii, ss) into LDS buffer `buf`; rows past N read as zeros
   auto prefetch = [&](int ii, int ss, int buf) {
-    int tx = tid;
-    asm volatile("" : "+v"(tx));  // keep the per-lane address math local to this call
-    const int j0 = ss * 128;
     const int64_t sl = ((int64_t)b * N + ii) * H + h;  // slice-head row index
-    if (tx < 128 * CPR) {
-      const int pr_row = tx / CPR;
-      const unsigned off = (unsigned)(min(j0 + pr_row, N - 1) * D + ((tx % CPR) ^ swz<D>(pr_row)) * 8);
-      dma16(q + sl * slice_elems + off, lds + qd_off(buf) + w * 1024);
-      dma16(dO + sl * slice_elems + off, lds + qd_off(buf) + 128 * D * 2 + w * 1024);
+    if (w < 2 * CPR) {
+      dma16b(buf_rsrc(q + sl * slice_elems, N * D * 2), qd_vo, ss * 128 * D * 2, lds + qd_off(buf) + w * 1024);
+      dma16b(buf_rsrc(dO + sl * slice_elems, N * D * 2), qd_vo, ss * 128 * D * 2,
+             lds + qd_off(buf) + 128 * D * 2 + w * 1024);
     }
-    if (w == 0 && l < 32) dma16(L2p + sl * Jp + j0 + 4 * tx, lds + oL + buf * 512);
-    if (w == 1 && l < 32) dma16(Dp + sl * Jp + j0 + 4 * (tx - 64), lds + oDv + buf * 512);
+    if (w == 0 && l < 32) dma16b(buf_rsrc(L2p + sl * Jp, Jp * 4), row_vo, ss * 512, lds + oL + buf * 512);
+    if (w == 1 && l < 32) dma16b(buf_rsrc(Dp + sl * Jp, Jp * 4), row_vo, ss * 512, lds + oDv + buf * 512);
   };
   // K and V blocks of slice ii (single buffer: issued once the previous slice is done with it)
   auto prefetch_kv = [&](int ii) {
-    int tx = tid;
-    asm volatile("" : "+v"(tx));
     constexpr int KC = 64 * CPR;  // 16-byte chunks per block
     const int64_t sl = ((int64_t)b * N + ii) * H + h;
-    const int kv_t = tx < 256 ? tx : tx - 256;  // K (waves 0-3) / V (waves 4-7)
-    const int kv_row = kv_t / CPR;
-    const unsigned off = (unsigned)(min(kb * 64 + kv_row, N - 1) * D + ((kv_t % CPR) ^ swz<D>(kv_row)) * 8);
-    if (tx < KC) dma16(k + sl * slice_elems + off, lds + oK + w * 1024);
-    else if (tx >= 256 && tx < 256 + KC) dma16(v + sl * slice_elems + off, lds + oV + (w - 4) * 1024);
+    if (w < KC / 64) dma16b(buf_rsrc(k + sl * slice_elems, N * D * 2), kv_vo, 0, lds + oK + w * 1024);
+    else if (w >= 4 && w < 4 + KC / 64)
+      dma16b(buf_rsrc(v + sl * slice_elems, N * D * 2), kv_vo, 0, lds + oV + (w - 4) * 1024);
   };
 
   // the bias column of this work-group: nsteps * 16 KiB, contiguous in the prepared layout
@@ -586,8 +598,8 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
       __syncthreads();  // dS^T complete
       // dQ^T tiles (16 channels x 16 queries) over the 64 keys of this block
       {
-        float* dqs = dqp + (int64_t)kb * dq_stride + sbase;
-        const int jj = j0 + (w >> 1) * 32 + (w & 1) * 16 + (lx & 15);
+        char* dqs = (char*)(dqp + (int64_t)kb * dq_stride + sbase + (int64_t)j0 * D);
+        const bool rows_ok = j0 + 128 <= N || j0 + (int)(dq_vo / (D * 4)) < N;
         const int sT = 8 * G16 * LDT + (w >> 1) * 32 + (w & 1) * 16 + tr_lane(LDT);
 #pragma unroll
         for (int u = 0; u < NC; u++) {
@@ -598,7 +610,7 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
             const bf16x8 bb = cat8(tr16p(dST + sT + kk * LDT), tr16p(dST + sT + (kk + 4) * LDT));
             c = mfma16(a, bb, c);
           }
-          if (jj < N) *(f32x4*)(dqs + jj * D + u * 16 + 4 * G16) = c;
+          if (rows_ok) *(f32x4*)(dqs + (dq_vo + u * 64)) = c;
         }
       }
       cur ^= 1;
