@@ -100,6 +100,32 @@ __device__ __forceinline__ bf16x8 pack8(const float* f) {
   return r;
 }
 
+// The dq partials are FP32 values kept to 24 bits: sign, exponent and the top 15 mantissa
+// bits, rounded to nearest even (relative error <= 2^-16, 128x below the bf16 rounding of
+// the final dq).  Four of them pack into three dwords.  MFMA results are finite or the
+// canonical quiet NaN, which both survive the encoding.
+typedef unsigned u32x3 __attribute__((ext_vector_type(3)));
+__device__ __forceinline__ unsigned f24_bits(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  return (u + 0x7Fu + ((u >> 8) & 1u)) >> 8;
+}
+__device__ __forceinline__ u32x3 pack_f24x4(f32x4 v) {
+  const unsigned r0 = f24_bits(v[0]), r1 = f24_bits(v[1]), r2 = f24_bits(v[2]), r3 = f24_bits(v[3]);
+  u32x3 w;
+  w[0] = r0 | (r1 << 24);
+  w[1] = (r1 >> 8) | (r2 << 16);
+  w[2] = (r2 >> 16) | (r3 << 8);
+  return w;
+}
+__device__ __forceinline__ f32x4 unpack_f24x4(u32x3 w) {
+  f32x4 v;
+  v[0] = __builtin_bit_cast(float, w[0] << 8);
+  v[1] = __builtin_bit_cast(float, ((w[0] >> 24) | (w[1] << 8)) << 8);
+  v[2] = __builtin_bit_cast(float, ((w[1] >> 16) | (w[2] << 16)) << 8);
+  v[3] = __builtin_bit_cast(float, w[2] & 0xFFFFFF00u);
+  return v;
+}
+
 // Work-group id -> logical tile, so that tiles [x*per, (x+1)*per) run on XCD x.
 __device__ __forceinline__ int64_t xcd_tile(int64_t ntiles) {
   const int64_t per = (ntiles + kXcd - 1) / kXcd;
@@ -404,7 +430,7 @@ __global__ __launch_bounds__(512, 1)
 void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
                 const bf16* __restrict__ dO, const bf16* __restrict__ biasB, const uint8_t* __restrict__ mask,
                 const float* __restrict__ L2p, const float* __restrict__ Dp,
-                float* __restrict__ dqp, float* __restrict__ dbp, bf16* __restrict__ dk, bf16* __restrict__ dv,
+                unsigned* __restrict__ dqp, float* __restrict__ dbp, bf16* __restrict__ dk, bf16* __restrict__ dv,
                 int B, int N, int H, int G, int ngroups, float alpha, float inv_alpha) {
   constexpr int NC = D / 16;
   constexpr int CPR = D / 8;    // 16-byte chunks per row
@@ -443,7 +469,7 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   const float c1 = alpha * kLog2e;
   const float mneg = kMaskNeg / alpha;
   const int64_t slice_elems = (int64_t)N * D;
-  const int64_t dq_stride = (int64_t)B * N * H * slice_elems;  // one full dq partial
+  const int64_t dq_stride = (int64_t)B * N * H * slice_elems;  // elements of one full dq partial
   const int nsteps = (N + 127) / 128;
 
   auto qd_off = [](int buf) { return buf ? oQD1 : oQD0; };
@@ -463,7 +489,9 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   const int kv_t = tid & 255;  // K (waves 0-3) / V (waves 4-7)
   const unsigned kv_vo = (unsigned)(((kb * 64 + kv_t / CPR) * D + ((kv_t % CPR) ^ swz<D>(kv_t / CPR)) * 8) * 2);
   const unsigned row_vo = (unsigned)(l & 31) * 16u;
-  const unsigned dq_vo = (unsigned)((((w >> 1) * 32 + (w & 1) * 16 + (l & 15)) * D + 4 * (l >> 4)) * 4);
+  // dq partial of (query row, 4-channel group): 12 bytes at (row * D/4 + group) * 12
+  const int dq_row = (w >> 1) * 32 + (w & 1) * 16 + (l & 15);
+  const unsigned dq_vo = (unsigned)((dq_row * (D / 4) + (l >> 4)) * 12);
 
   // issue the loads of work item (ii, ss) into LDS buffer `buf`; rows past N read as zeros
   auto prefetch = [&](int ii, int ss, int buf) {
@@ -598,8 +626,8 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
       __syncthreads();  // dS^T complete
       // dQ^T tiles (16 channels x 16 queries) over the 64 keys of this block
       {
-        char* dqs = (char*)(dqp + (int64_t)kb * dq_stride + sbase + (int64_t)j0 * D);
-        const bool rows_ok = j0 + 128 <= N || j0 + (int)(dq_vo / (D * 4)) < N;
+        char* dqs = (char*)dqp + ((int64_t)kb * dq_stride + sbase + (int64_t)j0 * D) * 3;  // 3 bytes per element
+        const bool rows_ok = j0 + 128 <= N || j0 + dq_row < N;
         const int sT = 8 * G16 * LDT + (w >> 1) * 32 + (w & 1) * 16 + tr_lane(LDT);
 #pragma unroll
         for (int u = 0; u < NC; u++) {
@@ -610,7 +638,7 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
             const bf16x8 bb = cat8(tr16p(dST + sT + kk * LDT), tr16p(dST + sT + (kk + 4) * LDT));
             c = mfma16(a, bb, c);
           }
-          if (rows_ok) *(f32x4*)(dqs + (dq_vo + u * 64)) = c;
+          if (rows_ok) *(u32x3*)(dqs + (dq_vo + u * 48)) = pack_f24x4(c);
         }
       }
       cur ^= 1;
@@ -689,21 +717,22 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
 }
 
 // ------------------------------------------------------------------ backward: ordered sums
-// dq = bf16(alpha * sum_kb dqp[kb]) with kb ascending; dbias = sum_g dbp[g] with g ascending.
+// dq = bf16(alpha * sum_kb dqp[kb]) with kb ascending (partials decoded from their 24-bit
+// form); dbias = sum_g dbp[g] with g ascending.
 // All loads of a thread are issued before the sum (indexes past the last partial re-read it
 // and are not added), so the kernels stream at memory speed instead of one latency per term.
 __global__ __launch_bounds__(256)
-void reduce_dq_kernel(const float* __restrict__ dqp, bf16* __restrict__ dq, int KB, int64_t n4, float alpha) {
+void reduce_dq_kernel(const unsigned* __restrict__ dqp, bf16* __restrict__ dq, int KB, int64_t n4, float alpha) {
   constexpr int kMaxKB = TRI_ATTN_MAX_N / 64;
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= n4) return;
-  f32x4 x[kMaxKB];
+  u32x3 x[kMaxKB];
 #pragma unroll
-  for (int kb = 0; kb < kMaxKB; kb++) x[kb] = *(const f32x4*)(dqp + ((int64_t)min(kb, KB - 1) * n4 + t) * 4);
-  f32x4 s = x[0];
+  for (int kb = 0; kb < kMaxKB; kb++) x[kb] = *(const u32x3*)(dqp + ((int64_t)min(kb, KB - 1) * n4 + t) * 3);
+  f32x4 s = unpack_f24x4(x[0]);
 #pragma unroll
   for (int kb = 1; kb < kMaxKB; kb++)
-    if (kb < KB) s += x[kb];
+    if (kb < KB) s += unpack_f24x4(x[kb]);
   bf16x4 r;
 #pragma unroll
   for (int e = 0; e < 4; e++) r[e] = (bf16)(s[e] * alpha);
@@ -774,7 +803,7 @@ Plan make_plan(int64_t B, int64_t N, int64_t H, int64_t D) {
   p.off_D = p.bias_b16_bytes;
   p.off_L2 = p.off_D + round_up(B * N * H * p.Jp * 4, kAlign);
   p.off_dqp = p.off_L2 + round_up(B * N * H * p.Jp * 4, kAlign);
-  p.off_dbp = p.off_dqp + round_up(p.KB * p.elems * 4, kAlign);
+  p.off_dbp = p.off_dqp + round_up(p.KB * p.elems * 3, kAlign);
   p.bwd_bytes = p.off_dbp + round_up(p.ngroups * B * H * N * N * 4, kAlign);
   return p;
 }
@@ -830,7 +859,7 @@ tri_attn_status launch_bwd(unsigned stages, const Plan& P, const void* q, const 
   bf16* biasB = (bf16*)base;
   float* Dg = (float*)(base + P.off_D);
   float* L2g = (float*)(base + P.off_L2);
-  float* dqp = (float*)(base + P.off_dqp);
+  unsigned* dqp = (unsigned*)(base + P.off_dqp);
   float* dbp = (float*)(base + P.off_dbp);
   const int64_t nb = P.B * P.H * P.Kp * P.Jp;
   if (stages & TRI_ATTN_STAGE_PREP) {
