@@ -186,21 +186,63 @@ __global__ void bias_prep_bwd_kernel(const bf16* __restrict__ bias, bf16* __rest
   out[idx] = (j < N && k < N) ? bias[(bh * N + j) * N + k] : (bf16)(-INFINITY);
 }
 
+// ------------------------------------------------------------------ streaming helpers
+
+__device__ __forceinline__ void dma16(const void* g, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+}
+
+// Raw buffer resource over [base, base + bytes): loads past the end return zeros, which is how
+// rows beyond N are read below.  (Only loads go through buffer resources: the compiler's
+// wait-state rule for the store-data hazard of wide buffer stores does not cover the form
+// with a register scalar offset on gfx950, where such stores were seen to write
+// overwritten data.  Global stores get the wait states.)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+// 16 bytes per lane from a buffer straight into LDS: lane l's bytes land at lds_wave_base + 16 l
+__device__ __forceinline__ void dma16b(__amdgpu_buffer_rsrc_t r, unsigned voff, int soff, void* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave_base, 16, voff, soff,
+                                           0, 0);
+}
+
+// chunk swizzle for rows of D bf16 (D/8 chunks of 16 bytes per row)
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  return D == 32 ? ((row >> 2) & 3) : ((row >> 3) & 1);
+}
+
+// Element offset, in a row-swizzled [rows][D] bf16 tile, of the 8 bytes this lane reads for a
+// transposed load of the 4-row group starting at r0 (column block c0, 16 columns).
+template <int D>
+__device__ __forceinline__ int tr_off(int lane, int r0, int c0) {
+  const int t16 = lane & 15;
+  const int rr = r0 + (t16 >> 2), col = c0 + 4 * (t16 & 3);
+  return rr * D + ((((col >> 3) ^ swz<D>(rr)) << 3) | (col & 7));
+}
+
 // ------------------------------------------------------------------ forward
 // One work-group = 4 waves = 128 queries of one slice (b,i,h); wave w owns 32 queries.
 // S^T (keys x queries) = K Q^T on 32x32x16 MFMA: each lane holds one query column and
 // 16 keys per 32-key tile, so the running max/sum of a query needs one cross-lane step.
+// The accumulator of each score tile starts from the prepared bias/alpha tile.
+//
+// Software pipeline over 64-key tiles: while tile t is computed, tile t+1's K and V (shared
+// by the work-group) and each wave's two bias tiles stream into the other half of
+// double-buffered LDS (buffer loads to LDS); keys past N read as zeros and carry a -inf
+// bias.  K and V rows are XOR-swizzled like the backward's.
 template <int D, bool MASK>
-__global__ __launch_bounds__(256, 2)
+__global__ __launch_bounds__(256, 5)
 void fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
                 const float* __restrict__ biasF, const uint8_t* __restrict__ mask,
                 bf16* __restrict__ o, float* __restrict__ lse, bf16* __restrict__ res,
                 int B, int N, int H, float alpha) {
   constexpr int KT = 64;        // keys per iteration
   constexpr int NC = D / 16;    // 16-wide channel chunks
-  __shared__ __attribute__((aligned(16))) bf16 Ks[KT * D];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[KT * D];
-  __shared__ __attribute__((aligned(16))) uint8_t Ms[KT];
+  constexpr int CPR = D / 8;    // 16-byte chunks per row
+  __shared__ __attribute__((aligned(16))) bf16 Ks_[2][KT * D];
+  __shared__ __attribute__((aligned(16))) bf16 Vs_[2][KT * D];
+  __shared__ __attribute__((aligned(16))) uint8_t Ms_[2][KT];
 
   const int QT = (N + 127) / 128;
   const int64_t ntiles = (int64_t)B * H * N * QT;
@@ -212,7 +254,7 @@ void fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   const int h = (int)(rest % H);
   const int b = (int)(rest / H);
 
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 5, ln = l & 31;
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, g = l >> 5, ln = l & 31;
   const int64_t sbase = (((int64_t)b * N + i) * H + h) * (int64_t)N * D;
   const int j = qt * 128 + w * 32 + ln;  // this lane's query
   const bool jok = j < N;
@@ -220,6 +262,17 @@ void fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   const float* btile = biasF + ((int64_t)(b * H + h) * (Jp / 32) + (qt * 4 + w)) * (int64_t)(Kp / 32) * 1024;
   const float c1 = alpha * kLog2e;
   const float mneg = kMaskNeg / alpha;
+  const uint8_t* mrow = MASK ? mask + ((int64_t)b * N + i) * N : nullptr;
+
+  // streamed loads: K and V rows (lane -> swizzled 16-byte chunk), this wave's bias tiles
+  const __amdgpu_buffer_rsrc_t rk = buf_rsrc(k + sbase, N * D * 2), rv = buf_rsrc(v + sbase, N * D * 2);
+  const unsigned kv_vo = (unsigned)(((tid / CPR) * D + ((tid % CPR) ^ swz<D>(tid / CPR)) * 8) * 2);
+  auto prefetch = [&](int kt, int buf) {
+    if (w < KT * CPR / 64) {
+      dma16b(rk, kv_vo, kt * KT * D * 2, &Ks_[buf][w * 512]);
+      dma16b(rv, kv_vo, kt * KT * D * 2, &Vs_[buf][w * 512]);
+    }
+  };
 
   bf16x8 qf[NC];
 #pragma unroll
@@ -230,35 +283,34 @@ void fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   float m_run = -INFINITY, l_run = 0.0f;
 
   const int nkt = (N + KT - 1) / KT;
+  if (MASK && tid < KT) Ms_[0][tid] = tid < N ? mrow[tid] : (uint8_t)1;
+  prefetch(0, 0);
   for (int kt = 0; kt < nkt; kt++) {
-    const int k0 = kt * KT;
-    // stage K and V tiles (zero beyond N) and the mask bytes
-    for (int c = tid; c < KT * D / 8; c += 256) {
-      const int r = c / (D / 8), col = (c % (D / 8)) * 8;
-      bf16x8 kv = zero8(), vv = zero8();
-      if (k0 + r < N) {
-        kv = *(const bf16x8*)(k + sbase + (int64_t)(k0 + r) * D + col);
-        vv = *(const bf16x8*)(v + sbase + (int64_t)(k0 + r) * D + col);
-      }
-      *(bf16x8*)(Ks + r * D + col) = kv;
-      *(bf16x8*)(Vs + r * D + col) = vv;
+    const int cur = kt & 1;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's part of tile kt is in LDS
+    __syncthreads();                     // all of tile kt is in LDS; buffer cur^1 is free
+    uint8_t mnext = 1;
+    if (kt + 1 < nkt) {
+      // the mask byte is loaded before the tile so that waiting for it leaves the tile in flight
+      if (MASK && tid < KT && (kt + 1) * KT + tid < N) mnext = mrow[(kt + 1) * KT + tid];
+      prefetch(kt + 1, cur ^ 1);
     }
-    if (MASK && tid < KT) Ms[tid] = (k0 + tid < N) ? mask[((int64_t)b * N + i) * N + k0 + tid] : (uint8_t)1;
-    __syncthreads();
+    const lbf16* Ks = (const lbf16*)Ks_[cur];
+    const lbf16* Vs = (const lbf16*)Vs_[cur];
 
     f32x16 s[2];
 #pragma unroll
     for (int tt = 0; tt < 2; tt++) {
-      const float* bt = btile + (int64_t)(kt * 2 + tt) * 1024;
 #pragma unroll
       for (int R = 0; R < 4; R++) {
-        const f32x4 bv = *(const f32x4*)(bt + ((R * 2 + g) * 32 + ln) * 4);
+        const f32x4 bv = *(const f32x4*)(btile + (int64_t)(kt * 2 + tt) * 1024 + ((R * 2 + g) * 32 + ln) * 4);
         s[tt][R * 4 + 0] = bv[0]; s[tt][R * 4 + 1] = bv[1];
         s[tt][R * 4 + 2] = bv[2]; s[tt][R * 4 + 3] = bv[3];
       }
+      const int rk_ = tt * 32 + ln;
 #pragma unroll
       for (int cc = 0; cc < NC; cc++) {
-        const bf16x8 a = *(const bf16x8*)(Ks + (tt * 32 + ln) * D + cc * 16 + g * 8);
+        const bf16x8 a = *(const lbf16x8*)(Ks + rk_ * D + ((cc * 2 + g) ^ swz<D>(rk_)) * 8);
         s[tt] = mfma32(a, qf[cc], s[tt]);
       }
       if (MASK) {
@@ -266,7 +318,7 @@ void fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
         for (int R = 0; R < 4; R++) {
 #pragma unroll
           for (int e = 0; e < 4; e++)
-            if (!Ms[tt * 32 + R * 8 + g * 4 + e]) s[tt][R * 4 + e] += mneg;
+            if (!Ms_[cur][tt * 32 + R * 8 + g * 4 + e]) s[tt][R * 4 + e] += mneg;
         }
       }
     }
@@ -304,13 +356,14 @@ void fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
         const int r0 = tt * 32 + m2 * 16 + g * 4;
         bf16x8 a;
         if (D == 32 || chalf == 0) {
-          a = cat8(tr16(Vs, D, r0, chalf * 16), tr16(Vs, D, r0 + 8, chalf * 16));
+          const int c0 = D == 32 ? chalf * 16 : 0;
+          a = cat8(tr16p(Vs + tr_off<D>(l, r0, c0)), tr16p(Vs + tr_off<D>(l, r0 + 8, c0)));
         } else {
           a = zero8();
         }
         acc_o = mfma32(a, pb, acc_o);
       }
-    __syncthreads();
+    if (MASK && tid < KT) Ms_[cur ^ 1][tid] = mnext;  // read after the next barrier
   }
 
   // epilogue: normalise, round, residual, logsumexp
@@ -337,7 +390,6 @@ void fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   }
 }
 
-// ------------------------------------------------------------------ backward: correction D
 // D[b,i,h,j] = sum_c dO * (o + residual) in FP32 (or dO * o without a residual), written
 // with lse2 = lse * log2(e) into rows padded to Jp floats (16-byte aligned, zero padding),
 // the layout the main kernel streams into LDS.  D/8 adjacent lanes share a row (16 bytes
@@ -401,30 +453,6 @@ void bwd_pre_kernel(const bf16* __restrict__ dO, const bf16* __restrict__ o, con
 // over all LDS banks.
 constexpr int kBwdMaxSteps = 6;  // 6 steps x 128 queries = TRI_ATTN_MAX_N
 
-__device__ __forceinline__ void dma16(const void* g, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
-}
-
-// Raw buffer resource over [base, base + bytes): loads past the end return zeros, which is how
-// rows beyond N are read below.  (Only loads go through buffer resources: the compiler's
-// wait-state rule for the store-data hazard of wide buffer stores does not cover the form
-// with a register scalar offset on gfx950, where such stores were seen to write
-// overwritten data.  Global stores get the wait states.)
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
-}
-// 16 bytes per lane from a buffer straight into LDS: lane l's bytes land at lds_wave_base + 16 l
-__device__ __forceinline__ void dma16b(__amdgpu_buffer_rsrc_t r, unsigned voff, int soff, void* lds_wave_base) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave_base, 16, voff, soff,
-                                           0, 0);
-}
-
-// chunk swizzle for rows of D bf16 (D/8 chunks of 16 bytes per row)
-template <int D>
-__device__ __forceinline__ int swz(int row) {
-  return D == 32 ? ((row >> 2) & 3) : ((row >> 3) & 1);
-}
-
 template <int D, bool MASK>
 __global__ __launch_bounds__(512, 1)
 void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
@@ -474,15 +502,8 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
 
   auto qd_off = [](int buf) { return buf ? oQD1 : oQD0; };
 
-  // ---- per-lane LDS offsets (elements) of the operand reads
-  // natural row reads: row rr, chunk c -> rr*D + ((c ^ swz(rr)) * 8)
-  // transposed reads of a 4-row group starting at row r0 (swz constant over the group)
-  auto tr_off = [](int lane, int r0, int c0) {  // element offset of this lane's 8 bytes
-    const int t16 = lane & 15;
-    const int rr = r0 + (t16 >> 2), col = c0 + 4 * (t16 & 3);
-    return rr * D + ((((col >> 3) ^ swz<D>(rr)) << 3) | (col & 7));
-  };
-
+  // LDS operand reads: natural row reads of row rr, chunk c at rr*D + ((c ^ swz(rr)) * 8);
+  // transposed reads through tr_off.
   // Per-lane byte offsets of the streamed loads, fixed for the whole work-group; slice and
   // step enter through the buffer base and the scalar offset.  Q and dO land swizzled.
   const unsigned qd_vo = (unsigned)(((tid / CPR) * D + ((tid % CPR) ^ swz<D>(tid / CPR)) * 8) * 2);
@@ -609,7 +630,7 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
         // at D = 16 the upper 16 channel rows of the 32x32 product repeat the lower ones;
         // those accumulator rows are never stored
         const int r0 = p * 32 + m2 * 16 + 4 * g, c0 = D == 32 ? 16 * chalf : 0;
-        const int o1 = tr_off(lx, r0, c0), o2 = tr_off(lx, r0 + 8, c0);
+        const int o1 = tr_off<D>(lx, r0, c0), o2 = tr_off<D>(lx, r0 + 8, c0);
         const bf16x8 ao = cat8(tr16p(dOs + o1), tr16p(dOs + o2));
         const bf16x8 aq = cat8(tr16p(Qs + o1), tr16p(Qs + o2));
         dvT = mfma32(ao, pb, dvT);
@@ -634,7 +655,7 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
           f32x4 c = {};
 #pragma unroll
           for (int kk = 0; kk < 64; kk += 32) {
-            const bf16x8 a = cat8(tr16p(Ks + tr_off(lx, kk + 8 * G16, u * 16)), tr16p(Ks + tr_off(lx, kk + 8 * G16 + 4, u * 16)));
+            const bf16x8 a = cat8(tr16p(Ks + tr_off<D>(lx, kk + 8 * G16, u * 16)), tr16p(Ks + tr_off<D>(lx, kk + 8 * G16 + 4, u * 16)));
             const bf16x8 bb = cat8(tr16p(dST + sT + kk * LDT), tr16p(dST + sT + (kk + 4) * LDT));
             c = mfma16(a, bb, c);
           }
