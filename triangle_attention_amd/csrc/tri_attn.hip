@@ -68,6 +68,8 @@ typedef __attribute__((address_space(3))) bf16x8 lbf16x8;
 typedef __attribute__((address_space(3))) bf16x4 lbf16x4;
 typedef __attribute__((address_space(3))) f32x4 lf32x4;
 typedef __attribute__((address_space(3))) s16x4 ls16x4;
+typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) u32x4v lu32x4;
 
 // Lane part of a transposed read: lane t of a 16-lane group addresses row t/4 and
 // column 4*(t%4) of the 4x16 block it helps to load.
@@ -100,29 +102,31 @@ __device__ __forceinline__ bf16x8 pack8(const float* f) {
   return r;
 }
 
-// The dq partials are FP32 values kept to 24 bits: sign, exponent and the top 15 mantissa
-// bits, rounded to nearest even (relative error <= 2^-16, 128x below the bf16 rounding of
-// the final dq).  Four of them pack into three dwords.  MFMA results are finite or the
+// The dq partials are FP32 values kept to their top 24 bits (sign, exponent and 15 mantissa
+// bits, truncated: relative error below 2^-15, 64x under the bf16 rounding of the final dq).
+// Four of them pack into three dwords with byte permutes.  MFMA results are finite or the
 // canonical quiet NaN, which both survive the encoding.
 typedef unsigned u32x3 __attribute__((ext_vector_type(3)));
-__device__ __forceinline__ unsigned f24_bits(float x) {
-  const unsigned u = __builtin_bit_cast(unsigned, x);
-  return (u + 0x7Fu + ((u >> 8) & 1u)) >> 8;
-}
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+// v_perm_b32 (a, b, sel): byte k of the result is byte sel.k of the 8-byte value {a, b} (a high),
+// selector 0x0C gives a zero byte
 __device__ __forceinline__ u32x3 pack_f24x4(f32x4 v) {
-  const unsigned r0 = f24_bits(v[0]), r1 = f24_bits(v[1]), r2 = f24_bits(v[2]), r3 = f24_bits(v[3]);
+  // (bit-cast the whole vector: hipcc mis-reads __builtin_bit_cast of a single vector element)
+  const u32x4 u = __builtin_bit_cast(u32x4, v);
+  const unsigned u0 = u[0], u1 = u[1], u2 = u[2], u3 = u[3];
   u32x3 w;
-  w[0] = r0 | (r1 << 24);
-  w[1] = (r1 >> 8) | (r2 << 16);
-  w[2] = (r2 >> 16) | (r3 << 8);
+  w[0] = __builtin_amdgcn_perm(u1, u0, 0x05030201u);  // u0.b1 u0.b2 u0.b3 u1.b1
+  w[1] = __builtin_amdgcn_perm(u2, u1, 0x06050302u);  // u1.b2 u1.b3 u2.b1 u2.b2
+  w[2] = __builtin_amdgcn_perm(u3, u2, 0x07060503u);  // u2.b3 u3.b1 u3.b2 u3.b3
   return w;
 }
 __device__ __forceinline__ f32x4 unpack_f24x4(u32x3 w) {
   f32x4 v;
-  v[0] = __builtin_bit_cast(float, w[0] << 8);
-  v[1] = __builtin_bit_cast(float, ((w[0] >> 24) | (w[1] << 8)) << 8);
-  v[2] = __builtin_bit_cast(float, ((w[1] >> 16) | (w[2] << 16)) << 8);
-  v[3] = __builtin_bit_cast(float, w[2] & 0xFFFFFF00u);
+  v[0] = __builtin_bit_cast(float, __builtin_amdgcn_perm(0u, w[0], 0x0201000Cu));
+  v[1] = __builtin_bit_cast(float, __builtin_amdgcn_perm(w[1], w[0], 0x0504030Cu));
+  v[2] = __builtin_bit_cast(float, __builtin_amdgcn_perm(w[2], w[1], 0x0403020Cu));
+  v[3] = __builtin_bit_cast(float, __builtin_amdgcn_perm(0u, w[2], 0x0302010Cu));
   return v;
 }
 
@@ -204,6 +208,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, int
 __device__ __forceinline__ void dma16b(__amdgpu_buffer_rsrc_t r, unsigned voff, int soff, void* lds_wave_base) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave_base, 16, voff, soff,
                                            0, 0);
+}
+
+// Work-group barrier that orders LDS accesses only.  __syncthreads() also waits for every
+// outstanding global access of the wave (its release fence covers the direct-to-LDS loads),
+// which would expose the latency of a prefetch issued just before it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // chunk swizzle for rows of D bf16 (D/8 chunks of 16 bytes per row)
@@ -391,7 +405,8 @@ void fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
 }
 
 // D[b,i,h,j] = sum_c dO * (o + residual) in FP32 (or dO * o without a residual), written
-// with lse2 = lse * log2(e) into rows padded to Jp floats (16-byte aligned, zero padding),
+// negated (the main kernel starts its dO V^T accumulator from -D), with
+// lse2 = lse * log2(e), into rows padded to Jp floats (16-byte aligned, zero padding),
 // the layout the main kernel streams into LDS.  D/8 adjacent lanes share a row (16 bytes
 // each, so a wave reads contiguous memory); their partial sums combine in a fixed order.
 template <int D>
@@ -423,7 +438,7 @@ void bwd_pre_kernel(const bf16* __restrict__ dO, const bf16* __restrict__ o, con
   acc += __shfl_xor(acc, 1);
   if (LPR == 4) acc += __shfl_xor(acc, 2);
   if (part == 0) {
-    Dp[prow] = acc;
+    Dp[prow] = -acc;
     L2p[prow] = j < N ? lse[row * N + j] * kLog2e : 0.0f;
   }
 }
@@ -459,7 +474,7 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
                 const bf16* __restrict__ dO, const bf16* __restrict__ biasB, const uint8_t* __restrict__ mask,
                 const float* __restrict__ L2p, const float* __restrict__ Dp,
                 unsigned* __restrict__ dqp, float* __restrict__ dbp, bf16* __restrict__ dk, bf16* __restrict__ dv,
-                int B, int N, int H, int G, int ngroups, float alpha, float inv_alpha) {
+                int B, int N, int H, int G, int ngroups, float alpha) {
   constexpr int NC = D / 16;
   constexpr int CPR = D / 8;    // 16-byte chunks per row
   constexpr int LDT = 128 + 8;  // dS^T row stride (elements), padded
@@ -495,10 +510,10 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   const bool kok = kg < N;
   const int Jp = (int)round_up(N, 128);
   const float c1 = alpha * kLog2e;
-  const float mneg = kMaskNeg / alpha;
   const int64_t slice_elems = (int64_t)N * D;
-  const int64_t dq_stride = (int64_t)B * N * H * slice_elems;  // elements of one full dq partial
   const int nsteps = (N + 127) / 128;
+  const int nqt = Jp / 16;                                    // 16-query tiles per slice
+  const int64_t dq_kb_stride = (int64_t)B * N * H * nqt * (16 * D * 3);  // bytes of one key block's partials
 
   auto qd_off = [](int buf) { return buf ? oQD1 : oQD0; };
 
@@ -510,9 +525,32 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   const int kv_t = tid & 255;  // K (waves 0-3) / V (waves 4-7)
   const unsigned kv_vo = (unsigned)(((kb * 64 + kv_t / CPR) * D + ((kv_t % CPR) ^ swz<D>(kv_t / CPR)) * 8) * 2);
   const unsigned row_vo = (unsigned)(l & 31) * 16u;
-  // dq partial of (query row, 4-channel group): 12 bytes at (row * D/4 + group) * 12
-  const int dq_row = (w >> 1) * 32 + (w & 1) * 16 + (l & 15);
-  const unsigned dq_vo = (unsigned)((dq_row * (D / 4) + (l >> 4)) * 12);
+
+  // Per-lane LDS byte offsets of the operand reads, fixed for the work-group; the item's
+  // buffer and the step enter as uniform additions or immediate offsets.
+  //  * row reads (A/B operands of the 32x32x16 products): row rr = (p or kh)*32 + ln, chunk
+  //    cc*2+g in swizzled position; the swizzle of such a row depends on ln only
+  //  * transposed reads of dO/Q (dV^T, dK^T A operands) over query rows p*32 + m2*16 + 4g (+8)
+  //  * transposed reads of K (dQ^T A operand) over key rows 8*(l/16) (+4) of each 32-key half
+  const int swl = swz<D>(ln);
+  unsigned offR[NC];
+#pragma unroll
+  for (int cc = 0; cc < NC; cc++) offR[cc] = (unsigned)((ln * D + (((cc * 2 + g) ^ swl) * 8)) * 2);
+  const unsigned offQ = (unsigned)(p * 32 * D * 2), offKV = (unsigned)(oK + kh * 32 * D * 2);
+  const int G16 = l >> 4, chalf = G16 & 1;
+  const int c0 = D == 32 ? 16 * chalf : 0;
+  const unsigned trA = (unsigned)((tr_off<D>(l, 4 * g, c0) + p * 32 * D) * 2);
+  const unsigned trB = (unsigned)((tr_off<D>(l, 4 * g + 8, c0) + p * 32 * D) * 2);
+  unsigned trK[NC][2];
+#pragma unroll
+  for (int u = 0; u < NC; u++) {
+    trK[u][0] = (unsigned)(oK + tr_off<D>(l, 8 * G16, u * 16) * 2);
+    trK[u][1] = (unsigned)(oK + tr_off<D>(l, 8 * G16 + 4, u * 16) * 2);
+  }
+  const unsigned offBias = (unsigned)((kh * 4 + p) * 2048 + l * 16);
+  const unsigned offRow = (unsigned)((p * 32 + g * 4) * 4);                  // lse2 / -D rows of this lane
+  const unsigned offST = (unsigned)(oDST + (kl * LDT + p * 32 + g * 4) * 2);  // dS^T write
+  const unsigned offSTr = (unsigned)(oDST + (8 * G16 * LDT + (w >> 1) * 32 + (w & 1) * 16 + tr_lane(LDT)) * 2);
 
   // issue the loads of work item (ii, ss) into LDS buffer `buf`; rows past N read as zeros
   auto prefetch = [&](int ii, int ss, int buf) {
@@ -548,25 +586,19 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   prefetch_kv(i_begin);
   int cur = 0;
   for (int i = i_begin; i < i_end; i++) {
-    const int64_t sbase = (((int64_t)b * N + i) * H + h) * slice_elems;
-    float madd = 0.0f;
+    const int64_t sl_row = ((int64_t)b * N + i) * H + h;  // slice-head row index
+    const int64_t sbase = sl_row * slice_elems;
+    float mterm = 0.0f;
     f32x16 dkT = {}, dvT = {};
 
     auto step = [&](auto S_) {
       constexpr int s = decltype(S_)::value;
-      const int j0 = s * 128;
-      // The lane index is made opaque at every unrolled step, so that addresses derived from
-      // it are rebuilt locally instead of being held live across all six steps.
-      int lx = l;
-      asm volatile("" : "+v"(lx));
-      const int g = lx >> 5, ln = lx & 31, G16 = lx >> 4, chalf = G16 & 1;
-      const int kl = kh * 32 + ln, rq = p * 32 + ln, rk = kl;
       // item (i, s) was issued before the previous item's dq stores (and, at a slice
       // boundary, before the previous slice's K/V loads and dk/dv stores, where everything
       // is drained)
       if (s == 0) {
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-        if (MASK) madd = (kok && !mask[((int64_t)b * N + i) * N + kg]) ? mneg : 0.0f;
+        if (MASK) mterm = (kok && !mask[((int64_t)b * N + i) * N + kg]) ? kMaskNeg * kLog2e : 0.0f;
       } else if (NC == 2) {
         __builtin_amdgcn_s_waitcnt(0x0F72);  // vmcnt(2): the two dq stores may be in flight
       } else {
@@ -576,90 +608,98 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
       if (s + 1 < nsteps) prefetch(i, s + 1, cur ^ 1);
       else if (i + 1 < i_end) prefetch(i + 1, 0, cur ^ 1);
 
-      const lbf16* Qs = (const lbf16*)(lds + qd_off(cur));
-      const lbf16* dOs = (const lbf16*)(lds + qd_off(cur) + 128 * D * 2);
-      const lbf16* Ks = (const lbf16*)(lds + oK);
-      const lbf16* Vs = (const lbf16*)(lds + oV);
-      const lbf16* bS = (const lbf16*)lds + ((s * 2 + kh) * 4 + p) * 1024 + lx * 8;
-      const lf32* lS = (const lf32*)(lds + oL) + cur * 128;
-      const lf32* DSv = (const lf32*)(lds + oDv) + cur * 128;
-      lbf16* dST = (lbf16*)(lds + oDST);
+      char* const qd = lds + (cur ? oQD1 : oQD0);  // this item's Q rows, then its dO rows
+      const unsigned lrow = offRow + cur * 512;    // this item's lse2 and -D rows (oL / oDv)
 
-      // S = bias/alpha + Q K^T  and  dP = dO V^T   (rows: 32 queries, cols: 32 keys)
-      f32x16 sacc, dp = {};
-      {
-        const bf16x8 b0 = *(const lbf16x8*)bS, b1 = *(const lbf16x8*)(bS + 512);
+      // S = Q K^T (rows: 32 queries, cols: 32 keys) and dP - D = dO V^T - D, the second
+      // accumulator starting from -D
+      f32x16 sacc = {}, dp;
 #pragma unroll
-        for (int r = 0; r < 8; r++) {
-          sacc[r] = (float)b0[r] * inv_alpha;
-          sacc[r + 8] = (float)b1[r] * inv_alpha;
-        }
+      for (int R = 0; R < 4; R++) {
+        const f32x4 x = *(const lf32x4*)(lds + oDv + lrow + R * 32);
+#pragma unroll
+        for (int e = 0; e < 4; e++) dp[R * 4 + e] = x[e];
       }
 #pragma unroll
       for (int cc = 0; cc < NC; cc++) {
-        const int cq = ((cc * 2 + g) ^ swz<D>(rq)) * 8, ck = ((cc * 2 + g) ^ swz<D>(rk)) * 8;
-        const bf16x8 aq = *(const lbf16x8*)(Qs + rq * D + cq);
-        const bf16x8 kf = *(const lbf16x8*)(Ks + rk * D + ck);
+        const bf16x8 aq = *(const lbf16x8*)(qd + offQ + offR[cc]);
+        const bf16x8 kf = *(const lbf16x8*)(lds + offKV + offR[cc]);
         sacc = mfma32(aq, kf, sacc);
-        const bf16x8 ao = *(const lbf16x8*)(dOs + rq * D + cq);
-        const bf16x8 vf = *(const lbf16x8*)(Vs + rk * D + ck);
+        const bf16x8 ao = *(const lbf16x8*)(qd + 128 * D * 2 + offQ + offR[cc]);
+        const bf16x8 vf = *(const lbf16x8*)(lds + offKV + 64 * D * 2 + offR[cc]);
         dp = mfma32(ao, vf, dp);
       }
+      // P = exp2(c1 S + log2e bias - lse2) and dS = P (dP - D); dS is summed into the face
+      const lbf16* bS = (const lbf16*)(lds + s * 16384 + offBias);
+      const bf16x8 b0 = *(const lbf16x8*)bS, b1 = *(const lbf16x8*)(bS + 512);
       float P[16], dS[16];
 #pragma unroll
       for (int R = 0; R < 4; R++) {
-        const f32x4 lv = *(const lf32x4*)(lS + p * 32 + R * 8 + g * 4);
-        const f32x4 dd = *(const lf32x4*)(DSv + p * 32 + R * 8 + g * 4);
+        const f32x4 lv = *(const lf32x4*)(lds + oL + lrow + R * 32);
 #pragma unroll
         for (int e = 0; e < 4; e++) {
           const int r = R * 4 + e;
-          float x = sacc[r];
-          if (MASK) x += madd;
-          P[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(x, c1, -lv[e]));
-          dS[r] = P[r] * (dp[r] - dd[e]);
+          const float bb = (float)(r < 8 ? b0[r] : b1[r - 8]);
+          float z = __builtin_fmaf(sacc[r], c1, __builtin_fmaf(bb, kLog2e, -lv[e]));
+          if (MASK) z += mterm;
+          P[r] = __builtin_amdgcn_exp2f(z);
+          dS[r] = P[r] * dp[r];
         }
       }
 #pragma unroll
       for (int r = 0; r < 16; r++) face[s][r] += dS[r];
 
-      // dV^T += dO^T P ; dK^T += Q^T dS   (rows: channels, cols: keys)
+      // dV^T += dO^T P ; dK^T += Q^T dS   (rows: channels, cols: keys).  At D = 16 the upper
+      // 16 channel rows of the 32x32 product repeat the lower ones and are never stored.
+      bf16x8 pb[2], sb[2];
 #pragma unroll
       for (int m2 = 0; m2 < 2; m2++) {
-        const bf16x8 pb = pack8(&P[m2 * 8]);
-        const bf16x8 sb = pack8(&dS[m2 * 8]);
-        // at D = 16 the upper 16 channel rows of the 32x32 product repeat the lower ones;
-        // those accumulator rows are never stored
-        const int r0 = p * 32 + m2 * 16 + 4 * g, c0 = D == 32 ? 16 * chalf : 0;
-        const int o1 = tr_off<D>(lx, r0, c0), o2 = tr_off<D>(lx, r0 + 8, c0);
-        const bf16x8 ao = cat8(tr16p(dOs + o1), tr16p(dOs + o2));
-        const bf16x8 aq = cat8(tr16p(Qs + o1), tr16p(Qs + o2));
-        dvT = mfma32(ao, pb, dvT);
-        dkT = mfma32(aq, sb, dkT);
+        pb[m2] = pack8(&P[m2 * 8]);
+        sb[m2] = pack8(&dS[m2 * 8]);
+        const bf16x8 ao = cat8(tr16p((const lbf16*)(qd + 128 * D * 2 + trA + m2 * 16 * D * 2)),
+                               tr16p((const lbf16*)(qd + 128 * D * 2 + trB + m2 * 16 * D * 2)));
+        const bf16x8 aq = cat8(tr16p((const lbf16*)(qd + trA + m2 * 16 * D * 2)),
+                               tr16p((const lbf16*)(qd + trB + m2 * 16 * D * 2)));
+        dvT = mfma32(ao, pb[m2], dvT);
+        dkT = mfma32(aq, sb[m2], dkT);
       }
-      // dS^T (keys x queries) to LDS for the dQ product
+      // dS^T (keys x queries) to LDS for the dQ product: accumulator rows 8R+4g+0..3 of this
+      // lane's key are four consecutive queries
 #pragma unroll
-      for (int R = 0; R < 4; R++) {
-        bf16x4 t4;
-#pragma unroll
-        for (int e = 0; e < 4; e++) t4[e] = (bf16)dS[R * 4 + e];
-        *(lbf16x4*)(dST + kl * LDT + p * 32 + R * 8 + g * 4) = t4;
+      for (int m2 = 0; m2 < 2; m2++) {
+        *(lbf16x4*)(lds + offST + m2 * 32) = __builtin_shufflevector(sb[m2], sb[m2], 0, 1, 2, 3);
+        *(lbf16x4*)(lds + offST + m2 * 32 + 16) = __builtin_shufflevector(sb[m2], sb[m2], 4, 5, 6, 7);
       }
       __syncthreads();  // dS^T complete
-      // dQ^T tiles (16 channels x 16 queries) over the 64 keys of this block
+      // dQ^T tiles (16 channels x 16 queries) over the 64 keys of this block, stored as this
+      // block's partial in 24-bit form: one 16 x D block per (slice, 16-query tile), lane-major,
+      // so that every store writes whole cache lines
       {
-        char* dqs = (char*)dqp + ((int64_t)kb * dq_stride + sbase + (int64_t)j0 * D) * 3;  // 3 bytes per element
-        const bool rows_ok = j0 + 128 <= N || j0 + dq_row < N;
-        const int sT = 8 * G16 * LDT + (w >> 1) * 32 + (w & 1) * 16 + tr_lane(LDT);
+        u32x3 pk[NC];
 #pragma unroll
         for (int u = 0; u < NC; u++) {
           f32x4 c = {};
 #pragma unroll
           for (int kk = 0; kk < 64; kk += 32) {
-            const bf16x8 a = cat8(tr16p(Ks + tr_off<D>(lx, kk + 8 * G16, u * 16)), tr16p(Ks + tr_off<D>(lx, kk + 8 * G16 + 4, u * 16)));
-            const bf16x8 bb = cat8(tr16p(dST + sT + kk * LDT), tr16p(dST + sT + (kk + 4) * LDT));
+            const bf16x8 a = cat8(tr16p((const lbf16*)(lds + trK[u][0] + kk * D * 2)),
+                                  tr16p((const lbf16*)(lds + trK[u][1] + kk * D * 2)));
+            const bf16x8 bb = cat8(tr16p((const lbf16*)(lds + offSTr + kk * LDT * 2)),
+                                   tr16p((const lbf16*)(lds + offSTr + (kk + 4) * LDT * 2)));
             c = mfma16(a, bb, c);
           }
-          if (rows_ok) *(u32x3*)(dqs + (dq_vo + u * 48)) = pack_f24x4(c);
+          pk[u] = pack_f24x4(c);
+        }
+        char* blk = (char*)dqp + kb * dq_kb_stride +
+                    ((sl_row * nqt + s * 8 + w) * (int64_t)(16 * D * 3));
+        if (NC == 2) {
+          u32x4 w4;
+          w4[0] = pk[0][0]; w4[1] = pk[0][1]; w4[2] = pk[0][2]; w4[3] = pk[NC - 1][0];
+          u32x2 w2;
+          w2[0] = pk[NC - 1][1]; w2[1] = pk[NC - 1][2];
+          *(u32x4*)(blk + l * 16) = w4;
+          *(u32x2*)(blk + 1024 + l * 8) = w2;
+        } else {
+          *(u32x3*)(blk + l * 12) = pk[0];
         }
       }
       cur ^= 1;
@@ -673,8 +713,8 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
     if (nsteps > 5) step(std::integral_constant<int, 5>{});
     static_assert(kBwdMaxSteps == 6, "six unrolled steps");
 
-    __syncthreads();  // every wave is past the last dQ product: K, V and dS^T are free
-    if (i + 1 < i_end) prefetch_kv(i + 1);
+    lds_barrier();  // every wave is past the last dQ product: K, V and dS^T are free
+    if (i + 1 < i_end) prefetch_kv(i + 1);  // in flight during the reduction below
 
     // end of slice i: dK^T, dV^T summed over the four query lanes as (p0 + p1) + (p2 + p3),
     // in the Q/dO buffer of the last item and the dS^T area next to it (the prefetch of the
@@ -688,7 +728,7 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
         red[slot_w + (NR + r) * 64] = dvT[r];
       }
     }
-    __syncthreads();
+    lds_barrier();
     if (!(p & 1)) {
 #pragma unroll
       for (int r = 0; r < NR; r++) {
@@ -703,7 +743,7 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
         red[slot_w + (NR + r) * 64] = dvT[r];
       }
     }
-    __syncthreads();
+    lds_barrier();
     if (p == 0) {
       const int slot2 = (kh * 2 + 1) * (2 * NR * 64) + l;
 #pragma unroll
@@ -738,26 +778,67 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
 }
 
 // ------------------------------------------------------------------ backward: ordered sums
-// dq = bf16(alpha * sum_kb dqp[kb]) with kb ascending (partials decoded from their 24-bit
-// form); dbias = sum_g dbp[g] with g ascending.
-// All loads of a thread are issued before the sum (indexes past the last partial re-read it
-// and are not added), so the kernels stream at memory speed instead of one latency per term.
+// dq = bf16(alpha * sum_kb partial[kb]) with kb ascending.  The partials are 24-bit values in
+// blocks of 16 queries x D channels per (key block, slice-head row, 16-query tile); inside a
+// block lane t (0..63) of the writing wave owns query t%16 and channels u*16 + 4*(t/16) + 0..3
+// (u < D/16), stored as its first 16 bytes at 16*t and, for D = 32, its last 8 bytes at
+// 1024 + 8*t.  One thread here handles one (block, lane) slot.  All loads of a thread are
+// issued before the sum (indexes past the last partial re-read it and are not added), so the
+// kernel streams at memory speed instead of paying one latency per term.
+template <int D>
 __global__ __launch_bounds__(256)
-void reduce_dq_kernel(const unsigned* __restrict__ dqp, bf16* __restrict__ dq, int KB, int64_t n4, float alpha) {
+void reduce_dq_kernel(const unsigned* __restrict__ dqp, bf16* __restrict__ dq, int KB, int N, int nqt,
+                      int64_t nslots, float alpha) {
+  constexpr int NC = D / 16;
   constexpr int kMaxKB = TRI_ATTN_MAX_N / 64;
+  constexpr int BLK = 16 * D * 3;  // bytes per block
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= n4) return;
-  u32x3 x[kMaxKB];
+  if (t >= nslots) return;
+  const int64_t blk = t >> 6;
+  const int lane = (int)(t & 63);
+  const int64_t sl = blk / nqt;
+  const int row = (int)(blk % nqt) * 16 + (lane & 15);
+  if (row >= N) return;
+  const int64_t kb_stride = nslots / 64 * BLK;
+  const char* base = (const char*)dqp + blk * BLK;
+  f32x4 acc[NC];
+  if (NC == 2) {
+    u32x4 x4[kMaxKB];
+    u32x2 x2[kMaxKB];
 #pragma unroll
-  for (int kb = 0; kb < kMaxKB; kb++) x[kb] = *(const u32x3*)(dqp + ((int64_t)min(kb, KB - 1) * n4 + t) * 3);
-  f32x4 s = unpack_f24x4(x[0]);
+    for (int kb = 0; kb < kMaxKB; kb++) {
+      const char* pb = base + min(kb, KB - 1) * kb_stride;
+      x4[kb] = *(const u32x4*)(pb + lane * 16);
+      x2[kb] = *(const u32x2*)(pb + 1024 + lane * 8);
+    }
 #pragma unroll
-  for (int kb = 1; kb < kMaxKB; kb++)
-    if (kb < KB) s += unpack_f24x4(x[kb]);
-  bf16x4 r;
+    for (int kb = 0; kb < kMaxKB; kb++) {
+      u32x3 w0, w1;
+      w0[0] = x4[kb][0]; w0[1] = x4[kb][1]; w0[2] = x4[kb][2];
+      w1[0] = x4[kb][3]; w1[1] = x2[kb][0]; w1[2] = x2[kb][1];
+      const f32x4 v0 = unpack_f24x4(w0), v1 = unpack_f24x4(w1);
+      if (kb == 0) { acc[0] = v0; acc[NC - 1] = v1; }
+      else if (kb < KB) { acc[0] += v0; acc[NC - 1] += v1; }
+    }
+  } else {
+    u32x3 x3[kMaxKB];
 #pragma unroll
-  for (int e = 0; e < 4; e++) r[e] = (bf16)(s[e] * alpha);
-  *(bf16x4*)(dq + t * 4) = r;
+    for (int kb = 0; kb < kMaxKB; kb++) x3[kb] = *(const u32x3*)(base + min(kb, KB - 1) * kb_stride + lane * 12);
+#pragma unroll
+    for (int kb = 0; kb < kMaxKB; kb++) {
+      const f32x4 v0 = unpack_f24x4(x3[kb]);
+      if (kb == 0) acc[0] = v0;
+      else if (kb < KB) acc[0] += v0;
+    }
+  }
+  bf16* out = dq + (sl * N + row) * D + 4 * (lane >> 4);
+#pragma unroll
+  for (int u = 0; u < NC; u++) {
+    bf16x4 r;
+#pragma unroll
+    for (int e = 0; e < 4; e++) r[e] = (bf16)(acc[u][e] * alpha);
+    *(bf16x4*)(out + u * 16) = r;
+  }
 }
 
 // VEC: four adjacent elements per thread (n divisible by 4, so every partial stays 16-byte aligned)
@@ -824,7 +905,7 @@ Plan make_plan(int64_t B, int64_t N, int64_t H, int64_t D) {
   p.off_D = p.bias_b16_bytes;
   p.off_L2 = p.off_D + round_up(B * N * H * p.Jp * 4, kAlign);
   p.off_dqp = p.off_L2 + round_up(B * N * H * p.Jp * 4, kAlign);
-  p.off_dbp = p.off_dqp + round_up(p.KB * p.elems * 3, kAlign);
+  p.off_dbp = p.off_dqp + round_up(p.KB * B * N * H * p.Jp * D * 3, kAlign);
   p.bwd_bytes = p.off_dbp + round_up(p.ngroups * B * H * N * N * 4, kAlign);
   return p;
 }
@@ -896,15 +977,15 @@ tri_attn_status launch_bwd(unsigned stages, const Plan& P, const void* q, const 
   } else if (mask)
     hipLaunchKernelGGL((bwd_kernel<D, true>), dim3(grid_xcd(ntiles)), dim3(512), 0, st, (const bf16*)q,
                        (const bf16*)k, (const bf16*)v, (const bf16*)dO, biasB, mask, L2g, Dg, dqp, dbp, (bf16*)dk,
-                       (bf16*)dv, (int)P.B, (int)P.N, (int)P.H, (int)P.G, (int)P.ngroups, alpha, 1.0f / alpha);
+                       (bf16*)dv, (int)P.B, (int)P.N, (int)P.H, (int)P.G, (int)P.ngroups, alpha);
   else
     hipLaunchKernelGGL((bwd_kernel<D, false>), dim3(grid_xcd(ntiles)), dim3(512), 0, st, (const bf16*)q,
                        (const bf16*)k, (const bf16*)v, (const bf16*)dO, biasB, mask, L2g, Dg, dqp, dbp, (bf16*)dk,
-                       (bf16*)dv, (int)P.B, (int)P.N, (int)P.H, (int)P.G, (int)P.ngroups, alpha, 1.0f / alpha);
+                       (bf16*)dv, (int)P.B, (int)P.N, (int)P.H, (int)P.G, (int)P.ngroups, alpha);
   if (stages & TRI_ATTN_STAGE_FINAL) {
-    const int64_t n4 = P.elems / 4;
-    hipLaunchKernelGGL(reduce_dq_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, dqp, (bf16*)dq,
-                       (int)P.KB, n4, alpha);
+    const int64_t nslots = P.B * P.N * P.H * (P.Jp / 16) * 64;
+    hipLaunchKernelGGL(reduce_dq_kernel<D>, dim3((unsigned)((nslots + 255) / 256)), dim3(256), 0, st, dqp,
+                       (bf16*)dq, (int)P.KB, (int)P.N, (int)(P.Jp / 16), nslots, alpha);
     const int64_t nbias = P.B * P.H * P.N * P.N;
     if (nbias % 4 == 0)
       hipLaunchKernelGGL(reduce_dbias_kernel<true>, dim3((unsigned)((nbias / 4 + 255) / 256)), dim3(256), 0, st, dbp,
