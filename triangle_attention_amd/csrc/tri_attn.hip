@@ -210,6 +210,37 @@ __device__ __forceinline__ void dma16b(__amdgpu_buffer_rsrc_t r, unsigned voff, 
                                            0, 0);
 }
 
+// Direct-to-LDS loads written as inline assembly.  The compiler's own form of these loads
+// makes it wait for every outstanding one before any later LDS read it cannot prove
+// unrelated (the transposing reads among them), which would expose the latency of a
+// prefetch issued one item ahead.  In this form the loads are invisible to the compiler's
+// wait-count tracking; the kernels wait for them explicitly (vmcnt) before the barrier that
+// publishes the data.  rsrc is a raw buffer descriptor (wave-uniform): base address, byte
+// count (reads at or past it return zeros), raw flags.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 raw_rsrc(const void* base, int bytes) {
+  const unsigned long long a = (unsigned long long)(uintptr_t)base;
+  i32x4 r = {__builtin_amdgcn_readfirstlane((int)(unsigned)a),
+             __builtin_amdgcn_readfirstlane((int)((unsigned)(a >> 32) & 0xFFFFu)),
+             __builtin_amdgcn_readfirstlane(bytes), 0x00020000};
+  return r;
+}
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+// 16 bytes per lane: lane l's bytes land at lds_wave_base + 16 l
+__device__ __forceinline__ void dma16_asm(i32x4 rsrc, unsigned voff, int soff, const void* lds_wave_base) {
+  const unsigned m0v = __builtin_amdgcn_readfirstlane(lds_addr(lds_wave_base));
+  asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soff)), "s"(m0v) : "memory", "m0");
+}
+// one byte per lane, zero-extended into lane l's dword at lds_wave_base + 4 l
+__device__ __forceinline__ void dma1_asm(i32x4 rsrc, unsigned voff, int soff, const void* lds_wave_base) {
+  const unsigned m0v = __builtin_amdgcn_readfirstlane(lds_addr(lds_wave_base));
+  asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_ubyte %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soff)), "s"(m0v) : "memory", "m0");
+}
+
 // Work-group barrier that orders LDS accesses only.  __syncthreads() also waits for every
 // outstanding global access of the wave (its release fence covers the direct-to-LDS loads),
 // which would expose the latency of a prefetch issued just before it.
@@ -452,21 +483,45 @@ void bwd_pre_kernel(const bf16* __restrict__ dO, const bf16* __restrict__ o, con
 // summed over slices on chip and written once per group.  The steps of a slice are
 // unrolled at compile time so that every face slot is addressed statically.
 //
-// The pair bias is the same for every slice, so the work-group's whole bias column
-// (all queries x its 64 keys, bf16, 96 KiB at N = 768) is loaded into LDS once and stays
-// there for the slice group.
+// One barrier per item.  The dQ product of an item needs dS from both key halves, so it
+// runs one item late: after the barrier that starts item t, every wave has written its
+// dS^T of item t-1, and the wave computes dQ of item t-1 before the products of item t.
+// dS^T, K and V are therefore kept in two (dS^T) and three (K/V, a buffer per slice)
+// copies in LDS.
 //
-// Software pipeline: while item t is computed, item t+1's Q, dO, lse2 and D stream from
-// global memory straight into the other half of double-buffered LDS (buffer loads to LDS,
-// no registers involved); the next slice's K and V follow once the last item of a slice
-// has finished reading them.  Rows past N read as zeros through the buffer range check,
-// and the -inf padding of the prepared bias turns every padded query or key into an exact
-// zero probability.
+// Software pipeline: while item t is computed, item t+1's Q, dO, lse2, -D and pair-bias
+// tiles stream from global memory straight into the other half of double-buffered LDS
+// (direct-to-LDS loads, no registers involved), and the next slice's K, V and key-mask
+// bytes stream into their own buffer from the first item of a slice on.  Rows past N read
+// as zeros through the buffer range check, and the -inf padding of the prepared bias turns
+// every padded query or key into an exact zero probability.
 //
 // Rows of Q, dO, K and V in LDS hold their 16-byte chunks in XOR-swizzled order (chunk c
 // of row r sits in slot c ^ swz(r)), which spreads the row-wise operand reads of a wave
 // over all LDS banks.
 constexpr int kBwdMaxSteps = 6;  // 6 steps x 128 queries = TRI_ATTN_MAX_N
+
+// s_waitcnt vmcnt(n) for a wave-uniform n in 0..15 (the instruction takes an immediate)
+__device__ __forceinline__ void wait_vmcnt(int n) {
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
+    case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
+    case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
+    case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
+    case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
+    case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
+    case 7: __builtin_amdgcn_s_waitcnt(0x0F77); break;
+    case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
+    case 9: __builtin_amdgcn_s_waitcnt(0x0F79); break;
+    case 10: __builtin_amdgcn_s_waitcnt(0x0F7A); break;
+    case 11: __builtin_amdgcn_s_waitcnt(0x0F7B); break;
+    case 12: __builtin_amdgcn_s_waitcnt(0x0F7C); break;
+    case 13: __builtin_amdgcn_s_waitcnt(0x0F7D); break;
+    case 14: __builtin_amdgcn_s_waitcnt(0x0F7E); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0F7F); break;
+  }
+}
 
 template <int D, bool MASK>
 __global__ __launch_bounds__(512, 1)
@@ -479,15 +534,17 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   constexpr int CPR = D / 8;    // 16-byte chunks per row
   constexpr int LDT = 128 + 8;  // dS^T row stride (elements), padded
   constexpr int NR = D / 2;     // accumulator registers of dK^T / dV^T holding channels c < D
-  // LDS map (bytes): bias column | Q,dO of buffer 0 | dS^T | Q,dO of buffer 1 | K, V | lse2, D.
-  // Buffer 0 + dS^T and dS^T + buffer 1 are contiguous: the end-of-slice dK/dV reduction
-  // uses whichever of the two ranges holds no prefetched data.
-  constexpr int kBiasBytes = kBwdMaxSteps * 8 * 1024 * 2;
-  constexpr int kQD = 2 * 128 * D * 2;
-  constexpr int oQD0 = kBiasBytes, oDST = oQD0 + kQD, oQD1 = oDST + 64 * LDT * 2, oK = oQD1 + kQD;
-  constexpr int oV = oK + 64 * D * 2, oL = oV + 64 * D * 2, oDv = oL + 2 * 128 * 4, kLdsBytes = oDv + 2 * 128 * 4;
+  // LDS map (bytes): pair-bias tiles x2 | Q,dO x2 | K,V,mask x3 | lse2,-D x2 | dS^T x2 | dK/dV reduction
+  // (the odd query lanes' partials)
+  constexpr int kBiasB = 8 * 2048;                  // 8 waves x one 32x32 bf16 tile
+  constexpr int kQDB = 2 * 128 * D * 2;             // Q rows then dO rows
+  constexpr int kKVB = 2 * 64 * D * 2 + 64 * 4;     // K rows, V rows, 64 mask bytes (one per dword)
+  constexpr int kLDB = 2 * 128 * 4;                 // lse2 rows then -D rows
+  constexpr int kSTB = 64 * LDT * 2;
+  constexpr int kREDB = 4 * 2 * NR * 64 * 4;        // dK^T, dV^T partials of four waves
+  constexpr int oBias = 0, oQD = oBias + 2 * kBiasB, oKV = oQD + 2 * kQDB, oLD = oKV + 3 * kKVB;
+  constexpr int oST = oLD + 2 * kLDB, oRED = oST + 2 * kSTB, kLdsBytes = oRED + kREDB;
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
-  static_assert(4 * 2 * NR * 64 * 4 <= kQD + 64 * LDT * 2, "dK/dV reduction scratch");
   __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
 
   const int KB = (N + 63) / 64;
@@ -512,22 +569,20 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   const float c1 = alpha * kLog2e;
   const int64_t slice_elems = (int64_t)N * D;
   const int nsteps = (N + 127) / 128;
-  const int nqt = Jp / 16;                                    // 16-query tiles per slice
+  const int nqt = Jp / 16;                                               // 16-query tiles per slice
   const int64_t dq_kb_stride = (int64_t)B * N * H * nqt * (16 * D * 3);  // bytes of one key block's partials
+  const int nitems = (i_end - i_begin) * nsteps;
 
-  auto qd_off = [](int buf) { return buf ? oQD1 : oQD0; };
-
-  // LDS operand reads: natural row reads of row rr, chunk c at rr*D + ((c ^ swz(rr)) * 8);
-  // transposed reads through tr_off.
   // Per-lane byte offsets of the streamed loads, fixed for the whole work-group; slice and
-  // step enter through the buffer base and the scalar offset.  Q and dO land swizzled.
+  // step enter through the buffer base and the scalar offset.  Q, dO, K and V land swizzled.
   const unsigned qd_vo = (unsigned)(((tid / CPR) * D + ((tid % CPR) ^ swz<D>(tid / CPR)) * 8) * 2);
   const int kv_t = tid & 255;  // K (waves 0-3) / V (waves 4-7)
   const unsigned kv_vo = (unsigned)(((kb * 64 + kv_t / CPR) * D + ((kv_t % CPR) ^ swz<D>(kv_t / CPR)) * 8) * 2);
   const unsigned row_vo = (unsigned)(l & 31) * 16u;
+  const bf16* bias_blk = biasB + ((int64_t)(b * H + h) * KB + kb) * (int64_t)nsteps * 8192;
 
-  // Per-lane LDS byte offsets of the operand reads, fixed for the work-group; the item's
-  // buffer and the step enter as uniform additions or immediate offsets.
+  // Per-lane LDS byte offsets of the operand reads; the buffer and the step enter as uniform
+  // additions or immediate offsets.
   //  * row reads (A/B operands of the 32x32x16 products): row rr = (p or kh)*32 + ln, chunk
   //    cc*2+g in swizzled position; the swizzle of such a row depends on ln only
   //  * transposed reads of dO/Q (dV^T, dK^T A operands) over query rows p*32 + m2*16 + 4g (+8)
@@ -536,7 +591,7 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   unsigned offR[NC];
 #pragma unroll
   for (int cc = 0; cc < NC; cc++) offR[cc] = (unsigned)((ln * D + (((cc * 2 + g) ^ swl) * 8)) * 2);
-  const unsigned offQ = (unsigned)(p * 32 * D * 2), offKV = (unsigned)(oK + kh * 32 * D * 2);
+  const unsigned offQ = (unsigned)(p * 32 * D * 2), offK = (unsigned)(kh * 32 * D * 2);
   const int G16 = l >> 4, chalf = G16 & 1;
   const int c0 = D == 32 ? 16 * chalf : 0;
   const unsigned trA = (unsigned)((tr_off<D>(l, 4 * g, c0) + p * 32 * D) * 2);
@@ -544,98 +599,142 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   unsigned trK[NC][2];
 #pragma unroll
   for (int u = 0; u < NC; u++) {
-    trK[u][0] = (unsigned)(oK + tr_off<D>(l, 8 * G16, u * 16) * 2);
-    trK[u][1] = (unsigned)(oK + tr_off<D>(l, 8 * G16 + 4, u * 16) * 2);
+    trK[u][0] = (unsigned)(tr_off<D>(l, 8 * G16, u * 16) * 2);
+    trK[u][1] = (unsigned)(tr_off<D>(l, 8 * G16 + 4, u * 16) * 2);
   }
   const unsigned offBias = (unsigned)((kh * 4 + p) * 2048 + l * 16);
-  const unsigned offRow = (unsigned)((p * 32 + g * 4) * 4);                  // lse2 / -D rows of this lane
-  const unsigned offST = (unsigned)(oDST + (kl * LDT + p * 32 + g * 4) * 2);  // dS^T write
-  const unsigned offSTr = (unsigned)(oDST + (8 * G16 * LDT + (w >> 1) * 32 + (w & 1) * 16 + tr_lane(LDT)) * 2);
+  const unsigned offRow = (unsigned)((p * 32 + g * 4) * 4);  // lse2 / -D rows of this lane
+  const unsigned offST = (unsigned)((kl * LDT + p * 32 + g * 4) * 2);  // dS^T write
+  const unsigned offSTr = (unsigned)((8 * G16 * LDT + (w >> 1) * 32 + (w & 1) * 16 + tr_lane(LDT)) * 2);
 
   // issue the loads of work item (ii, ss) into LDS buffer `buf`; rows past N read as zeros
   auto prefetch = [&](int ii, int ss, int buf) {
     const int64_t sl = ((int64_t)b * N + ii) * H + h;  // slice-head row index
     if (w < 2 * CPR) {
-      dma16b(buf_rsrc(q + sl * slice_elems, N * D * 2), qd_vo, ss * 128 * D * 2, lds + qd_off(buf) + w * 1024);
-      dma16b(buf_rsrc(dO + sl * slice_elems, N * D * 2), qd_vo, ss * 128 * D * 2,
-             lds + qd_off(buf) + 128 * D * 2 + w * 1024);
+      dma16_asm(raw_rsrc(q + sl * slice_elems, N * D * 2), qd_vo, ss * 128 * D * 2, lds + oQD + buf * kQDB + w * 1024);
+      dma16_asm(raw_rsrc(dO + sl * slice_elems, N * D * 2), qd_vo, ss * 128 * D * 2,
+                lds + oQD + buf * kQDB + 128 * D * 2 + w * 1024);
     }
-    if (w == 0 && l < 32) dma16b(buf_rsrc(L2p + sl * Jp, Jp * 4), row_vo, ss * 512, lds + oL + buf * 512);
-    if (w == 1 && l < 32) dma16b(buf_rsrc(Dp + sl * Jp, Jp * 4), row_vo, ss * 512, lds + oDv + buf * 512);
+    if (w == 0 && l < 32) dma16_asm(raw_rsrc(L2p + sl * Jp, Jp * 4), row_vo, ss * 512, lds + oLD + buf * kLDB);
+    if (w == 1 && l < 32) dma16_asm(raw_rsrc(Dp + sl * Jp, Jp * 4), row_vo, ss * 512, lds + oLD + buf * kLDB + 512);
+    // this step's pair-bias tiles: 16 KiB, 2 KiB per wave
+    const i32x4 rb = raw_rsrc(bias_blk + (int64_t)ss * 8192 + w * 1024, 2048);
+    dma16_asm(rb, (unsigned)l * 16u, 0, lds + oBias + buf * kBiasB + w * 2048);
+    dma16_asm(rb, (unsigned)l * 16u, 1024, lds + oBias + buf * kBiasB + w * 2048 + 1024);
   };
-  // K and V blocks of slice ii (single buffer: issued once the previous slice is done with it)
-  auto prefetch_kv = [&](int ii) {
+  // K, V and the key-mask bytes of slice ii into K/V buffer kvb
+  auto prefetch_kv = [&](int ii, int kvb) {
     constexpr int KC = 64 * CPR;  // 16-byte chunks per block
     const int64_t sl = ((int64_t)b * N + ii) * H + h;
-    if (w < KC / 64) dma16b(buf_rsrc(k + sl * slice_elems, N * D * 2), kv_vo, 0, lds + oK + w * 1024);
+    char* dst = lds + oKV + kvb * kKVB;
+    if (w < KC / 64) dma16_asm(raw_rsrc(k + sl * slice_elems, N * D * 2), kv_vo, 0, dst + w * 1024);
     else if (w >= 4 && w < 4 + KC / 64)
-      dma16b(buf_rsrc(v + sl * slice_elems, N * D * 2), kv_vo, 0, lds + oV + (w - 4) * 1024);
+      dma16_asm(raw_rsrc(v + sl * slice_elems, N * D * 2), kv_vo, 0, dst + 64 * D * 2 + (w - 4) * 1024);
+    if (MASK && w == 7)  // one byte per lane, each landing in its own dword
+      dma1_asm(raw_rsrc(mask + ((int64_t)b * N + ii) * N, N), (unsigned)(kb * 64 + l), 0, dst + 2 * 64 * D * 2);
   };
-
-  // the bias column of this work-group: nsteps * 16 KiB, contiguous in the prepared layout
-  {
-    const bf16* src = biasB + ((int64_t)(b * H + h) * KB + kb) * (int64_t)nsteps * 8192;
-    for (int c = w; c < nsteps * 16; c += 8) dma16(src + c * 512 + l * 8, lds + c * 1024);
-  }
 
   f32x16 face[kBwdMaxSteps];
 #pragma unroll
   for (int s = 0; s < kBwdMaxSteps; s++) face[s] = f32x16{};
 
+  prefetch_kv(i_begin, 0);
   prefetch(i_begin, 0, 0);
-  prefetch_kv(i_begin);
-  int cur = 0;
+
+  // dQ^T tiles (16 channels x 16 queries) of the previous item over the 64 keys of this
+  // block, stored as this block's partial in 24-bit form: one 16 x D block per (slice,
+  // 16-query tile), lane-major, so that every store writes whole cache lines
+  int64_t prev_sl = 0;
+  int prev_s = 0, prev_kv = 0;
+  auto dq_product = [&](int stb) {
+    const char* kbase = lds + oKV + prev_kv * kKVB;
+    const char* sbase_t = lds + oST + stb * kSTB + offSTr;
+    u32x3 pk[NC];
+#pragma unroll
+    for (int u = 0; u < NC; u++) {
+      f32x4 c = {};
+#pragma unroll
+      for (int kk = 0; kk < 64; kk += 32) {
+        const bf16x8 a = cat8(tr16p((const lbf16*)(kbase + trK[u][0] + kk * D * 2)),
+                              tr16p((const lbf16*)(kbase + trK[u][1] + kk * D * 2)));
+        const bf16x8 bb = cat8(tr16p((const lbf16*)(sbase_t + kk * LDT * 2)),
+                               tr16p((const lbf16*)(sbase_t + (kk + 4) * LDT * 2)));
+        c = mfma16(a, bb, c);
+      }
+      pk[u] = pack_f24x4(c);
+    }
+    char* blk = (char*)dqp + kb * dq_kb_stride + ((prev_sl * nqt + prev_s * 8 + w) * (int64_t)(16 * D * 3));
+    if (NC == 2) {
+      u32x4 w4;
+      w4[0] = pk[0][0]; w4[1] = pk[0][1]; w4[2] = pk[0][2]; w4[3] = pk[NC - 1][0];
+      u32x2 w2;
+      w2[0] = pk[NC - 1][1]; w2[1] = pk[NC - 1][2];
+      *(u32x4*)(blk + l * 16) = w4;
+      *(u32x2*)(blk + 1024 + l * 8) = w2;
+    } else {
+      *(u32x3*)(blk + l * 12) = pk[0];
+    }
+  };
+
+  // VMEM operations a wave issues after an item's prefetch and before that item's wait:
+  // the previous item's dq stores and, after the last item of a slice, the dK/dV stores
+  constexpr int kDqStores = NC == 2 ? 2 : 1;
+  const int kvStores = p == 0 ? 2 * (NR / 4) : 0;  // dk and dv stores of a slice's end
+  int t = 0;     // item index within the work-group
+  int cur = 0;   // LDS buffer of item t
   for (int i = i_begin; i < i_end; i++) {
     const int64_t sl_row = ((int64_t)b * N + i) * H + h;  // slice-head row index
     const int64_t sbase = sl_row * slice_elems;
+    const int kvc = (i - i_begin) % 3;                     // K/V buffer of this slice
+    const char* Ks = lds + oKV + kvc * kKVB;
+    const char* Vs = Ks + 64 * D * 2;
     float mterm = 0.0f;
     f32x16 dkT = {}, dvT = {};
 
     auto step = [&](auto S_) {
       constexpr int s = decltype(S_)::value;
-      // item (i, s) was issued before the previous item's dq stores (and, at a slice
-      // boundary, before the previous slice's K/V loads and dk/dv stores, where everything
-      // is drained)
-      if (s == 0) {
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-        if (MASK) mterm = (kok && !mask[((int64_t)b * N + i) * N + kg]) ? kMaskNeg * kLog2e : 0.0f;
-      } else if (NC == 2) {
-        __builtin_amdgcn_s_waitcnt(0x0F72);  // vmcnt(2): the two dq stores may be in flight
-      } else {
-        __builtin_amdgcn_s_waitcnt(0x0F71);  // vmcnt(1)
-      }
-      __syncthreads();  // item (i, s) is in LDS everywhere; the other buffers and dS^T are free
+      // wait for item t's loads (issued one item earlier); what follows them in the queue
+      // is the previous item's dq stores and, at a slice start, the dK/dV stores
+      if (t == 0) wait_vmcnt(0);
+      else wait_vmcnt((t >= 2 ? kDqStores : 0) + (s == 0 ? kvStores : 0));
+      lds_barrier();  // item t is in LDS everywhere, dS^T of item t-1 is complete, the other buffers are free
+      if (s == 0 && i + 1 < i_end) prefetch_kv(i + 1, (i + 1 - i_begin) % 3);
       if (s + 1 < nsteps) prefetch(i, s + 1, cur ^ 1);
       else if (i + 1 < i_end) prefetch(i + 1, 0, cur ^ 1);
+      if (MASK && s == 0) {
+        const unsigned mb = *(const __attribute__((address_space(3))) unsigned*)(Ks + 2 * 64 * D * 2 + kl * 4);
+        mterm = (kok && (mb & 0xFFu) == 0) ? kMaskNeg * kLog2e : 0.0f;
+      }
+      if (t >= 1) dq_product(cur ^ 1);
 
-      char* const qd = lds + (cur ? oQD1 : oQD0);  // this item's Q rows, then its dO rows
-      const unsigned lrow = offRow + cur * 512;    // this item's lse2 and -D rows (oL / oDv)
+      const char* qd = lds + oQD + cur * kQDB;   // this item's Q rows, then its dO rows
+      const char* ld = lds + oLD + cur * kLDB + offRow;
 
       // S = Q K^T (rows: 32 queries, cols: 32 keys) and dP - D = dO V^T - D, the second
       // accumulator starting from -D
       f32x16 sacc = {}, dp;
 #pragma unroll
       for (int R = 0; R < 4; R++) {
-        const f32x4 x = *(const lf32x4*)(lds + oDv + lrow + R * 32);
+        const f32x4 x = *(const lf32x4*)(ld + 512 + R * 32);
 #pragma unroll
         for (int e = 0; e < 4; e++) dp[R * 4 + e] = x[e];
       }
 #pragma unroll
       for (int cc = 0; cc < NC; cc++) {
         const bf16x8 aq = *(const lbf16x8*)(qd + offQ + offR[cc]);
-        const bf16x8 kf = *(const lbf16x8*)(lds + offKV + offR[cc]);
+        const bf16x8 kf = *(const lbf16x8*)(Ks + offK + offR[cc]);
         sacc = mfma32(aq, kf, sacc);
         const bf16x8 ao = *(const lbf16x8*)(qd + 128 * D * 2 + offQ + offR[cc]);
-        const bf16x8 vf = *(const lbf16x8*)(lds + offKV + 64 * D * 2 + offR[cc]);
+        const bf16x8 vf = *(const lbf16x8*)(Vs + offK + offR[cc]);
         dp = mfma32(ao, vf, dp);
       }
       // P = exp2(c1 S + log2e bias - lse2) and dS = P (dP - D); dS is summed into the face
-      const lbf16* bS = (const lbf16*)(lds + s * 16384 + offBias);
+      const lbf16* bS = (const lbf16*)(lds + oBias + cur * kBiasB + offBias);
       const bf16x8 b0 = *(const lbf16x8*)bS, b1 = *(const lbf16x8*)(bS + 512);
       float P[16], dS[16];
 #pragma unroll
       for (int R = 0; R < 4; R++) {
-        const f32x4 lv = *(const lf32x4*)(lds + oL + lrow + R * 32);
+        const f32x4 lv = *(const lf32x4*)(ld + R * 32);
 #pragma unroll
         for (int e = 0; e < 4; e++) {
           const int r = R * 4 + e;
@@ -656,6 +755,17 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
       for (int m2 = 0; m2 < 2; m2++) {
         pb[m2] = pack8(&P[m2 * 8]);
         sb[m2] = pack8(&dS[m2 * 8]);
+      }
+      // dS^T (keys x queries) to LDS for the dQ product of the next item: accumulator rows
+      // 8R+4g+0..3 of this lane's key are four consecutive queries
+      char* stw = lds + oST + cur * kSTB + offST;
+#pragma unroll
+      for (int m2 = 0; m2 < 2; m2++) {
+        *(lbf16x4*)(stw + m2 * 32) = __builtin_shufflevector(sb[m2], sb[m2], 0, 1, 2, 3);
+        *(lbf16x4*)(stw + m2 * 32 + 16) = __builtin_shufflevector(sb[m2], sb[m2], 4, 5, 6, 7);
+      }
+#pragma unroll
+      for (int m2 = 0; m2 < 2; m2++) {
         const bf16x8 ao = cat8(tr16p((const lbf16*)(qd + 128 * D * 2 + trA + m2 * 16 * D * 2)),
                                tr16p((const lbf16*)(qd + 128 * D * 2 + trB + m2 * 16 * D * 2)));
         const bf16x8 aq = cat8(tr16p((const lbf16*)(qd + trA + m2 * 16 * D * 2)),
@@ -663,46 +773,11 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
         dvT = mfma32(ao, pb[m2], dvT);
         dkT = mfma32(aq, sb[m2], dkT);
       }
-      // dS^T (keys x queries) to LDS for the dQ product: accumulator rows 8R+4g+0..3 of this
-      // lane's key are four consecutive queries
-#pragma unroll
-      for (int m2 = 0; m2 < 2; m2++) {
-        *(lbf16x4*)(lds + offST + m2 * 32) = __builtin_shufflevector(sb[m2], sb[m2], 0, 1, 2, 3);
-        *(lbf16x4*)(lds + offST + m2 * 32 + 16) = __builtin_shufflevector(sb[m2], sb[m2], 4, 5, 6, 7);
-      }
-      __syncthreads();  // dS^T complete
-      // dQ^T tiles (16 channels x 16 queries) over the 64 keys of this block, stored as this
-      // block's partial in 24-bit form: one 16 x D block per (slice, 16-query tile), lane-major,
-      // so that every store writes whole cache lines
-      {
-        u32x3 pk[NC];
-#pragma unroll
-        for (int u = 0; u < NC; u++) {
-          f32x4 c = {};
-#pragma unroll
-          for (int kk = 0; kk < 64; kk += 32) {
-            const bf16x8 a = cat8(tr16p((const lbf16*)(lds + trK[u][0] + kk * D * 2)),
-                                  tr16p((const lbf16*)(lds + trK[u][1] + kk * D * 2)));
-            const bf16x8 bb = cat8(tr16p((const lbf16*)(lds + offSTr + kk * LDT * 2)),
-                                   tr16p((const lbf16*)(lds + offSTr + (kk + 4) * LDT * 2)));
-            c = mfma16(a, bb, c);
-          }
-          pk[u] = pack_f24x4(c);
-        }
-        char* blk = (char*)dqp + kb * dq_kb_stride +
-                    ((sl_row * nqt + s * 8 + w) * (int64_t)(16 * D * 3));
-        if (NC == 2) {
-          u32x4 w4;
-          w4[0] = pk[0][0]; w4[1] = pk[0][1]; w4[2] = pk[0][2]; w4[3] = pk[NC - 1][0];
-          u32x2 w2;
-          w2[0] = pk[NC - 1][1]; w2[1] = pk[NC - 1][2];
-          *(u32x4*)(blk + l * 16) = w4;
-          *(u32x2*)(blk + 1024 + l * 8) = w2;
-        } else {
-          *(u32x3*)(blk + l * 12) = pk[0];
-        }
-      }
+      prev_sl = sl_row;
+      prev_s = s;
+      prev_kv = kvc;
       cur ^= 1;
+      t++;
     };
 
     step(std::integral_constant<int, 0>{});
@@ -713,13 +788,10 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
     if (nsteps > 5) step(std::integral_constant<int, 5>{});
     static_assert(kBwdMaxSteps == 6, "six unrolled steps");
 
-    lds_barrier();  // every wave is past the last dQ product: K, V and dS^T are free
-    if (i + 1 < i_end) prefetch_kv(i + 1);  // in flight during the reduction below
-
-    // end of slice i: dK^T, dV^T summed over the four query lanes as (p0 + p1) + (p2 + p3),
-    // in the Q/dO buffer of the last item and the dS^T area next to it (the prefetch of the
-    // next slice's first item targets the other buffer)
-    lf32* red = (lf32*)(lds + (cur ? oQD0 : oDST));
+    // end of slice i: dK^T and dV^T summed over the four query lanes as (p0 + p1) + (p2 + p3)
+    // through a dedicated LDS area (no other data lives there, so the first write needs no
+    // barrier: the previous slice's readers passed this slice's item barriers long ago)
+    lf32* red = (lf32*)(lds + oRED);
     const int slot_w = (kh * 2 + (p >> 1)) * (2 * NR * 64) + l;
     if (p & 1) {
 #pragma unroll
@@ -763,6 +835,10 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
       }
     }
   }
+  // the last item's dQ product
+  lds_barrier();
+  dq_product(cur ^ 1);
+
   // write this group's pair-bias gradient partial: dbp[grp][b][h][j][k]
   float* dst = dbp + (((int64_t)grp * B + b) * H + h) * (int64_t)N * N;
 #pragma unroll
