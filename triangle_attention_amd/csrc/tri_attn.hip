@@ -68,8 +68,6 @@ typedef __attribute__((address_space(3))) bf16x8 lbf16x8;
 typedef __attribute__((address_space(3))) bf16x4 lbf16x4;
 typedef __attribute__((address_space(3))) f32x4 lf32x4;
 typedef __attribute__((address_space(3))) s16x4 ls16x4;
-typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) u32x4v lu32x4;
 
 // Lane part of a transposed read: lane t of a 16-lane group addresses row t/4 and
 // column 4*(t%4) of the 4x16 block it helps to load.
@@ -100,34 +98,6 @@ __device__ __forceinline__ bf16x8 pack8(const float* f) {
 #pragma unroll
   for (int i = 0; i < 8; i++) r[i] = (bf16)f[i];
   return r;
-}
-
-// The dq partials are FP32 values kept to their top 24 bits (sign, exponent and 15 mantissa
-// bits, truncated: relative error below 2^-15, 64x under the bf16 rounding of the final dq).
-// Four of them pack into three dwords with byte permutes.  MFMA results are finite or the
-// canonical quiet NaN, which both survive the encoding.
-typedef unsigned u32x3 __attribute__((ext_vector_type(3)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-// v_perm_b32 (a, b, sel): byte k of the result is byte sel.k of the 8-byte value {a, b} (a high),
-// selector 0x0C gives a zero byte
-__device__ __forceinline__ u32x3 pack_f24x4(f32x4 v) {
-  // (bit-cast the whole vector: hipcc mis-reads __builtin_bit_cast of a single vector element)
-  const u32x4 u = __builtin_bit_cast(u32x4, v);
-  const unsigned u0 = u[0], u1 = u[1], u2 = u[2], u3 = u[3];
-  u32x3 w;
-  w[0] = __builtin_amdgcn_perm(u1, u0, 0x05030201u);  // u0.b1 u0.b2 u0.b3 u1.b1
-  w[1] = __builtin_amdgcn_perm(u2, u1, 0x06050302u);  // u1.b2 u1.b3 u2.b1 u2.b2
-  w[2] = __builtin_amdgcn_perm(u3, u2, 0x07060503u);  // u2.b3 u3.b1 u3.b2 u3.b3
-  return w;
-}
-__device__ __forceinline__ f32x4 unpack_f24x4(u32x3 w) {
-  f32x4 v;
-  v[0] = __builtin_bit_cast(float, __builtin_amdgcn_perm(0u, w[0], 0x0201000Cu));
-  v[1] = __builtin_bit_cast(float, __builtin_amdgcn_perm(w[1], w[0], 0x0504030Cu));
-  v[2] = __builtin_bit_cast(float, __builtin_amdgcn_perm(w[2], w[1], 0x0403020Cu));
-  v[3] = __builtin_bit_cast(float, __builtin_amdgcn_perm(0u, w[2], 0x0302010Cu));
-  return v;
 }
 
 // Work-group id -> logical tile, so that tiles [x*per, (x+1)*per) run on XCD x.
@@ -570,7 +540,7 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   const int64_t slice_elems = (int64_t)N * D;
   const int nsteps = (N + 127) / 128;
   const int nqt = Jp / 16;                                               // 16-query tiles per slice
-  const int64_t dq_kb_stride = (int64_t)B * N * H * nqt * (16 * D * 3);  // bytes of one key block's partials
+  const int64_t dq_kb_stride = (int64_t)B * N * H * nqt * (16 * D * 2);  // bytes of one key block's partials
   const int nitems = (i_end - i_begin) * nsteps;
 
   // Per-lane byte offsets of the streamed loads, fixed for the whole work-group; slice and
@@ -649,7 +619,7 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   auto dq_product = [&](int stb) {
     const char* kbase = lds + oKV + prev_kv * kKVB;
     const char* sbase_t = lds + oST + stb * kSTB + offSTr;
-    u32x3 pk[NC];
+    bf16x4 pk[NC];
 #pragma unroll
     for (int u = 0; u < NC; u++) {
       f32x4 c = {};
@@ -661,24 +631,17 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
                                tr16p((const lbf16*)(sbase_t + (kk + 4) * LDT * 2)));
         c = mfma16(a, bb, c);
       }
-      pk[u] = pack_f24x4(c);
+#pragma unroll
+      for (int e = 0; e < 4; e++) pk[u][e] = (bf16)c[e];
     }
-    char* blk = (char*)dqp + kb * dq_kb_stride + ((prev_sl * nqt + prev_s * 8 + w) * (int64_t)(16 * D * 3));
-    if (NC == 2) {
-      u32x4 w4;
-      w4[0] = pk[0][0]; w4[1] = pk[0][1]; w4[2] = pk[0][2]; w4[3] = pk[NC - 1][0];
-      u32x2 w2;
-      w2[0] = pk[NC - 1][1]; w2[1] = pk[NC - 1][2];
-      *(u32x4*)(blk + l * 16) = w4;
-      *(u32x2*)(blk + 1024 + l * 8) = w2;
-    } else {
-      *(u32x3*)(blk + l * 12) = pk[0];
-    }
+    char* blk = (char*)dqp + kb * dq_kb_stride + ((prev_sl * nqt + prev_s * 8 + w) * (int64_t)(16 * D * 2));
+    if (NC == 2) *(bf16x8*)(blk + l * 16) = __builtin_shufflevector(pk[0], pk[NC - 1], 0, 1, 2, 3, 4, 5, 6, 7);
+    else *(bf16x4*)(blk + l * 8) = pk[0];
   };
 
   // VMEM operations a wave issues after an item's prefetch and before that item's wait:
   // the previous item's dq stores and, after the last item of a slice, the dK/dV stores
-  constexpr int kDqStores = NC == 2 ? 2 : 1;
+  constexpr int kDqStores = 1;
   const int kvStores = p == 0 ? 2 * (NR / 4) : 0;  // dk and dv stores of a slice's end
   int t = 0;     // item index within the work-group
   int cur = 0;   // LDS buffer of item t
@@ -854,20 +817,21 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
 }
 
 // ------------------------------------------------------------------ backward: ordered sums
-// dq = bf16(alpha * sum_kb partial[kb]) with kb ascending.  The partials are 24-bit values in
-// blocks of 16 queries x D channels per (key block, slice-head row, 16-query tile); inside a
-// block lane t (0..63) of the writing wave owns query t%16 and channels u*16 + 4*(t/16) + 0..3
-// (u < D/16), stored as its first 16 bytes at 16*t and, for D = 32, its last 8 bytes at
-// 1024 + 8*t.  One thread here handles one (block, lane) slot.  All loads of a thread are
-// issued before the sum (indexes past the last partial re-read it and are not added), so the
-// kernel streams at memory speed instead of paying one latency per term.
+// dq = bf16(alpha * sum_kb partial[kb]) with kb ascending, summed in FP32.  The partials are
+// bf16 blocks of 16 queries x D channels per (key block, slice-head row, 16-query tile); inside
+// a block lane t (0..63) of the writing wave owns query t%16 and channels u*16 + 4*(t/16) + 0..3
+// (u < D/16), stored contiguously at (D/4)*2*t bytes.  One thread here handles one (block,
+// lane) slot.  All loads of a thread are issued before the sum (indexes past the last partial
+// re-read it and are not added), so the kernel streams at memory speed instead of paying one
+// latency per term.
 template <int D>
 __global__ __launch_bounds__(256)
 void reduce_dq_kernel(const unsigned* __restrict__ dqp, bf16* __restrict__ dq, int KB, int N, int nqt,
                       int64_t nslots, float alpha) {
   constexpr int NC = D / 16;
   constexpr int kMaxKB = TRI_ATTN_MAX_N / 64;
-  constexpr int BLK = 16 * D * 3;  // bytes per block
+  constexpr int BLK = 16 * D * 2;  // bytes per block
+  typedef typename std::conditional<NC == 2, bf16x8, bf16x4>::type V;
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= nslots) return;
   const int64_t blk = t >> 6;
@@ -876,43 +840,25 @@ void reduce_dq_kernel(const unsigned* __restrict__ dqp, bf16* __restrict__ dq, i
   const int row = (int)(blk % nqt) * 16 + (lane & 15);
   if (row >= N) return;
   const int64_t kb_stride = nslots / 64 * BLK;
-  const char* base = (const char*)dqp + blk * BLK;
-  f32x4 acc[NC];
-  if (NC == 2) {
-    u32x4 x4[kMaxKB];
-    u32x2 x2[kMaxKB];
+  const char* base = (const char*)dqp + blk * BLK + lane * (int)sizeof(V);
+  V x[kMaxKB];
 #pragma unroll
-    for (int kb = 0; kb < kMaxKB; kb++) {
-      const char* pb = base + min(kb, KB - 1) * kb_stride;
-      x4[kb] = *(const u32x4*)(pb + lane * 16);
-      x2[kb] = *(const u32x2*)(pb + 1024 + lane * 8);
+  for (int kb = 0; kb < kMaxKB; kb++) x[kb] = *(const V*)(base + min(kb, KB - 1) * kb_stride);
+  float acc[4 * NC];
+#pragma unroll
+  for (int e = 0; e < 4 * NC; e++) acc[e] = (float)x[0][e];
+#pragma unroll
+  for (int kb = 1; kb < kMaxKB; kb++)
+    if (kb < KB) {
+#pragma unroll
+      for (int e = 0; e < 4 * NC; e++) acc[e] += (float)x[kb][e];
     }
-#pragma unroll
-    for (int kb = 0; kb < kMaxKB; kb++) {
-      u32x3 w0, w1;
-      w0[0] = x4[kb][0]; w0[1] = x4[kb][1]; w0[2] = x4[kb][2];
-      w1[0] = x4[kb][3]; w1[1] = x2[kb][0]; w1[2] = x2[kb][1];
-      const f32x4 v0 = unpack_f24x4(w0), v1 = unpack_f24x4(w1);
-      if (kb == 0) { acc[0] = v0; acc[NC - 1] = v1; }
-      else if (kb < KB) { acc[0] += v0; acc[NC - 1] += v1; }
-    }
-  } else {
-    u32x3 x3[kMaxKB];
-#pragma unroll
-    for (int kb = 0; kb < kMaxKB; kb++) x3[kb] = *(const u32x3*)(base + min(kb, KB - 1) * kb_stride + lane * 12);
-#pragma unroll
-    for (int kb = 0; kb < kMaxKB; kb++) {
-      const f32x4 v0 = unpack_f24x4(x3[kb]);
-      if (kb == 0) acc[0] = v0;
-      else if (kb < KB) acc[0] += v0;
-    }
-  }
   bf16* out = dq + (sl * N + row) * D + 4 * (lane >> 4);
 #pragma unroll
   for (int u = 0; u < NC; u++) {
     bf16x4 r;
 #pragma unroll
-    for (int e = 0; e < 4; e++) r[e] = (bf16)(acc[u][e] * alpha);
+    for (int e = 0; e < 4; e++) r[e] = (bf16)(acc[u * 4 + e] * alpha);
     *(bf16x4*)(out + u * 16) = r;
   }
 }
@@ -981,7 +927,7 @@ Plan make_plan(int64_t B, int64_t N, int64_t H, int64_t D) {
   p.off_D = p.bias_b16_bytes;
   p.off_L2 = p.off_D + round_up(B * N * H * p.Jp * 4, kAlign);
   p.off_dqp = p.off_L2 + round_up(B * N * H * p.Jp * 4, kAlign);
-  p.off_dbp = p.off_dqp + round_up(p.KB * B * N * H * p.Jp * D * 3, kAlign);
+  p.off_dbp = p.off_dqp + round_up(p.KB * B * N * H * p.Jp * D * 2, kAlign);
   p.bwd_bytes = p.off_dbp + round_up(p.ngroups * B * H * N * N * 4, kAlign);
   return p;
 }
