@@ -68,6 +68,8 @@ typedef __attribute__((address_space(3))) bf16x8 lbf16x8;
 typedef __attribute__((address_space(3))) bf16x4 lbf16x4;
 typedef __attribute__((address_space(3))) f32x4 lf32x4;
 typedef __attribute__((address_space(3))) s16x4 ls16x4;
+typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) u32x4v lu32x4;
 
 // Lane part of a transposed read: lane t of a 16-lane group addresses row t/4 and
 // column 4*(t%4) of the 4x16 block it helps to load.
@@ -139,14 +141,16 @@ __global__ void bias_prep_fwd_kernel(const bf16* __restrict__ bias, float* __res
   out[idx] = val;
 }
 
-// biasB: backward operand, bf16, one contiguous block per (b, h, 64-key block kb) that the
-// backward work-group copies into LDS as is.  Inside a block: 128-query step s, then tile
-// t = 4*kh + p (key half kh, 32-query tile p), then 1024 values in lane order
+// biasB: backward operand, fp16, one contiguous block per (b, h, 64-key block kb) that the
+// backward work-group streams into LDS step by step.  Inside a block: 128-query step s, then
+// tile t = 4*kh + p (key half kh, 32-query tile p), then 1024 values in lane order
 // [half hf][lane 32g+n][8]: position 4R'+e of the 8 holds query 128s + 32p + 8(2hf+R') + 4g + e
 // and key 64kb + 32kh + n, i.e. accumulator register 8hf+4R'+e of lane 32g+n of the 32x32
-// score tile.  The value is the bias itself (exact), -inf where j >= N or k >= N.
-__global__ void bias_prep_bwd_kernel(const bf16* __restrict__ bias, bf16* __restrict__ out, int N, int KB, int nsteps,
-                                     int64_t total) {
+// score tile.  fp16 holds every bf16 value of magnitude 2^-17..65504 exactly (smaller ones
+// to 2^-25 absolute); larger magnitudes saturate at 65504, infinities stay infinite, and the
+// padding (j >= N or k >= N) is -inf.  The main kernel widens it inside v_fma_mix_f32.
+__global__ void bias_prep_bwd_kernel(const bf16* __restrict__ bias, _Float16* __restrict__ out, int N, int KB,
+                                     int nsteps, int64_t total) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= total) return;
   const int off = (int)(idx & 1023), t = (int)((idx >> 10) & 7);
@@ -157,7 +161,12 @@ __global__ void bias_prep_bwd_kernel(const bf16* __restrict__ bias, bf16* __rest
   const int e = off & 3, R = ((off >> 9) << 1) | ((off >> 2) & 1), lane = (off >> 3) & 63;
   const int j = s * 128 + (t & 3) * 32 + R * 8 + (lane >> 5) * 4 + e;
   const int k = kb * 64 + (t >> 2) * 32 + (lane & 31);
-  out[idx] = (j < N && k < N) ? bias[(bh * N + j) * N + k] : (bf16)(-INFINITY);
+  float x = -INFINITY;
+  if (j < N && k < N) {
+    x = (float)bias[(bh * N + j) * N + k];
+    if (!__builtin_isinf(x)) x = fminf(fmaxf(x, -65504.0f), 65504.0f);
+  }
+  out[idx] = (_Float16)x;
 }
 
 // ------------------------------------------------------------------ streaming helpers
@@ -209,6 +218,18 @@ __device__ __forceinline__ void dma1_asm(i32x4 rsrc, unsigned voff, int soff, co
   const unsigned m0v = __builtin_amdgcn_readfirstlane(lds_addr(lds_wave_base));
   asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_ubyte %0, %1, %2 offen lds"
                :: "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soff)), "s"(m0v) : "memory", "m0");
+}
+
+// fma(float(h), c, x) for the low (SEL = 0) or high (SEL = 1) fp16 half h of `pair`, in one
+// v_fma_mix_f32 (the fp16 operand is widened exactly inside the instruction).
+template <int SEL>
+__device__ __forceinline__ float fma_mix_f16(unsigned pair, float c, float x) {
+  float r;
+  if (SEL == 0)
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[0,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(pair), "v"(c), "v"(x));
+  else
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(pair), "v"(c), "v"(x));
+  return r;
 }
 
 // Work-group barrier that orders LDS accesses only.  __syncthreads() also waits for every
@@ -407,7 +428,7 @@ void fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
 
 // D[b,i,h,j] = sum_c dO * (o + residual) in FP32 (or dO * o without a residual), written
 // negated (the main kernel starts its dO V^T accumulator from -D), with
-// lse2 = lse * log2(e), into rows padded to Jp floats (16-byte aligned, zero padding),
+// -lse2 = -lse * log2(e), into rows padded to Jp floats (16-byte aligned, zero padding),
 // the layout the main kernel streams into LDS.  D/8 adjacent lanes share a row (16 bytes
 // each, so a wave reads contiguous memory); their partial sums combine in a fixed order.
 template <int D>
@@ -440,7 +461,7 @@ void bwd_pre_kernel(const bf16* __restrict__ dO, const bf16* __restrict__ o, con
   if (LPR == 4) acc += __shfl_xor(acc, 2);
   if (part == 0) {
     Dp[prow] = -acc;
-    L2p[prow] = j < N ? lse[row * N + j] * kLog2e : 0.0f;
+    L2p[prow] = j < N ? -lse[row * N + j] * kLog2e : 0.0f;
   }
 }
 
@@ -455,7 +476,8 @@ void bwd_pre_kernel(const bf16* __restrict__ dO, const bf16* __restrict__ o, con
 //
 // One barrier per item.  The dQ product of an item needs dS from both key halves, so it
 // runs one item late: after the barrier that starts item t, every wave has written its
-// dS^T of item t-1, and the wave computes dQ of item t-1 before the products of item t.
+// dS^T of item t-1, and the wave computes dQ of item t-1 after the products of item t
+// (placed last, its LDS reads do not pile up right behind the barrier).
 // dS^T, K and V are therefore kept in two (dS^T) and three (K/V, a buffer per slice)
 // copies in LDS.
 //
@@ -668,7 +690,6 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
         const unsigned mb = *(const __attribute__((address_space(3))) unsigned*)(Ks + 2 * 64 * D * 2 + kl * 4);
         mterm = (kok && (mb & 0xFFu) == 0) ? kMaskNeg * kLog2e : 0.0f;
       }
-      if (t >= 1) dq_product(cur ^ 1);
 
       const char* qd = lds + oQD + cur * kQDB;   // this item's Q rows, then its dO rows
       const char* ld = lds + oLD + cur * kLDB + offRow;
@@ -691,9 +712,11 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
         const bf16x8 vf = *(const lbf16x8*)(Vs + offK + offR[cc]);
         dp = mfma32(ao, vf, dp);
       }
-      // P = exp2(c1 S + log2e bias - lse2) and dS = P (dP - D); dS is summed into the face
-      const lbf16* bS = (const lbf16*)(lds + oBias + cur * kBiasB + offBias);
-      const bf16x8 b0 = *(const lbf16x8*)bS, b1 = *(const lbf16x8*)(bS + 512);
+      // P = exp2(c1 S + log2e bias - lse2) and dS = P (dP - D); dS is summed into the face.
+      // The bias term log2e * bias - lse2 comes from one v_fma_mix_f32 per element (fp16
+      // bias pairs, -lse2 rows), independent of the products above.
+      const char* bS = lds + oBias + cur * kBiasB + offBias;
+      const u32x4v b0 = *(const lu32x4*)bS, b1 = *(const lu32x4*)(bS + 1024);
       float P[16], dS[16];
 #pragma unroll
       for (int R = 0; R < 4; R++) {
@@ -701,8 +724,9 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
 #pragma unroll
         for (int e = 0; e < 4; e++) {
           const int r = R * 4 + e;
-          const float bb = (float)(r < 8 ? b0[r] : b1[r - 8]);
-          float z = __builtin_fmaf(sacc[r], c1, __builtin_fmaf(bb, kLog2e, -lv[e]));
+          const unsigned pr = r < 8 ? b0[(r & 7) >> 1] : b1[(r & 7) >> 1];
+          const float zb = (r & 1) ? fma_mix_f16<1>(pr, kLog2e, lv[e]) : fma_mix_f16<0>(pr, kLog2e, lv[e]);
+          float z = __builtin_fmaf(sacc[r], c1, zb);
           if (MASK) z += mterm;
           P[r] = __builtin_amdgcn_exp2f(z);
           dS[r] = P[r] * dp[r];
@@ -736,6 +760,7 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
         dvT = mfma32(ao, pb[m2], dvT);
         dkT = mfma32(aq, sb[m2], dkT);
       }
+      if (t >= 1) dq_product(cur ^ 1);
       prev_sl = sl_row;
       prev_s = s;
       prev_kv = kvc;
@@ -988,7 +1013,7 @@ tri_attn_status launch_bwd(unsigned stages, const Plan& P, const void* q, const 
   const int64_t nb = P.B * P.H * P.Kp * P.Jp;
   if (stages & TRI_ATTN_STAGE_PREP) {
     hipLaunchKernelGGL(bias_prep_bwd_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, st,
-                       (const bf16*)bias, biasB, (int)P.N, (int)P.KB, (int)(P.Jp / 128), nb);
+                       (const bf16*)bias, (_Float16*)biasB, (int)P.N, (int)P.KB, (int)(P.Jp / 128), nb);
     const int64_t nrows = P.B * P.N * P.H;
     hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3((unsigned)(nrows * P.Jp * (D / 8) / 256)), dim3(256), 0, st,
                        (const bf16*)dO, (const bf16*)o, (const bf16*)res, lse, Dg, L2g, (int)P.N, (int)P.Jp,
