@@ -365,10 +365,19 @@ void fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
 #pragma unroll
     for (int r = 0; r < 16; r++) mx = fmaxf(mx, s[1][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float scale = __builtin_amdgcn_exp2f((m_run - m_new) * c1);
-    const float nm = m_new * c1;
-    m_run = m_new;
+    // The reference maximum of a query moves only when a score exceeds it by more than
+    // 2^8 in probability (exp2 units): probabilities stay <= 256, exact in FP32 and with
+    // bf16's relative precision, and most tiles skip the rescale of the accumulators.  The
+    // test is written so that a NaN comparison counts as growth.
+    if (!(mx * c1 <= m_run * c1 + 8.0f)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float scale = __builtin_amdgcn_exp2f((m_run - m_new) * c1);
+      m_run = m_new;
+      l_run *= scale;
+#pragma unroll
+      for (int r = 0; r < 16; r++) acc_o[r] *= scale;
+    }
+    const float nm = m_run * c1;
     float p[2][16];
     float lsum = 0.0f;
 #pragma unroll
@@ -378,9 +387,7 @@ void fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
         p[tt][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[tt][r], c1, -nm));
         lsum += p[tt][r];
       }
-    l_run = l_run * scale + lsum;
-#pragma unroll
-    for (int r = 0; r < 16; r++) acc_o[r] *= scale;
+    l_run += lsum;
 
     // O^T (channels x queries) += V^T P^T; lane group (l/16) selects channel half and key run
     const int G16 = l >> 4, chalf = G16 & 1;
