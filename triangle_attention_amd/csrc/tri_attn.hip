@@ -207,17 +207,20 @@ __device__ __forceinline__ i32x4 raw_rsrc(const void* base, int bytes) {
 __device__ __forceinline__ unsigned lds_addr(const void* p) {
   return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
-// 16 bytes per lane: lane l's bytes land at lds_wave_base + 16 l
-__device__ __forceinline__ void dma16_asm(i32x4 rsrc, unsigned voff, int soff, const void* lds_wave_base) {
-  const unsigned m0v = __builtin_amdgcn_readfirstlane(lds_addr(lds_wave_base));
+// 16 bytes per lane: lane l's bytes land at LDS byte address lds_wave_base + 16 l
+__device__ __forceinline__ void dma16_asm(i32x4 rsrc, unsigned voff, int soff, unsigned lds_wave_base) {
   asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
-               :: "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soff)), "s"(m0v) : "memory", "m0");
+               :: "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soff)),
+                  "s"(__builtin_amdgcn_readfirstlane(lds_wave_base)) : "memory", "m0");
 }
-// one byte per lane, zero-extended into lane l's dword at lds_wave_base + 4 l
-__device__ __forceinline__ void dma1_asm(i32x4 rsrc, unsigned voff, int soff, const void* lds_wave_base) {
-  const unsigned m0v = __builtin_amdgcn_readfirstlane(lds_addr(lds_wave_base));
+__device__ __forceinline__ void dma16_asm(i32x4 rsrc, unsigned voff, int soff, const void* lds_wave_base) {
+  dma16_asm(rsrc, voff, soff, lds_addr(lds_wave_base));
+}
+// one byte per lane, zero-extended into lane l's dword at LDS byte address lds_wave_base + 4 l
+__device__ __forceinline__ void dma1_asm(i32x4 rsrc, unsigned voff, int soff, unsigned lds_wave_base) {
   asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_ubyte %0, %1, %2 offen lds"
-               :: "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soff)), "s"(m0v) : "memory", "m0");
+               :: "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soff)),
+                  "s"(__builtin_amdgcn_readfirstlane(lds_wave_base)) : "memory", "m0");
 }
 
 // fma(float(h), c, x) for the low (SEL = 0) or high (SEL = 1) fp16 half h of `pair`, in one
@@ -435,14 +438,14 @@ void fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
 
 // D[b,i,h,j] = sum_c dO * (o + residual) in FP32 (or dO * o without a residual), written
 // negated (the main kernel starts its dO V^T accumulator from -D), with
-// -lse2 = -lse * log2(e), into rows padded to Jp floats (16-byte aligned, zero padding),
-// the layout the main kernel streams into LDS.  D/8 adjacent lanes share a row (16 bytes
+// -lse2 = -lse * log2(e).  Layout: per slice-head row, per 128-query step, 128 values of
+// -lse2 then 128 of -D (zero padding past N): one KiB per step, the block the main kernel
+// streams into LDS with one load per lane.  D/8 adjacent lanes share a row (16 bytes
 // each, so a wave reads contiguous memory); their partial sums combine in a fixed order.
 template <int D>
 __global__ __launch_bounds__(256)
 void bwd_pre_kernel(const bf16* __restrict__ dO, const bf16* __restrict__ o, const bf16* __restrict__ res,
-                    const float* __restrict__ lse, float* __restrict__ Dp, float* __restrict__ L2p, int N, int Jp,
-                    int64_t nrows) {
+                    const float* __restrict__ lse, float* __restrict__ LDp, int N, int Jp, int64_t nrows) {
   constexpr int LPR = D / 8;  // lanes per row
   // the grid covers nrows * Jp * LPR threads exactly (Jp * LPR is a multiple of 256)
   const int64_t gt = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -467,8 +470,9 @@ void bwd_pre_kernel(const bf16* __restrict__ dO, const bf16* __restrict__ o, con
   acc += __shfl_xor(acc, 1);
   if (LPR == 4) acc += __shfl_xor(acc, 2);
   if (part == 0) {
-    Dp[prow] = -acc;
-    L2p[prow] = j < N ? -lse[row * N + j] * kLog2e : 0.0f;
+    float* dst = LDp + row * 2 * Jp + (j >> 7) * 256 + (j & 127);
+    dst[0] = j < N ? -lse[row * N + j] * kLog2e : 0.0f;
+    dst[128] = -acc;
   }
 }
 
@@ -526,8 +530,7 @@ template <int D, bool MASK>
 __global__ __launch_bounds__(512, 1)
 void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
                 const bf16* __restrict__ dO, const bf16* __restrict__ biasB, const uint8_t* __restrict__ mask,
-                const float* __restrict__ L2p, const float* __restrict__ Dp,
-                unsigned* __restrict__ dqp, float* __restrict__ dbp, bf16* __restrict__ dk, bf16* __restrict__ dv,
+                const float* __restrict__ LDp, unsigned* __restrict__ dqp, float* __restrict__ dbp, bf16* __restrict__ dk, bf16* __restrict__ dv,
                 int B, int N, int H, int G, int ngroups, float alpha) {
   constexpr int NC = D / 16;
   constexpr int CPR = D / 8;    // 16-byte chunks per row
@@ -577,7 +580,6 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   const unsigned qd_vo = (unsigned)(((tid / CPR) * D + ((tid % CPR) ^ swz<D>(tid / CPR)) * 8) * 2);
   const int kv_t = tid & 255;  // K (waves 0-3) / V (waves 4-7)
   const unsigned kv_vo = (unsigned)(((kb * 64 + kv_t / CPR) * D + ((kv_t % CPR) ^ swz<D>(kv_t / CPR)) * 8) * 2);
-  const unsigned row_vo = (unsigned)(l & 31) * 16u;
   const bf16* bias_blk = biasB + ((int64_t)(b * H + h) * KB + kb) * (int64_t)nsteps * 8192;
 
   // Per-lane LDS byte offsets of the operand reads; the buffer and the step enter as uniform
@@ -607,25 +609,39 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   const unsigned offSTr = (unsigned)((8 * G16 * LDT + (w >> 1) * 32 + (w & 1) * 16 + tr_lane(LDT)) * 2);
 
   // issue the loads of work item (ii, ss) into LDS buffer `buf`; rows past N read as zeros
-  auto prefetch = [&](int ii, int ss, int buf) {
+  // LDS byte address of the work-group's LDS block; the streamed loads take LDS addresses
+  // relative to it and buffer descriptors built once per slice (the buffer range of a
+  // slice-head row returns zeros for rows past N)
+  const unsigned lds0 = __builtin_amdgcn_readfirstlane(lds_addr(lds));
+  const i32x4 rbias = raw_rsrc(bias_blk, nsteps * 16384);  // this work-group's pair-bias column
+  // per slice-head row: the base addresses of its Q, dO and row-statistics rows (the
+  // descriptors' other words are fixed)
+  struct RowRes { i32x4 q, dO, ld; };
+  auto row_res = [&](int ii) {
     const int64_t sl = ((int64_t)b * N + ii) * H + h;  // slice-head row index
+    RowRes r;
+    r.q = raw_rsrc(q + sl * slice_elems, N * D * 2);
+    r.dO = raw_rsrc(dO + sl * slice_elems, N * D * 2);
+    r.ld = raw_rsrc(LDp + sl * 2 * Jp, Jp * 8);
+    return r;
+  };
+  // issue the loads of work item (slice with row descriptors rr, step ss) into LDS buffer `buf`
+  auto prefetch = [&](const RowRes& rr, int ss, int buf) {
+    static_assert(2 * CPR <= 8, "Q/dO rows of a step in one load per wave");
     if (w < 2 * CPR) {
-      dma16_asm(raw_rsrc(q + sl * slice_elems, N * D * 2), qd_vo, ss * 128 * D * 2, lds + oQD + buf * kQDB + w * 1024);
-      dma16_asm(raw_rsrc(dO + sl * slice_elems, N * D * 2), qd_vo, ss * 128 * D * 2,
-                lds + oQD + buf * kQDB + 128 * D * 2 + w * 1024);
+      dma16_asm(rr.q, qd_vo, ss * 128 * D * 2, lds0 + oQD + buf * kQDB + w * 1024);
+      dma16_asm(rr.dO, qd_vo, ss * 128 * D * 2, lds0 + oQD + buf * kQDB + 128 * D * 2 + w * 1024);
     }
-    if (w == 0 && l < 32) dma16_asm(raw_rsrc(L2p + sl * Jp, Jp * 4), row_vo, ss * 512, lds + oLD + buf * kLDB);
-    if (w == 1 && l < 32) dma16_asm(raw_rsrc(Dp + sl * Jp, Jp * 4), row_vo, ss * 512, lds + oLD + buf * kLDB + 512);
+    if (w == 0) dma16_asm(rr.ld, (unsigned)l * 16u, ss * 1024, lds0 + oLD + buf * kLDB);
     // this step's pair-bias tiles: 16 KiB, 2 KiB per wave
-    const i32x4 rb = raw_rsrc(bias_blk + (int64_t)ss * 8192 + w * 1024, 2048);
-    dma16_asm(rb, (unsigned)l * 16u, 0, lds + oBias + buf * kBiasB + w * 2048);
-    dma16_asm(rb, (unsigned)l * 16u, 1024, lds + oBias + buf * kBiasB + w * 2048 + 1024);
+    dma16_asm(rbias, (unsigned)l * 16u, ss * 16384 + w * 2048, lds0 + oBias + buf * kBiasB + w * 2048);
+    dma16_asm(rbias, (unsigned)l * 16u, ss * 16384 + w * 2048 + 1024, lds0 + oBias + buf * kBiasB + w * 2048 + 1024);
   };
   // K, V and the key-mask bytes of slice ii into K/V buffer kvb
   auto prefetch_kv = [&](int ii, int kvb) {
     constexpr int KC = 64 * CPR;  // 16-byte chunks per block
     const int64_t sl = ((int64_t)b * N + ii) * H + h;
-    char* dst = lds + oKV + kvb * kKVB;
+    const unsigned dst = lds0 + oKV + kvb * kKVB;
     if (w < KC / 64) dma16_asm(raw_rsrc(k + sl * slice_elems, N * D * 2), kv_vo, 0, dst + w * 1024);
     else if (w >= 4 && w < 4 + KC / 64)
       dma16_asm(raw_rsrc(v + sl * slice_elems, N * D * 2), kv_vo, 0, dst + 64 * D * 2 + (w - 4) * 1024);
@@ -638,7 +654,8 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   for (int s = 0; s < kBwdMaxSteps; s++) face[s] = f32x16{};
 
   prefetch_kv(i_begin, 0);
-  prefetch(i_begin, 0, 0);
+  RowRes rr_cur = row_res(i_begin);  // descriptors of slice i
+  prefetch(rr_cur, 0, 0);
 
   // dQ^T tiles (16 channels x 16 queries) of the previous item over the 64 keys of this
   // block, stored as this block's partial in 24-bit form: one 16 x D block per (slice,
@@ -682,6 +699,7 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
     const char* Vs = Ks + 64 * D * 2;
     float mterm = 0.0f;
     f32x16 dkT = {}, dvT = {};
+    const RowRes rr_next = row_res(min(i + 1, i_end - 1));  // descriptors of slice i+1
 
     auto step = [&](auto S_) {
       constexpr int s = decltype(S_)::value;
@@ -691,8 +709,14 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
       else wait_vmcnt((t >= 2 ? kDqStores : 0) + (s == 0 ? kvStores : 0));
       lds_barrier();  // item t is in LDS everywhere, dS^T of item t-1 is complete, the other buffers are free
       if (s == 0 && i + 1 < i_end) prefetch_kv(i + 1, (i + 1 - i_begin) % 3);
-      if (s + 1 < nsteps) prefetch(i, s + 1, cur ^ 1);
-      else if (i + 1 < i_end) prefetch(i + 1, 0, cur ^ 1);
+      {  // the next item: step s+1 of this slice, else step 0 of the next slice
+        const bool same = s + 1 < nsteps;
+        RowRes rn;
+        rn.q = same ? rr_cur.q : rr_next.q;
+        rn.dO = same ? rr_cur.dO : rr_next.dO;
+        rn.ld = same ? rr_cur.ld : rr_next.ld;
+        if (same || i + 1 < i_end) prefetch(rn, same ? s + 1 : 0, cur ^ 1);
+      }
       if (MASK && s == 0) {
         const unsigned mb = *(const __attribute__((address_space(3))) unsigned*)(Ks + 2 * 64 * D * 2 + kl * 4);
         mterm = (kok && (mb & 0xFFu) == 0) ? kMaskNeg * kLog2e : 0.0f;
@@ -782,6 +806,7 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
     if (nsteps > 4) step(std::integral_constant<int, 4>{});
     if (nsteps > 5) step(std::integral_constant<int, 5>{});
     static_assert(kBwdMaxSteps == 6, "six unrolled steps");
+    rr_cur = rr_next;
 
     // end of slice i: dK^T and dV^T summed over the four query lanes as (p0 + p1) + (p2 + p3)
     // through a dedicated LDS area (no other data lives there, so the first write needs no
@@ -928,7 +953,7 @@ struct Plan {
   int64_t rows;             // B*N*H*N
   int64_t bias_f32_bytes;   // prepared forward bias (FP32 tiles)
   int64_t bias_b16_bytes;   // prepared backward bias (bf16 column blocks)
-  int64_t off_D, off_L2, off_dqp, off_dbp, bwd_bytes;
+  int64_t off_LD, off_dqp, off_dbp, bwd_bytes;
 };
 
 constexpr int64_t kAlign = 256;
@@ -956,9 +981,8 @@ Plan make_plan(int64_t B, int64_t N, int64_t H, int64_t D) {
   p.rows = B * N * H * N;
   p.bias_f32_bytes = round_up(B * H * p.Kp * p.Jp * 4, kAlign);
   p.bias_b16_bytes = round_up(B * H * p.Kp * p.Jp * 2, kAlign);
-  p.off_D = p.bias_b16_bytes;
-  p.off_L2 = p.off_D + round_up(B * N * H * p.Jp * 4, kAlign);
-  p.off_dqp = p.off_L2 + round_up(B * N * H * p.Jp * 4, kAlign);
+  p.off_LD = p.bias_b16_bytes;
+  p.off_dqp = p.off_LD + round_up(B * N * H * p.Jp * 2 * 4, kAlign);
   p.off_dbp = p.off_dqp + round_up(p.KB * B * N * H * p.Jp * D * 2, kAlign);
   p.bwd_bytes = p.off_dbp + round_up(p.ngroups * B * H * N * N * 4, kAlign);
   return p;
@@ -1013,8 +1037,7 @@ tri_attn_status launch_bwd(unsigned stages, const Plan& P, const void* q, const 
   const float alpha = 1.0f / sqrtf((float)D);
   char* base = (char*)ws;
   bf16* biasB = (bf16*)base;
-  float* Dg = (float*)(base + P.off_D);
-  float* L2g = (float*)(base + P.off_L2);
+  float* LDg = (float*)(base + P.off_LD);
   unsigned* dqp = (unsigned*)(base + P.off_dqp);
   float* dbp = (float*)(base + P.off_dbp);
   const int64_t nb = P.B * P.H * P.Kp * P.Jp;
@@ -1023,18 +1046,18 @@ tri_attn_status launch_bwd(unsigned stages, const Plan& P, const void* q, const 
                        (const bf16*)bias, (_Float16*)biasB, (int)P.N, (int)P.KB, (int)(P.Jp / 128), nb);
     const int64_t nrows = P.B * P.N * P.H;
     hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3((unsigned)(nrows * P.Jp * (D / 8) / 256)), dim3(256), 0, st,
-                       (const bf16*)dO, (const bf16*)o, (const bf16*)res, lse, Dg, L2g, (int)P.N, (int)P.Jp,
+                       (const bf16*)dO, (const bf16*)o, (const bf16*)res, lse, LDg, (int)P.N, (int)P.Jp,
                        nrows);
   }
   const int64_t ntiles = P.B * P.H * P.ngroups * P.KB;
   if (!(stages & TRI_ATTN_STAGE_MAIN)) {
   } else if (mask)
     hipLaunchKernelGGL((bwd_kernel<D, true>), dim3(grid_xcd(ntiles)), dim3(512), 0, st, (const bf16*)q,
-                       (const bf16*)k, (const bf16*)v, (const bf16*)dO, biasB, mask, L2g, Dg, dqp, dbp, (bf16*)dk,
+                       (const bf16*)k, (const bf16*)v, (const bf16*)dO, biasB, mask, LDg, dqp, dbp, (bf16*)dk,
                        (bf16*)dv, (int)P.B, (int)P.N, (int)P.H, (int)P.G, (int)P.ngroups, alpha);
   else
     hipLaunchKernelGGL((bwd_kernel<D, false>), dim3(grid_xcd(ntiles)), dim3(512), 0, st, (const bf16*)q,
-                       (const bf16*)k, (const bf16*)v, (const bf16*)dO, biasB, mask, L2g, Dg, dqp, dbp, (bf16*)dk,
+                       (const bf16*)k, (const bf16*)v, (const bf16*)dO, biasB, mask, LDg, dqp, dbp, (bf16*)dk,
                        (bf16*)dv, (int)P.B, (int)P.N, (int)P.H, (int)P.G, (int)P.ngroups, alpha);
   if (stages & TRI_ATTN_STAGE_FINAL) {
     const int64_t nslots = P.B * P.N * P.H * (P.Jp / 16) * 64;
