@@ -195,7 +195,11 @@ __device__ __forceinline__ void dma16b(__amdgpu_buffer_rsrc_t r, unsigned voff, 
 // prefetch issued one item ahead.  In this form the loads are invisible to the compiler's
 // wait-count tracking; the kernels wait for them explicitly (vmcnt) before the barrier that
 // publishes the data.  rsrc is a raw buffer descriptor (wave-uniform): base address, byte
-// count (reads at or past it return zeros), raw flags.
+// count (reads at or past it return zeros), raw flags.  The compiler does not look inside
+// the statement for hazards, so it carries its own wait states: one between the write of
+// M0 and the load that reads it, and five before a load whose scalar operands a vector
+// instruction (readfirstlane, readlane) may have just written; s_nop 4 after the M0 write
+// gives six.
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ i32x4 raw_rsrc(const void* base, int bytes) {
   const unsigned long long a = (unsigned long long)(uintptr_t)base;
@@ -209,7 +213,7 @@ __device__ __forceinline__ unsigned lds_addr(const void* p) {
 }
 // 16 bytes per lane: lane l's bytes land at LDS byte address lds_wave_base + 16 l
 __device__ __forceinline__ void dma16_asm(i32x4 rsrc, unsigned voff, int soff, unsigned lds_wave_base) {
-  asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+  asm volatile("s_mov_b32 m0, %3\n\ts_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
                :: "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soff)),
                   "s"(__builtin_amdgcn_readfirstlane(lds_wave_base)) : "memory", "m0");
 }
@@ -218,13 +222,16 @@ __device__ __forceinline__ void dma16_asm(i32x4 rsrc, unsigned voff, int soff, c
 }
 // one byte per lane, zero-extended into lane l's dword at LDS byte address lds_wave_base + 4 l
 __device__ __forceinline__ void dma1_asm(i32x4 rsrc, unsigned voff, int soff, unsigned lds_wave_base) {
-  asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_ubyte %0, %1, %2 offen lds"
+  asm volatile("s_mov_b32 m0, %3\n\ts_nop 4\n\tbuffer_load_ubyte %0, %1, %2 offen lds"
                :: "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soff)),
                   "s"(__builtin_amdgcn_readfirstlane(lds_wave_base)) : "memory", "m0");
 }
 
 // fma(float(h), c, x) for the low (SEL = 0) or high (SEL = 1) fp16 half h of `pair`, in one
-// v_fma_mix_f32 (the fp16 operand is widened exactly inside the instruction).
+// v_fma_mix_f32 (the fp16 operand is widened exactly inside the instruction).  Its operands
+// must come from memory loads or ordinary vector instructions, never straight from a
+// matrix product: the compiler does not insert the wait states a product's result needs
+// before an inline assembly statement reads it.
 template <int SEL>
 __device__ __forceinline__ float fma_mix_f16(unsigned pair, float c, float x) {
   float r;
