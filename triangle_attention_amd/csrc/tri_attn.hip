@@ -248,7 +248,9 @@ __device__ __forceinline__ float fma_mix_f16(unsigned pair, float c, float x) {
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_sched_barrier(0);   // no instruction moves across (register pressure)
   __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
   asm volatile("" ::: "memory");
 }
 
@@ -533,7 +535,7 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
   }
 }
 
-template <int D, bool MASK>
+template <int D, bool MASK, int NS>
 __global__ __launch_bounds__(512, 1)
 void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
                 const bf16* __restrict__ dO, const bf16* __restrict__ biasB, const uint8_t* __restrict__ mask,
@@ -574,11 +576,13 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   const int kl = kh * 32 + ln;          // key within the block
   const int kg = kb * 64 + kl;          // global key of this lane
   const bool kok = kg < N;
-  const int Jp = (int)round_up(N, 128);
+  // NS = ceil(N / 128) 128-query steps per slice, fixed at compile time so that the step
+  // loop, its buffer parity (for even NS) and every step offset are constants
+  constexpr int nsteps = NS;
+  constexpr int Jp = NS * 128;
   const float c1 = alpha * kLog2e;
   const int64_t slice_elems = (int64_t)N * D;
-  const int nsteps = (N + 127) / 128;
-  const int nqt = Jp / 16;                                               // 16-query tiles per slice
+  constexpr int nqt = Jp / 16;                                           // 16-query tiles per slice
   const int64_t dq_kb_stride = (int64_t)B * N * H * nqt * (16 * D * 2);  // bytes of one key block's partials
   const int nitems = (i_end - i_begin) * nsteps;
 
@@ -656,9 +660,9 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
       dma1_asm(raw_rsrc(mask + ((int64_t)b * N + ii) * N, N), (unsigned)(kb * 64 + l), 0, dst + 2 * 64 * D * 2);
   };
 
-  f32x16 face[kBwdMaxSteps];
+  f32x16 face[NS];
 #pragma unroll
-  for (int s = 0; s < kBwdMaxSteps; s++) face[s] = f32x16{};
+  for (int s = 0; s < NS; s++) face[s] = f32x16{};
 
   prefetch_kv(i_begin, 0);
   RowRes rr_cur = row_res(i_begin);  // descriptors of slice i
@@ -696,8 +700,10 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   // the previous item's dq stores and, after the last item of a slice, the dK/dV stores
   constexpr int kDqStores = 1;
   const int kvStores = p == 0 ? 2 * (NR / 4) : 0;  // dk and dv stores of a slice's end
-  int t = 0;     // item index within the work-group
-  int cur = 0;   // LDS buffer of item t
+  int ns_rt = NS;
+  asm volatile("" : "+s"(ns_rt));
+  int t = 0;        // item index within the work-group
+  int cur_rt = 0;   // LDS buffer of item t (its parity)
   for (int i = i_begin; i < i_end; i++) {
     const int64_t sl_row = ((int64_t)b * N + i) * H + h;  // slice-head row index
     const int64_t sbase = sl_row * slice_elems;
@@ -710,6 +716,9 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
 
     auto step = [&](auto S_) {
       constexpr int s = decltype(S_)::value;
+      // (a run-time value: with constant buffer offsets the compiler would keep a base
+      // register per buffer and region live across the loop)
+      const int cur = cur_rt;
       // wait for item t's loads (issued one item earlier); what follows them in the queue
       // is the previous item's dq stores and, at a slice start, the dK/dV stores
       if (t == 0) wait_vmcnt(0);
@@ -802,17 +811,19 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
       prev_sl = sl_row;
       prev_s = s;
       prev_kv = kvc;
-      cur ^= 1;
+      cur_rt ^= 1;
       t++;
     };
 
     step(std::integral_constant<int, 0>{});
-    if (nsteps > 1) step(std::integral_constant<int, 1>{});
-    if (nsteps > 2) step(std::integral_constant<int, 2>{});
-    if (nsteps > 3) step(std::integral_constant<int, 3>{});
-    if (nsteps > 4) step(std::integral_constant<int, 4>{});
-    if (nsteps > 5) step(std::integral_constant<int, 5>{});
-    static_assert(kBwdMaxSteps == 6, "six unrolled steps");
+    // (the steps stay behind run-time branches on an opaque copy of the step count: as one
+    // straight block the compiler's register allocation of the six steps spills)
+    if (ns_rt > 1) step(std::integral_constant<int, 1 < NS ? 1 : 0>{});
+    if (ns_rt > 2) step(std::integral_constant<int, 2 < NS ? 2 : 0>{});
+    if (ns_rt > 3) step(std::integral_constant<int, 3 < NS ? 3 : 0>{});
+    if (ns_rt > 4) step(std::integral_constant<int, 4 < NS ? 4 : 0>{});
+    if (ns_rt > 5) step(std::integral_constant<int, 5 < NS ? 5 : 0>{});
+    static_assert(NS >= 1 && NS <= kBwdMaxSteps && kBwdMaxSteps == 6, "at most six unrolled steps");
     rr_cur = rr_next;
 
     // end of slice i: dK^T and dV^T summed over the four query lanes as (p0 + p1) + (p2 + p3)
@@ -864,18 +875,16 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   }
   // the last item's dQ product
   lds_barrier();
-  dq_product(cur ^ 1);
+  dq_product(cur_rt ^ 1);
 
   // write this group's pair-bias gradient partial: dbp[grp][b][h][j][k]
   float* dst = dbp + (((int64_t)grp * B + b) * H + h) * (int64_t)N * N;
 #pragma unroll
-  for (int s = 0; s < kBwdMaxSteps; s++) {
-    if (s < nsteps) {
+  for (int s = 0; s < NS; s++) {
 #pragma unroll
-      for (int r = 0; r < 16; r++) {
-        const int jj = s * 128 + p * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
-        if (jj < N && kok) dst[(int64_t)jj * N + kg] = face[s][r];
-      }
+    for (int r = 0; r < 16; r++) {
+      const int jj = s * 128 + p * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
+      if (jj < N && kok) dst[(int64_t)jj * N + kg] = face[s][r];
     }
   }
 }
@@ -1056,16 +1065,28 @@ tri_attn_status launch_bwd(unsigned stages, const Plan& P, const void* q, const 
                        (const bf16*)dO, (const bf16*)o, (const bf16*)res, lse, LDg, (int)P.N, (int)P.Jp,
                        nrows);
   }
-  const int64_t ntiles = P.B * P.H * P.ngroups * P.KB;
-  if (!(stages & TRI_ATTN_STAGE_MAIN)) {
-  } else if (mask)
-    hipLaunchKernelGGL((bwd_kernel<D, true>), dim3(grid_xcd(ntiles)), dim3(512), 0, st, (const bf16*)q,
-                       (const bf16*)k, (const bf16*)v, (const bf16*)dO, biasB, mask, LDg, dqp, dbp, (bf16*)dk,
-                       (bf16*)dv, (int)P.B, (int)P.N, (int)P.H, (int)P.G, (int)P.ngroups, alpha);
-  else
-    hipLaunchKernelGGL((bwd_kernel<D, false>), dim3(grid_xcd(ntiles)), dim3(512), 0, st, (const bf16*)q,
-                       (const bf16*)k, (const bf16*)v, (const bf16*)dO, biasB, mask, LDg, dqp, dbp, (bf16*)dk,
-                       (bf16*)dv, (int)P.B, (int)P.N, (int)P.H, (int)P.G, (int)P.ngroups, alpha);
+  if (stages & TRI_ATTN_STAGE_MAIN) {
+    const int64_t ntiles = P.B * P.H * P.ngroups * P.KB;
+    auto launch = [&](auto ns_) {
+      constexpr int NS = decltype(ns_)::value;
+      if (mask)
+        hipLaunchKernelGGL((bwd_kernel<D, true, NS>), dim3(grid_xcd(ntiles)), dim3(512), 0, st, (const bf16*)q,
+                           (const bf16*)k, (const bf16*)v, (const bf16*)dO, biasB, mask, LDg, dqp, dbp, (bf16*)dk,
+                           (bf16*)dv, (int)P.B, (int)P.N, (int)P.H, (int)P.G, (int)P.ngroups, alpha);
+      else
+        hipLaunchKernelGGL((bwd_kernel<D, false, NS>), dim3(grid_xcd(ntiles)), dim3(512), 0, st, (const bf16*)q,
+                           (const bf16*)k, (const bf16*)v, (const bf16*)dO, biasB, mask, LDg, dqp, dbp, (bf16*)dk,
+                           (bf16*)dv, (int)P.B, (int)P.N, (int)P.H, (int)P.G, (int)P.ngroups, alpha);
+    };
+    switch (P.Jp / 128) {  // 128-query steps per slice (shape_ok bounds N by TRI_ATTN_MAX_N)
+      case 1: launch(std::integral_constant<int, 1>{}); break;
+      case 2: launch(std::integral_constant<int, 2>{}); break;
+      case 3: launch(std::integral_constant<int, 3>{}); break;
+      case 4: launch(std::integral_constant<int, 4>{}); break;
+      case 5: launch(std::integral_constant<int, 5>{}); break;
+      default: launch(std::integral_constant<int, 6>{}); break;
+    }
+  }
   if (stages & TRI_ATTN_STAGE_FINAL) {
     const int64_t nslots = P.B * P.N * P.H * (P.Jp / 16) * 64;
     hipLaunchKernelGGL(reduce_dq_kernel<D>, dim3((unsigned)((nslots + 255) / 256)), dim3(256), 0, st, dqp,
