@@ -744,30 +744,44 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
       // S = Q K^T (rows: 32 queries, cols: 32 keys) and dP - D = dO V^T - D, the second
       // accumulator starting from -D
       f32x16 sacc = {}, dp;
+      // all operand reads of the two products are issued before the first product, so that
+      // their latencies overlap instead of chaining read -> product -> read
+      bf16x8 aq[NC], kf[NC], ao[NC], vf[NC];
+#pragma unroll
+      for (int cc = 0; cc < NC; cc++) {
+        aq[cc] = *(const lbf16x8*)(qd + offQ + offR[cc]);
+        kf[cc] = *(const lbf16x8*)(Ks + offK + offR[cc]);
+        ao[cc] = *(const lbf16x8*)(qd + 128 * D * 2 + offQ + offR[cc]);
+        vf[cc] = *(const lbf16x8*)(Vs + offK + offR[cc]);
+      }
 #pragma unroll
       for (int R = 0; R < 4; R++) {
         const f32x4 x = *(const lf32x4*)(ld + 512 + R * 32);
 #pragma unroll
         for (int e = 0; e < 4; e++) dp[R * 4 + e] = x[e];
       }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int cc = 0; cc < NC; cc++) {
-        const bf16x8 aq = *(const lbf16x8*)(qd + offQ + offR[cc]);
-        const bf16x8 kf = *(const lbf16x8*)(Ks + offK + offR[cc]);
-        sacc = mfma32(aq, kf, sacc);
-        const bf16x8 ao = *(const lbf16x8*)(qd + 128 * D * 2 + offQ + offR[cc]);
-        const bf16x8 vf = *(const lbf16x8*)(Vs + offK + offR[cc]);
-        dp = mfma32(ao, vf, dp);
+        sacc = mfma32(aq[cc], kf[cc], sacc);
+        dp = mfma32(ao[cc], vf[cc], dp);
       }
       // P = exp2(c1 S + log2e bias - lse2) and dS = P (dP - D); dS is summed into the face.
       // The bias term log2e * bias - lse2 comes from one v_fma_mix_f32 per element (fp16
       // bias pairs, -lse2 rows), independent of the products above.
       const char* bS = lds + oBias + cur * kBiasB + offBias;
       const u32x4v b0 = *(const lu32x4*)bS, b1 = *(const lu32x4*)(bS + 1024);
+      // at D = 16 the four lse2 rows are read at once, while the products run; at D = 32 the
+      // registers for that are not free, and each row is read just before its use
+      f32x4 lvb[4];
+      if (D == 16) {
+#pragma unroll
+        for (int R = 0; R < 4; R++) lvb[R] = *(const lf32x4*)(ld + R * 32);
+      }
       float P[16], dS[16];
 #pragma unroll
       for (int R = 0; R < 4; R++) {
-        const f32x4 lv = *(const lf32x4*)(ld + R * 32);
+        const f32x4 lv = D == 16 ? lvb[R] : *(const lf32x4*)(ld + R * 32);
 #pragma unroll
         for (int e = 0; e < 4; e++) {
           const int r = R * 4 + e;
