@@ -677,17 +677,23 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
     const char* kbase = lds + oKV + prev_kv * kKVB;
     const char* sbase_t = lds + oST + stb * kSTB + offSTr;
     bf16x4 pk[NC];
+    // all operands first (one latency), then the products
+    bf16x8 a[NC][2], bb[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; kk++) {
+      bb[kk] = cat8(tr16p((const lbf16*)(sbase_t + kk * 32 * LDT * 2)),
+                    tr16p((const lbf16*)(sbase_t + (kk * 32 + 4) * LDT * 2)));
+#pragma unroll
+      for (int u = 0; u < NC; u++)
+        a[u][kk] = cat8(tr16p((const lbf16*)(kbase + trK[u][0] + kk * 32 * D * 2)),
+                        tr16p((const lbf16*)(kbase + trK[u][1] + kk * 32 * D * 2)));
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < NC; u++) {
       f32x4 c = {};
 #pragma unroll
-      for (int kk = 0; kk < 64; kk += 32) {
-        const bf16x8 a = cat8(tr16p((const lbf16*)(kbase + trK[u][0] + kk * D * 2)),
-                              tr16p((const lbf16*)(kbase + trK[u][1] + kk * D * 2)));
-        const bf16x8 bb = cat8(tr16p((const lbf16*)(sbase_t + kk * LDT * 2)),
-                               tr16p((const lbf16*)(sbase_t + (kk + 4) * LDT * 2)));
-        c = mfma16(a, bb, c);
-      }
+      for (int kk = 0; kk < 2; kk++) c = mfma16(a[u][kk], bb[kk], c);
 #pragma unroll
       for (int e = 0; e < 4; e++) pk[u][e] = (bf16)c[e];
     }
