@@ -70,6 +70,7 @@ typedef __attribute__((address_space(3))) f32x4 lf32x4;
 typedef __attribute__((address_space(3))) s16x4 ls16x4;
 typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) u32x4v lu32x4;
+typedef unsigned u32x2v __attribute__((ext_vector_type(2)));
 
 // Lane part of a transposed read: lane t of a 16-lane group addresses row t/4 and
 // column 4*(t%4) of the 4x16 block it helps to load.
@@ -698,8 +699,13 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
       for (int e = 0; e < 4; e++) pk[u][e] = (bf16)c[e];
     }
     char* blk = (char*)dqp + kb * dq_kb_stride + ((prev_sl * nqt + prev_s * 8 + w) * (int64_t)(16 * D * 2));
-    if (NC == 2) *(bf16x8*)(blk + l * 16) = __builtin_shufflevector(pk[0], pk[NC - 1], 0, 1, 2, 3, 4, 5, 6, 7);
-    else *(bf16x4*)(blk + l * 8) = pk[0];
+    // streaming stores: the partials are read back once, by the final reduction
+    if (NC == 2) {
+      const bf16x8 v8 = __builtin_shufflevector(pk[0], pk[NC - 1], 0, 1, 2, 3, 4, 5, 6, 7);
+      __builtin_nontemporal_store(__builtin_bit_cast(u32x4v, v8), (u32x4v*)(blk + l * 16));
+    } else {
+      __builtin_nontemporal_store(__builtin_bit_cast(u32x2v, pk[0]), (u32x2v*)(blk + l * 8));
+    }
   };
 
   // VMEM operations a wave issues after an item's prefetch and before that item's wait:
@@ -936,7 +942,7 @@ void reduce_dq_kernel(const unsigned* __restrict__ dqp, bf16* __restrict__ dq, i
   const char* base = (const char*)dqp + blk * BLK + lane * (int)sizeof(V);
   V x[kMaxKB];
 #pragma unroll
-  for (int kb = 0; kb < kMaxKB; kb++) x[kb] = *(const V*)(base + min(kb, KB - 1) * kb_stride);
+  for (int kb = 0; kb < kMaxKB; kb++) x[kb] = __builtin_nontemporal_load((const V*)(base + min(kb, KB - 1) * kb_stride));
   float acc[4 * NC];
 #pragma unroll
   for (int e = 0; e < 4 * NC; e++) acc[e] = (float)x[0][e];
