@@ -243,6 +243,12 @@ __device__ __forceinline__ float fma_mix_f16(unsigned pair, float c, float x) {
   return r;
 }
 
+// Non-temporal (streaming) 16-byte global load: data read once per pass, kept out of the way
+// of the tiles that are re-read.  (Streaming stores of partial lines measured slower.)
+__device__ __forceinline__ bf16x8 ld_nt(const bf16x8* p) {
+  return __builtin_bit_cast(bf16x8, __builtin_nontemporal_load((const u32x4v*)p));
+}
+
 // Work-group barrier that orders LDS accesses only.  __syncthreads() also waits for every
 // outstanding global access of the wave (its release fence covers the direct-to-LDS loads),
 // which would expose the latency of a prefetch issued just before it.
@@ -467,9 +473,9 @@ void bwd_pre_kernel(const bf16* __restrict__ dO, const bf16* __restrict__ o, con
   if (j < N) {
     const int64_t off = (row * N + j) * D + part * 8;
     const bf16x8 a = *(const bf16x8*)(dO + off);
-    const bf16x8 ov = *(const bf16x8*)(o + off);
+    const bf16x8 ov = ld_nt((const bf16x8*)(o + off));
     if (res) {
-      const bf16x8 rv = *(const bf16x8*)(res + off);
+      const bf16x8 rv = ld_nt((const bf16x8*)(res + off));
 #pragma unroll
       for (int e = 0; e < 8; e++) acc = __builtin_fmaf((float)a[e], (float)ov[e] + (float)rv[e], acc);
     } else {
@@ -974,7 +980,7 @@ void reduce_dbias_kernel(const float* __restrict__ dbp, float* __restrict__ dbia
   for (int g0 = 0; g0 < ngroups; g0 += U) {
     T x[U];
 #pragma unroll
-    for (int u = 0; u < U; u++) x[u] = *(const T*)(dbp + (int64_t)min(g0 + u, ngroups - 1) * n + t * W);
+    for (int u = 0; u < U; u++) x[u] = __builtin_nontemporal_load((const T*)(dbp + (int64_t)min(g0 + u, ngroups - 1) * n + t * W));
 #pragma unroll
     for (int u = 0; u < U; u++) {
       if (g0 + u == 0) s = x[u];
