@@ -717,7 +717,11 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   // VMEM operations a wave issues after an item's prefetch and before that item's wait:
   // the previous item's dq stores and, after the last item of a slice, the dK/dV stores
   constexpr int kDqStores = 1;
-  const int kvStores = p == 0 ? 2 * (NR / 4) : 0;  // dk and dv stores of a slice's end
+  // dk and dv stores of a slice's end: p = 0 waves whose 32 keys are not all past N (the
+  // stores sit behind that wave-uniform test, so each one the count includes is issued with
+  // at least one active lane)
+  const bool any_key = kb * 64 + kh * 32 < N;
+  const int kvStores = (p == 0 && any_key) ? 2 * (NR / 4) : 0;
   int ns_rt = NS;
   asm volatile("" : "+s"(ns_rt));
   int t = 0;        // item index within the work-group
@@ -886,7 +890,7 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
       }
     }
     lds_barrier();
-    if (p == 0) {
+    if (p == 0 && any_key) {
       const int slot2 = (kh * 2 + 1) * (2 * NR * 64) + l;
 #pragma unroll
       for (int R = 0; R < NR / 4; R++) {
