@@ -676,8 +676,8 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   prefetch(rr_cur, 0, 0);
 
   // dQ^T tiles (16 channels x 16 queries) of the previous item over the 64 keys of this
-  // block, stored as this block's partial in 24-bit form: one 16 x D block per (slice,
-  // 16-query tile), lane-major, so that every store writes whole cache lines
+  // block, stored as this block's bf16 partial: one 16 x D block per (slice, 16-query tile),
+  // lane-major, so that every store writes whole cache lines
   int64_t prev_sl = 0;
   int prev_s = 0, prev_kv = 0;
   auto dq_product = [&](int stb) {
