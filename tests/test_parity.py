@@ -46,6 +46,7 @@ SMALL = [
     (1, 130, 1, 32, "tail"),
     (1, 200, 2, 32, "random"),
     (1, 257, 1, 16, None),
+    (1, 450, 1, 32, "random"),  # four query steps; the last key block's upper half lies past N
 ]
 
 
