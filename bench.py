@@ -42,6 +42,8 @@ def _parse():
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--no-residual", action="store_true", help="uncompensated backward correction")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle CPU-baseline budget (0 = skip)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the whole fwd+bwd step captured in one HIP graph (small-N launch latency)")
     return ap.parse_args()
 
 
@@ -120,16 +122,17 @@ def main():
     fws = torch.empty(ta.tri_attn_fwd_workspace_bytes(B, N, H, D), dtype=torch.uint8, device=dev)
     bws = torch.empty(ta.tri_attn_bwd_workspace_bytes(B, N, H, D), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
-    sh = stream.cuda_stream
 
+    # each call enqueues on the stream current at call time (the capture stream under --graph)
     def fwd(stage):
-        st = ta.tri_attn_fwd_stages(stage, B, N, H, D, q, k, v, bias, mask, o, lse, res, fws, fws.numel(), sh)
+        st = ta.tri_attn_fwd_stages(stage, B, N, H, D, q, k, v, bias, mask, o, lse, res, fws, fws.numel(),
+                                    torch.cuda.current_stream().cuda_stream)
         if st:
             raise ta.TriAttnError(st, "tri_attn_fwd_stages")
 
     def bwd(stage):
         st = ta.tri_attn_bwd_stages(stage, B, N, H, D, q, k, v, bias, mask, o, lse, res, dO, dq, dk, dv, dbias,
-                                    bws, bws.numel(), sh)
+                                    bws, bws.numel(), torch.cuda.current_stream().cuda_stream)
         if st:
             raise ta.TriAttnError(st, "tri_attn_bwd_stages")
 
@@ -166,6 +169,34 @@ def main():
                 "kernel": "bwd_kernel (key-tile-parallel backward: S, dP, dV, dK, dQ products)",
                 "per_launch_flop": w.flops_bwd, "avg_launch_ms": round(bwd_main_ms, 4)}
 
+    graph = None
+    if args.graph:
+        # the same five calls captured once and replayed; no memset nodes are involved (the
+        # kernels write every byte they later read)
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            for c in calls:
+                c()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for c in calls:
+                c()
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        g_ms = e0.elapsed_time(e1) / args.steps
+        graph = {"ms_per_step": round(g_ms, 4), "value": round(flops / (g_ms * 1e-3) / 1e12, 2),
+                 "unit": "TFLOP/s", "eager_ms_per_step": round(ms_per_step, 4)}
+
     cpu = None
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(w, inp, args.cpu_seconds)
@@ -182,6 +213,8 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    if graph is not None:
+        out["graph"] = graph
     print(json.dumps(out), flush=True)
 
 

@@ -1,0 +1,82 @@
+"""Forward + backward captured in one HIP graph (the small-N latency path).
+
+The library makes only kernel launches on the caller's stream (no allocation, no memset, no
+host synchronisation), so a caller can capture a whole step and replay it.  Each replay must
+reproduce the eager results bit for bit; eager work and synchronisation run between the
+replays, as a capturing caller would interleave them.
+"""
+import numpy as np
+import pytest
+import torch
+
+from tri_synth import WORKLOADS, make_inputs, workload_inputs
+
+from ._util import mask_dev, to_dev
+
+pytestmark = pytest.mark.gpu
+
+OUTS = ("o", "lse", "res", "dq", "dk", "dv", "dbias")
+
+
+def _bits(t: torch.Tensor) -> torch.Tensor:
+    return t.view(torch.int32) if t.dtype == torch.float32 else t.view(torch.int16)
+
+
+def _check_graph_replays(inp):
+    import triangle_attention_amd as ta
+    q, k, v, bias, dO = (to_dev(inp[n]) for n in ("q", "k", "v", "bias", "dO"))
+    m = mask_dev(inp["key_mask"])
+    B, N, H, _, D = q.shape
+    dev = q.device
+    out = dict(o=torch.empty_like(q), res=torch.empty_like(q),
+               lse=torch.empty((B, N, H, N), dtype=torch.float32, device=dev),
+               dq=torch.empty_like(q), dk=torch.empty_like(q), dv=torch.empty_like(q),
+               dbias=torch.empty((B, H, N, N), dtype=torch.float32, device=dev))
+    fws = torch.empty(ta.tri_attn_fwd_workspace_bytes(B, N, H, D), dtype=torch.uint8, device=dev)
+    bws = torch.empty(ta.tri_attn_bwd_workspace_bytes(B, N, H, D), dtype=torch.uint8, device=dev)
+
+    def step():
+        sh = torch.cuda.current_stream().cuda_stream
+        st = ta.tri_attn_fwd(B, N, H, D, q, k, v, bias, m, out["o"], out["lse"], out["res"], fws, fws.numel(), sh)
+        assert st == 0, st
+        st = ta.tri_attn_bwd(B, N, H, D, q, k, v, bias, m, out["o"], out["lse"], out["res"], dO, out["dq"],
+                             out["dk"], out["dv"], out["dbias"], bws, bws.numel(), sh)
+        assert st == 0, st
+
+    step()
+    torch.cuda.synchronize()
+    ref = {n: out[n].clone() for n in OUTS}
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+
+    scratch = torch.zeros(1 << 20, device=dev)
+    for rep in range(3):
+        for n in OUTS:  # poison the outputs so that a replay that skips a write shows up
+            out[n].view(torch.uint8).fill_(0x7F)
+        g.replay()
+        scratch.add_(1.0)  # eager work between replays
+        torch.cuda.synchronize()
+        for n in OUTS:
+            assert torch.equal(_bits(out[n]), _bits(ref[n])), (rep, n)
+
+
+def test_graph_replay_small():
+    # the launch-bound workload the graph path is for
+    _check_graph_replays(workload_inputs(WORKLOADS["n64_h4_d16"]))
+
+
+def test_graph_replay_masked_ragged():
+    inp = make_inputs(1, 200, 2, 32, seed=77, bias_std=2.0)
+    rng = np.random.default_rng(78)
+    msk = (rng.random((1, 200, 200)) > 0.3).astype(np.uint8)
+    msk[:, :, 5] = 1
+    inp["key_mask"] = msk
+    _check_graph_replays(inp)
