@@ -37,8 +37,8 @@ KERNEL_SRC = os.path.join(ROOT, "triangle_attention_amd", "csrc", "tri_attn.hip"
 def _parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=40)
+    ap.add_argument("--warmup", type=int, default=30, help="untimed steps; the GPU needs about 30 to reach its steady clock")
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--no-residual", action="store_true", help="uncompensated backward correction")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle CPU-baseline budget (0 = skip)")
