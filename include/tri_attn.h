@@ -53,8 +53,11 @@ extern "C" {
 
 typedef enum {
   TRI_ATTN_SUCCESS = 0,
-  TRI_ATTN_ERROR_INVALID_VALUE = 1, /* NULL required pointer, B/N/H < 1, or output overlapping an input */
-  TRI_ATTN_ERROR_UNSUPPORTED = 2,   /* D not in {16, 32}, or N > TRI_ATTN_MAX_N */
+  TRI_ATTN_ERROR_INVALID_VALUE = 1, /* NULL required pointer, B/N/H < 1, output overlapping an input,
+                                       unknown stage bits or layout */
+  TRI_ATTN_ERROR_UNSUPPORTED = 2,   /* D not in {16, 32}, N > TRI_ATTN_MAX_N, B > 2^20, H > 4096,
+                                       B*N*H*ceil(N/128)*8 > 2^31 - 1, or a layout whose slice
+                                       span exceeds 32-bit offsets */
   TRI_ATTN_ERROR_MISALIGNED = 3,    /* a tensor pointer that is not 16-byte aligned */
   TRI_ATTN_ERROR_WORKSPACE = 4,     /* workspace NULL or smaller than *_workspace_bytes() */
   TRI_ATTN_ERROR_LAUNCH = 5         /* the HIP runtime rejected a kernel launch */
@@ -132,6 +135,54 @@ tri_attn_status tri_attn_bwd_stages(unsigned stages, int64_t B, int64_t N, int64
                                     const void *dO,
                                     void *dq, void *dk, void *dv, float *dbias,
                                     void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Token-tensor layouts: where entry (b, slice i, head h, token j, channel c) of q, k, v, o,
+ * residual, dO, dq, dk and dv lives.  All nine tensors of a call share one layout; each is
+ * still one dense, 16-byte aligned block of B*N*N*H*D bf16 values.
+ *
+ *   TRI_ATTN_LAYOUT_SLICE_HEAD  [B, N, H, N, D], index [b, i, h, j, c] (the layout above)
+ *   TRI_ATTN_LAYOUT_PAIR_START  [B, N, N, H, D], index [b, i, j, h, c]: the pair layout, heads
+ *                               innermost, attending along the second pair index (starting node)
+ *   TRI_ATTN_LAYOUT_PAIR_END    [B, N, N, H, D], index [b, j, i, h, c]: the same pair layout,
+ *                               attending along the first pair index with the second one fixed
+ *                               (ending node), with no transposed copy
+ *
+ * AlphaFold3-style Pairformers, the models TurboPairFormer's kernel serves (Abstract), run
+ * triangle attention around both the starting and the ending node; the ending-node form is
+ * the starting-node form applied to the transposed pair representation.  Only addressing
+ * changes with the layout: bias, dbias, key_mask and lse keep their layouts, indexed by slice
+ * and by the tokens along the attended axis, so the ending-node caller passes the pair bias
+ * and key mask for that orientation (N*N values per batch, not N*N*N).  For the same values in
+ * either layout every output is bitwise identical.
+ */
+typedef enum {
+  TRI_ATTN_LAYOUT_SLICE_HEAD = 0,
+  TRI_ATTN_LAYOUT_PAIR_START = 1,
+  TRI_ATTN_LAYOUT_PAIR_END = 2
+} tri_attn_layout;
+
+/*
+ * Staged calls with an explicit token layout (an int holding a tri_attn_layout value);
+ * tri_attn_fwd_stages / tri_attn_bwd_stages are these with TRI_ATTN_LAYOUT_SLICE_HEAD.
+ * Errors beyond those of the staged calls: TRI_ATTN_ERROR_INVALID_VALUE for an unknown
+ * layout; TRI_ATTN_ERROR_UNSUPPORTED when a slice's rows, padded to a multiple of 128 tokens,
+ * span more than 2^31 - 1 bytes (PAIR_END with N*N*H*D*2 near 2 GiB; the kernels address a
+ * slice with 32-bit offsets).
+ */
+tri_attn_status tri_attn_fwd_ex(unsigned stages, int layout, int64_t B, int64_t N, int64_t H, int64_t D,
+                                const void *q, const void *k, const void *v, const void *bias,
+                                const uint8_t *key_mask,
+                                void *o, float *lse, void *residual,
+                                void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+tri_attn_status tri_attn_bwd_ex(unsigned stages, int layout, int64_t B, int64_t N, int64_t H, int64_t D,
+                                const void *q, const void *k, const void *v, const void *bias,
+                                const uint8_t *key_mask,
+                                const void *o, const float *lse, const void *residual,
+                                const void *dO,
+                                void *dq, void *dk, void *dv, float *dbias,
+                                void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

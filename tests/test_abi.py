@@ -123,3 +123,32 @@ def test_bwd_validation(lib):
     assert _bwd(ptrs=p) == MISALIGNED
     assert _bwd(wsb=ta.tri_attn_bwd_workspace_bytes(1, 64, 4, 16) - 1) == WORKSPACE
     assert _bwd(ws=0) == WORKSPACE
+
+
+def _fwd_ex(layout, shape=(1, 64, 4, 16), stages=7, wsb=None):
+    q, k, v, bias, o, lse, r, w = _ptrs(8)
+    wsb = ta.tri_attn_fwd_workspace_bytes(*shape) if wsb is None else wsb
+    return ta.tri_attn_fwd_ex(stages, layout, *shape, q, k, v, bias, None, o, lse, r, w, wsb, 0)
+
+
+def _bwd_ex(layout, shape=(1, 64, 4, 16), stages=7, wsb=None):
+    q, k, v, bias, o, lse, r, dO, dq, dk, dv, db, w = _ptrs(13)
+    wsb = ta.tri_attn_bwd_workspace_bytes(*shape) if wsb is None else wsb
+    return ta.tri_attn_bwd_ex(stages, layout, *shape, q, k, v, bias, None, o, lse, r, dO, dq, dk, dv, db, w, wsb, 0)
+
+
+def test_layout_validation(lib):
+    assert ta.LAYOUTS == {"slice_head": 0, "pair_start": 1, "pair_end": 2}
+    for f in (_fwd_ex, _bwd_ex):
+        for bad in (-1, 3, 1 << 20):
+            assert f(bad) == INVALID, (f, bad)
+        assert f(0, stages=8) == INVALID
+        # every known layout passes validation up to the (too small) workspace
+        for layout in ta.LAYOUTS.values():
+            assert f(layout, wsb=16) == WORKSPACE, (f, layout)
+        # the ending-node layout at N=768: a slice's rows span N*H*D*2 bytes each, 32-bit offsets
+        # reach H=32 (768 padded rows x 768*32*32*2 bytes < 2^31) but not H=64
+        assert f(2, shape=(1, 768, 32, 32), wsb=16) == WORKSPACE
+        assert f(2, shape=(1, 768, 64, 32)) == UNSUPPORTED
+        assert f(1, shape=(1, 768, 64, 32), wsb=16) == WORKSPACE  # pair_start rows are H*D apart
+        assert f(0, shape=(1, 768, 64, 32), wsb=16) == WORKSPACE

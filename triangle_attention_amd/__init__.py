@@ -20,7 +20,7 @@ from ._build import LIB_PATH, build  # noqa: F401
 __all__ = [
     "TriAttnError", "load_library", "tri_attn_status_string", "tri_attn_fwd_workspace_bytes",
     "tri_attn_bwd_workspace_bytes", "tri_attn_fwd", "tri_attn_bwd", "tri_attn_fwd_stages", "tri_attn_bwd_stages",
-    "triangle_attention", "TRI_ATTN_MAX_N",
+    "tri_attn_fwd_ex", "tri_attn_bwd_ex", "triangle_attention", "TRI_ATTN_MAX_N", "LAYOUTS",
 ]
 
 TRI_ATTN_MAX_N = 768
@@ -56,6 +56,10 @@ def load_library(path: str = LIB_PATH):
     lib.tri_attn_fwd_stages.restype = ctypes.c_int
     lib.tri_attn_bwd_stages.argtypes = [ctypes.c_uint] + lib.tri_attn_bwd.argtypes
     lib.tri_attn_bwd_stages.restype = ctypes.c_int
+    lib.tri_attn_fwd_ex.argtypes = [ctypes.c_uint, ctypes.c_int] + lib.tri_attn_fwd.argtypes
+    lib.tri_attn_fwd_ex.restype = ctypes.c_int
+    lib.tri_attn_bwd_ex.argtypes = [ctypes.c_uint, ctypes.c_int] + lib.tri_attn_bwd.argtypes
+    lib.tri_attn_bwd_ex.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -121,17 +125,41 @@ def tri_attn_bwd_stages(stages, B, N, H, D, q, k, v, bias, key_mask, o, lse, res
                                                   int(workspace_bytes), _stream(stream)))
 
 
+# token-tensor layouts of tri_attn_fwd_ex / tri_attn_bwd_ex (tri_attn_layout)
+LAYOUTS = {"slice_head": 0, "pair_start": 1, "pair_end": 2}
+
+
+def tri_attn_fwd_ex(stages, layout, B, N, H, D, q, k, v, bias, key_mask, o, lse, residual, workspace,
+                    workspace_bytes, stream=None) -> int:
+    return int(load_library().tri_attn_fwd_ex(stages, layout, B, N, H, D, _ptr(q), _ptr(k), _ptr(v), _ptr(bias),
+                                              _ptr(key_mask), _ptr(o), _ptr(lse), _ptr(residual),
+                                              _ptr(workspace), int(workspace_bytes), _stream(stream)))
+
+
+def tri_attn_bwd_ex(stages, layout, B, N, H, D, q, k, v, bias, key_mask, o, lse, residual, dO, dq, dk, dv, dbias,
+                    workspace, workspace_bytes, stream=None) -> int:
+    return int(load_library().tri_attn_bwd_ex(stages, layout, B, N, H, D, _ptr(q), _ptr(k), _ptr(v), _ptr(bias),
+                                              _ptr(key_mask), _ptr(o), _ptr(lse), _ptr(residual), _ptr(dO),
+                                              _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbias), _ptr(workspace),
+                                              int(workspace_bytes), _stream(stream)))
+
+
 def _check(status: int, where: str):
     if status != 0:
         raise TriAttnError(status, where)
 
 
-def _shape(q):
+def _shape(q, layout="slice_head"):
+    if layout not in LAYOUTS:
+        raise ValueError(f"layout must be one of {sorted(LAYOUTS)}")
     if q.dim() != 5:
-        raise ValueError("q must be [B, N, H, N, D]")
-    B, N, H, N2, D = q.shape
+        raise ValueError("q must have 5 dimensions")
+    if layout == "slice_head":
+        B, N, H, N2, D = q.shape
+    else:
+        B, N, N2, H, D = q.shape
     if N2 != N:
-        raise ValueError("q must be [B, N, H, N, D] with equal slice and token extents")
+        raise ValueError("q must have equal slice and token extents")
     return B, N, H, D
 
 
@@ -139,47 +167,56 @@ def _workspace(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
 
 
-def forward(q, k, v, bias, key_mask=None, residual_compensation=True):
-    """Returns (o, lse, residual-or-None).  Tensors must be contiguous bf16 (mask uint8) on one GPU."""
-    B, N, H, D = _shape(q)
+def forward(q, k, v, bias, key_mask=None, residual_compensation=True, layout="slice_head"):
+    """Returns (o, lse, residual-or-None).  Tensors must be contiguous bf16 (mask uint8) on one GPU;
+    q, k, v (and o, residual) are laid out as `layout` names (see triangle_attention)."""
+    B, N, H, D = _shape(q, layout)
     o = torch.empty_like(q)
     lse = torch.empty((B, N, H, N), dtype=torch.float32, device=q.device)
     res = torch.empty_like(q) if residual_compensation else None
     nws = tri_attn_fwd_workspace_bytes(B, N, H, D)
     ws = _workspace(nws, q.device)
-    _check(tri_attn_fwd(B, N, H, D, q, k, v, bias, key_mask, o, lse, res, ws, ws.numel()), "tri_attn_fwd")
+    _check(tri_attn_fwd_ex(STAGE_ALL, LAYOUTS[layout], B, N, H, D, q, k, v, bias, key_mask, o, lse, res, ws,
+                           ws.numel()), "tri_attn_fwd_ex")
     return o, lse, res
 
 
-def backward(q, k, v, bias, key_mask, o, lse, residual, dO):
+def backward(q, k, v, bias, key_mask, o, lse, residual, dO, layout="slice_head"):
     """Returns (dq, dk, dv, dbias) with dbias in float32."""
-    B, N, H, D = _shape(q)
+    B, N, H, D = _shape(q, layout)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     dbias = torch.empty((B, H, N, N), dtype=torch.float32, device=q.device)
     nws = tri_attn_bwd_workspace_bytes(B, N, H, D)
     ws = _workspace(nws, q.device)
-    _check(tri_attn_bwd(B, N, H, D, q, k, v, bias, key_mask, o, lse, residual, dO, dq, dk, dv, dbias, ws,
-                        ws.numel()), "tri_attn_bwd")
+    _check(tri_attn_bwd_ex(STAGE_ALL, LAYOUTS[layout], B, N, H, D, q, k, v, bias, key_mask, o, lse, residual, dO,
+                           dq, dk, dv, dbias, ws, ws.numel()), "tri_attn_bwd_ex")
     return dq, dk, dv, dbias
 
 
 class _TriAttnFn(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, q, k, v, bias, key_mask, residual_compensation):
-        o, lse, res = forward(q, k, v, bias, key_mask, residual_compensation)
+    def forward(ctx, q, k, v, bias, key_mask, residual_compensation, layout):
+        o, lse, res = forward(q, k, v, bias, key_mask, residual_compensation, layout)
         ctx.save_for_backward(q, k, v, bias, o, lse, res, key_mask)
+        ctx.layout = layout
         return o
 
     @staticmethod
     def backward(ctx, dO):
         q, k, v, bias, o, lse, res, key_mask = ctx.saved_tensors
-        dq, dk, dv, dbias = backward(q, k, v, bias, key_mask, o, lse, res, dO.contiguous())
-        return dq, dk, dv, dbias.to(bias.dtype), None, None
+        dq, dk, dv, dbias = backward(q, k, v, bias, key_mask, o, lse, res, dO.contiguous(), ctx.layout)
+        return dq, dk, dv, dbias.to(bias.dtype), None, None, None
 
 
-def triangle_attention(q, k, v, bias, key_mask=None, residual_compensation=True):
-    """Starting-node triangle attention, differentiable in q, k, v and the shared bias.
+def triangle_attention(q, k, v, bias, key_mask=None, residual_compensation=True, layout="slice_head"):
+    """Triangle attention, differentiable in q, k, v and the shared bias.
 
-    q, k, v: bf16 [B, N, H, N, D]; bias: bf16 [B, H, N, N]; key_mask: uint8 [B, N, N] or None.
+    layout "slice_head": q, k, v bf16 [B, N, H, N, D], index [b, i, h, j, c] (starting node).
+    layout "pair_start": q, k, v bf16 [B, N, N, H, D] (the pair layout), index [b, i, j, h, c]:
+        attention along the second pair index (starting node).
+    layout "pair_end": the same pair layout, index [b, j, i, h, c]: attention along the first
+        pair index for each fixed second index (ending node), with no transposed copy.
+    bias: bf16 [B, H, N, N] indexed [b, h, query, key] and key_mask: uint8 [B, N, N] indexed
+    [b, slice, key], in the orientation of the attended axis, or None.
     """
-    return _TriAttnFn.apply(q, k, v, bias, key_mask, residual_compensation)
+    return _TriAttnFn.apply(q, k, v, bias, key_mask, residual_compensation, layout)

@@ -46,6 +46,26 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kMaskNeg = -1e9f;  // additive score term of a masked key
 constexpr int kXcd = 8;            // XCDs per MI355X; dispatch is round-robin over them
 
+// Element offsets of the token tensors (q, k, v, o, residual, dO, dq, dk, dv): entry
+// (b, i, h, j, c) of slice i, head h, token j, channel c sits at b*sB + i*sI + h*sH + j*sT + c.
+// Channels are contiguous; a token row is D elements.
+struct TokLayout {
+  int64_t sB, sI, sH;
+  int sT;
+  __device__ __forceinline__ int64_t slice(int b, int i, int h) const {
+    return (int64_t)b * sB + (int64_t)i * sI + (int64_t)h * sH;
+  }
+  // bytes spanned by the N token rows of one slice-head (what a buffer descriptor covers)
+  __device__ __forceinline__ int span_bytes(int N, int D) const { return ((N - 1) * sT + D) * 2; }
+};
+// The kernels take a STRIDED flag: without it they use the slice-major layout [B, N, H, N, D]
+// built here from the shape, so that its strides are compile-time multiples of D.
+template <bool STRIDED, int D>
+__device__ __forceinline__ TokLayout tok_layout(const TokLayout& given, int N, int H) {
+  if (STRIDED) return given;
+  return TokLayout{(int64_t)N * H * N * D, (int64_t)H * N * D, (int64_t)N * D, D};
+}
+
 // ------------------------------------------------------------------ small helpers
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -177,7 +197,9 @@ __device__ __forceinline__ void dma16(const void* g, void* lds_wave_base) {
 }
 
 // Raw buffer resource over [base, base + bytes): loads past the end return zeros, which is how
-// rows beyond N are read below.  (Only loads go through buffer resources: the compiler's
+// rows beyond N are read below.  The range check applies to the per-lane and the scalar
+// offset together (a load at voffset + soffset >= bytes returns zeros; measured on gfx950 with
+// every address inside the allocation), so row offsets may go into either.  (Only loads go through buffer resources: the compiler's
 // wait-state rule for the store-data hazard of wide buffer stores does not cover the form
 // with a register scalar offset on gfx950, where such stores were seen to write
 // overwritten data.  Global stores get the wait states.)
@@ -249,6 +271,15 @@ __device__ __forceinline__ bf16x8 ld_nt(const bf16x8* p) {
   return __builtin_bit_cast(bf16x8, __builtin_nontemporal_load((const u32x4v*)p));
 }
 
+// This lane's index in its wave, from a statement the compiler cannot move: a per-lane offset
+// derived from it is recomputed where it is used instead of holding a register (or a spill
+// slot) across a loop.  (Plain vector instructions, no hazard with the matrix products.)
+__device__ __forceinline__ int lane_here() {
+  int r;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(r));
+  return r;
+}
+
 // Work-group barrier that orders LDS accesses only.  __syncthreads() also waits for every
 // outstanding global access of the wave (its release fence covers the direct-to-LDS loads),
 // which would expose the latency of a prefetch issued just before it.
@@ -286,12 +317,13 @@ __device__ __forceinline__ int tr_off(int lane, int r0, int c0) {
 // by the work-group) and each wave's two bias tiles stream into the other half of
 // double-buffered LDS (buffer loads to LDS); keys past N read as zeros and carry a -inf
 // bias.  K and V rows are XOR-swizzled like the backward's.
-template <int D, bool MASK>
+template <int D, bool MASK, bool STRIDED>
 __global__ __launch_bounds__(256, 5)
 void fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
                 const float* __restrict__ biasF, const uint8_t* __restrict__ mask,
                 bf16* __restrict__ o, float* __restrict__ lse, bf16* __restrict__ res,
-                int B, int N, int H, float alpha) {
+                int B, int N, int H, float alpha, TokLayout Lg) {
+  const TokLayout L = tok_layout<STRIDED, D>(Lg, N, H);
   constexpr int KT = 64;        // keys per iteration
   constexpr int NC = D / 16;    // 16-wide channel chunks
   constexpr int CPR = D / 8;    // 16-byte chunks per row
@@ -310,7 +342,8 @@ void fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   const int b = (int)(rest / H);
 
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, g = l >> 5, ln = l & 31;
-  const int64_t sbase = (((int64_t)b * N + i) * H + h) * (int64_t)N * D;
+  const int64_t sbase = L.slice(b, i, h);
+  const int sT = L.sT;
   const int j = qt * 128 + w * 32 + ln;  // this lane's query
   const bool jok = j < N;
   const int Kp = (int)round_up(N, 64), Jp = (int)round_up(N, 128);
@@ -320,19 +353,19 @@ void fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   const uint8_t* mrow = MASK ? mask + ((int64_t)b * N + i) * N : nullptr;
 
   // streamed loads: K and V rows (lane -> swizzled 16-byte chunk), this wave's bias tiles
-  const __amdgpu_buffer_rsrc_t rk = buf_rsrc(k + sbase, N * D * 2), rv = buf_rsrc(v + sbase, N * D * 2);
-  const unsigned kv_vo = (unsigned)(((tid / CPR) * D + ((tid % CPR) ^ swz<D>(tid / CPR)) * 8) * 2);
+  const __amdgpu_buffer_rsrc_t rk = buf_rsrc(k + sbase, L.span_bytes(N, D)), rv = buf_rsrc(v + sbase, L.span_bytes(N, D));
+  const unsigned kv_vo = (unsigned)(((tid / CPR) * sT + ((tid % CPR) ^ swz<D>(tid / CPR)) * 8) * 2);
   auto prefetch = [&](int kt, int buf) {
     if (w < KT * CPR / 64) {
-      dma16b(rk, kv_vo, kt * KT * D * 2, &Ks_[buf][w * 512]);
-      dma16b(rv, kv_vo, kt * KT * D * 2, &Vs_[buf][w * 512]);
+      dma16b(rk, kv_vo, kt * KT * sT * 2, &Ks_[buf][w * 512]);
+      dma16b(rv, kv_vo, kt * KT * sT * 2, &Vs_[buf][w * 512]);
     }
   };
 
   bf16x8 qf[NC];
 #pragma unroll
   for (int cc = 0; cc < NC; cc++)
-    qf[cc] = jok ? *(const bf16x8*)(q + sbase + (int64_t)j * D + cc * 16 + g * 8) : zero8();
+    qf[cc] = jok ? *(const bf16x8*)(q + sbase + (int64_t)j * sT + cc * 16 + g * 8) : zero8();
 
   f32x16 acc_o = {};
   float m_run = -INFINITY, l_run = 0.0f;
@@ -432,8 +465,8 @@ void fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = 1.0f / l_tot;
   if (jok) {
-    bf16* orow = o + sbase + (int64_t)j * D;
-    bf16* rrow = res ? res + sbase + (int64_t)j * D : nullptr;
+    bf16* orow = o + sbase + (int64_t)j * sT;
+    bf16* rrow = res ? res + sbase + (int64_t)j * sT : nullptr;
 #pragma unroll
     for (int R = 0; R < D / 8; R++) {
       bf16x4 ob, rb;
@@ -458,20 +491,23 @@ void fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
 // -lse2 then 128 of -D (zero padding past N): one KiB per step, the block the main kernel
 // streams into LDS with one load per lane.  D/8 adjacent lanes share a row (16 bytes
 // each, so a wave reads contiguous memory); their partial sums combine in a fixed order.
-template <int D>
+template <int D, bool STRIDED>
 __global__ __launch_bounds__(256)
 void bwd_pre_kernel(const bf16* __restrict__ dO, const bf16* __restrict__ o, const bf16* __restrict__ res,
-                    const float* __restrict__ lse, float* __restrict__ LDp, int N, int Jp, int64_t nrows) {
+                    const float* __restrict__ lse, float* __restrict__ LDp, int N, int H, int Jp, TokLayout Lg) {
+  const TokLayout L = tok_layout<STRIDED, D>(Lg, N, H);
   constexpr int LPR = D / 8;  // lanes per row
-  // the grid covers nrows * Jp * LPR threads exactly (Jp * LPR is a multiple of 256)
-  const int64_t gt = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t prow = gt / LPR;  // padded row index
-  const int part = (int)(gt % LPR);
-  const int64_t row = prow / Jp;
-  const int j = (int)(prow % Jp);
+  // The grid covers the B*N*H slice-head rows, Jp * LPR threads each (a multiple of 256), so
+  // each work-group lies within one row: the row and its slice are work-group uniform.
+  const unsigned bpr = (unsigned)(Jp * LPR / 256);
+  const unsigned row = blockIdx.x / bpr;  // (b*N + i)*H + h
+  const int local = (int)(blockIdx.x % bpr) * 256 + (int)threadIdx.x;
+  const int j = local / LPR, part = local % LPR;
   float acc = 0.0f;
   if (j < N) {
-    const int64_t off = (row * N + j) * D + part * 8;
+    const unsigned bi = row / (unsigned)H;
+    const int64_t off = L.slice((int)(bi / (unsigned)N), (int)(bi % (unsigned)N), (int)(row % (unsigned)H)) +
+                        (int64_t)j * L.sT + part * 8;
     const bf16x8 a = *(const bf16x8*)(dO + off);
     const bf16x8 ov = ld_nt((const bf16x8*)(o + off));
     if (res) {
@@ -486,8 +522,8 @@ void bwd_pre_kernel(const bf16* __restrict__ dO, const bf16* __restrict__ o, con
   acc += __shfl_xor(acc, 1);
   if (LPR == 4) acc += __shfl_xor(acc, 2);
   if (part == 0) {
-    float* dst = LDp + row * 2 * Jp + (j >> 7) * 256 + (j & 127);
-    dst[0] = j < N ? -lse[row * N + j] * kLog2e : 0.0f;
+    float* dst = LDp + (int64_t)row * 2 * Jp + (j >> 7) * 256 + (j & 127);
+    dst[0] = j < N ? -lse[(int64_t)row * N + j] * kLog2e : 0.0f;
     dst[128] = -acc;
   }
 }
@@ -542,12 +578,13 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
   }
 }
 
-template <int D, bool MASK, int NS>
+template <int D, bool MASK, int NS, bool STRIDED>
 __global__ __launch_bounds__(512, 1)
 void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
                 const bf16* __restrict__ dO, const bf16* __restrict__ biasB, const uint8_t* __restrict__ mask,
                 const float* __restrict__ LDp, unsigned* __restrict__ dqp, float* __restrict__ dbp, bf16* __restrict__ dk, bf16* __restrict__ dv,
-                int B, int N, int H, int G, int ngroups, float alpha) {
+                int B, int N, int H, int G, int ngroups, float alpha, TokLayout Lg) {
+  const TokLayout L = tok_layout<STRIDED, D>(Lg, N, H);
   constexpr int NC = D / 16;
   constexpr int CPR = D / 8;    // 16-byte chunks per row
   constexpr int LDT = 128 + 8;  // dS^T row stride (elements), padded
@@ -588,16 +625,15 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   constexpr int nsteps = NS;
   constexpr int Jp = NS * 128;
   const float c1 = alpha * kLog2e;
-  const int64_t slice_elems = (int64_t)N * D;
+  const int sT = L.sT;
+  const int span = L.span_bytes(N, D);                                   // bytes of a slice-head's rows
   constexpr int nqt = Jp / 16;                                           // 16-query tiles per slice
   const int64_t dq_kb_stride = (int64_t)B * N * H * nqt * (16 * D * 2);  // bytes of one key block's partials
   const int nitems = (i_end - i_begin) * nsteps;
 
-  // Per-lane byte offsets of the streamed loads, fixed for the whole work-group; slice and
-  // step enter through the buffer base and the scalar offset.  Q, dO, K and V land swizzled.
-  const unsigned qd_vo = (unsigned)(((tid / CPR) * D + ((tid % CPR) ^ swz<D>(tid / CPR)) * 8) * 2);
-  const int kv_t = tid & 255;  // K (waves 0-3) / V (waves 4-7)
-  const unsigned kv_vo = (unsigned)(((kb * 64 + kv_t / CPR) * D + ((kv_t % CPR) ^ swz<D>(kv_t / CPR)) * 8) * 2);
+  // Per-lane byte offset of the streamed Q and dO loads, fixed for the whole work-group; slice
+  // and step enter through the buffer base and the scalar offset.  Q, dO, K and V land swizzled.
+  const unsigned qd_vo = (unsigned)(((tid / CPR) * sT + ((tid % CPR) ^ swz<D>(tid / CPR)) * 8) * 2);
   const bf16* bias_blk = biasB + ((int64_t)(b * H + h) * KB + kb) * (int64_t)nsteps * 8192;
 
   // Per-lane LDS byte offsets of the operand reads; the buffer and the step enter as uniform
@@ -632,14 +668,14 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   // slice-head row returns zeros for rows past N)
   const unsigned lds0 = __builtin_amdgcn_readfirstlane(lds_addr(lds));
   const i32x4 rbias = raw_rsrc(bias_blk, nsteps * 16384);  // this work-group's pair-bias column
-  // per slice-head row: the base addresses of its Q, dO and row-statistics rows (the
-  // descriptors' other words are fixed)
+  // per slice-head row: the descriptors of its Q, dO and row-statistics rows
   struct RowRes { i32x4 q, dO, ld; };
   auto row_res = [&](int ii) {
     const int64_t sl = ((int64_t)b * N + ii) * H + h;  // slice-head row index
     RowRes r;
-    r.q = raw_rsrc(q + sl * slice_elems, N * D * 2);
-    r.dO = raw_rsrc(dO + sl * slice_elems, N * D * 2);
+    const int64_t tb = L.slice(b, ii, h);
+    r.q = raw_rsrc(q + tb, span);
+    r.dO = raw_rsrc(dO + tb, span);
     r.ld = raw_rsrc(LDp + sl * 2 * Jp, Jp * 8);
     return r;
   };
@@ -647,8 +683,8 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   auto prefetch = [&](const RowRes& rr, int ss, int buf) {
     static_assert(2 * CPR <= 8, "Q/dO rows of a step in one load per wave");
     if (w < 2 * CPR) {
-      dma16_asm(rr.q, qd_vo, ss * 128 * D * 2, lds0 + oQD + buf * kQDB + w * 1024);
-      dma16_asm(rr.dO, qd_vo, ss * 128 * D * 2, lds0 + oQD + buf * kQDB + 128 * D * 2 + w * 1024);
+      dma16_asm(rr.q, qd_vo, ss * 128 * sT * 2, lds0 + oQD + buf * kQDB + w * 1024);
+      dma16_asm(rr.dO, qd_vo, ss * 128 * sT * 2, lds0 + oQD + buf * kQDB + 128 * D * 2 + w * 1024);
     }
     if (w == 0) dma16_asm(rr.ld, (unsigned)l * 16u, ss * 1024, lds0 + oLD + buf * kLDB);
     // this step's pair-bias tiles: 16 KiB, 2 KiB per wave
@@ -658,13 +694,16 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   // K, V and the key-mask bytes of slice ii into K/V buffer kvb
   auto prefetch_kv = [&](int ii, int kvb) {
     constexpr int KC = 64 * CPR;  // 16-byte chunks per block
-    const int64_t sl = ((int64_t)b * N + ii) * H + h;
+    const int64_t tb = L.slice(b, ii, h);
     const unsigned dst = lds0 + oKV + kvb * kKVB;
-    if (w < KC / 64) dma16_asm(raw_rsrc(k + sl * slice_elems, N * D * 2), kv_vo, 0, dst + w * 1024);
+    const int kv_t = (w & 3) * 64 + lane_here();  // K (waves 0-3) / V (waves 4-7); recomputed per slice
+    const unsigned kv_vo = (unsigned)(((kb * 64 + kv_t / CPR) * sT + ((kv_t % CPR) ^ swz<D>(kv_t / CPR)) * 8) * 2);
+    if (w < KC / 64) dma16_asm(raw_rsrc(k + tb, span), kv_vo, 0, dst + w * 1024);
     else if (w >= 4 && w < 4 + KC / 64)
-      dma16_asm(raw_rsrc(v + sl * slice_elems, N * D * 2), kv_vo, 0, dst + 64 * D * 2 + (w - 4) * 1024);
+      dma16_asm(raw_rsrc(v + tb, span), kv_vo, 0, dst + 64 * D * 2 + (w - 4) * 1024);
     if (MASK && w == 7)  // one byte per lane, each landing in its own dword
-      dma1_asm(raw_rsrc(mask + ((int64_t)b * N + ii) * N, N), (unsigned)(kb * 64 + l), 0, dst + 2 * 64 * D * 2);
+      dma1_asm(raw_rsrc(mask + ((int64_t)b * N + ii) * N, N), (unsigned)(kb * 64 + lane_here()), 0,
+               dst + 2 * 64 * D * 2);
   };
 
   f32x16 face[NS];
@@ -708,9 +747,9 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
     // streaming stores: the partials are read back once, by the final reduction
     if (NC == 2) {
       const bf16x8 v8 = __builtin_shufflevector(pk[0], pk[NC - 1], 0, 1, 2, 3, 4, 5, 6, 7);
-      __builtin_nontemporal_store(__builtin_bit_cast(u32x4v, v8), (u32x4v*)(blk + l * 16));
+      __builtin_nontemporal_store(__builtin_bit_cast(u32x4v, v8), (u32x4v*)(blk + (unsigned)(l * 16)));
     } else {
-      __builtin_nontemporal_store(__builtin_bit_cast(u32x2v, pk[0]), (u32x2v*)(blk + l * 8));
+      __builtin_nontemporal_store(__builtin_bit_cast(u32x2v, pk[0]), (u32x2v*)(blk + (unsigned)(l * 8)));
     }
   };
 
@@ -728,7 +767,7 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   int cur_rt = 0;   // LDS buffer of item t (its parity)
   for (int i = i_begin; i < i_end; i++) {
     const int64_t sl_row = ((int64_t)b * N + i) * H + h;  // slice-head row index
-    const int64_t sbase = sl_row * slice_elems;
+    const int64_t sbase = L.slice(b, i, h);
     const int kvc = (i - i_begin) % 3;                     // K/V buffer of this slice
     const char* Ks = lds + oKV + kvc * kKVB;
     const char* Vs = Ks + 64 * D * 2;
@@ -901,10 +940,12 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
           ok4[e] = (bf16)((dkT[r] + red[slot2 + r * 64]) * alpha);
           ov4[e] = (bf16)(dvT[r] + red[slot2 + (NR + r) * 64]);
         }
-        if (kok) {
-          const int c = R * 8 + g * 4;
-          *(bf16x4*)(dk + sbase + (int64_t)kg * D + c) = ok4;
-          *(bf16x4*)(dv + sbase + (int64_t)kg * D + c) = ov4;
+        if (kok) {  // (the lane offset is recomputed here rather than kept across the slice loop)
+          const int lh = lane_here();
+          const unsigned lo = (unsigned)(((kh * 32 + (lh & 31)) * sT + R * 8 + (lh >> 5) * 4) * 2);
+          const int64_t rb = sbase + (int64_t)kb * 64 * sT;
+          *(bf16x4*)((char*)(dk + rb) + lo) = ok4;
+          *(bf16x4*)((char*)(dv + rb) + lo) = ov4;
         }
       }
     }
@@ -933,23 +974,24 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
 // lane) slot.  All loads of a thread are issued before the sum (indexes past the last partial
 // re-read it and are not added), so the kernel streams at memory speed instead of paying one
 // latency per term.
-template <int D>
+template <int D, bool STRIDED>
 __global__ __launch_bounds__(256)
-void reduce_dq_kernel(const unsigned* __restrict__ dqp, bf16* __restrict__ dq, int KB, int N, int nqt,
-                      int64_t nslots, float alpha) {
+void reduce_dq_kernel(const unsigned* __restrict__ dqp, bf16* __restrict__ dq, int KB, int N, int H, int nqt,
+                      int64_t nslots, float alpha, TokLayout Lg) {
+  const TokLayout L = tok_layout<STRIDED, D>(Lg, N, H);
   constexpr int NC = D / 16;
   constexpr int kMaxKB = TRI_ATTN_MAX_N / 64;
   constexpr int BLK = 16 * D * 2;  // bytes per block
   typedef typename std::conditional<NC == 2, bf16x8, bf16x4>::type V;
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= nslots) return;
-  const int64_t blk = t >> 6;
-  const int lane = (int)(t & 63);
-  const int64_t sl = blk / nqt;
-  const int row = (int)(blk % nqt) * 16 + (lane & 15);
+  // one wave per 16 x D block: the block, its slice and its rows are wave-uniform
+  const unsigned blk = __builtin_amdgcn_readfirstlane(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6));
+  if ((int64_t)blk * 64 >= nslots) return;
+  const int lane = (int)(threadIdx.x & 63);
+  const unsigned sl = blk / (unsigned)nqt;  // (b*N + i)*H + h
+  const int row = (int)(blk % (unsigned)nqt) * 16 + (lane & 15);
   if (row >= N) return;
   const int64_t kb_stride = nslots / 64 * BLK;
-  const char* base = (const char*)dqp + blk * BLK + lane * (int)sizeof(V);
+  const char* base = (const char*)dqp + (int64_t)blk * BLK + lane * (int)sizeof(V);
   V x[kMaxKB];
 #pragma unroll
   for (int kb = 0; kb < kMaxKB; kb++) x[kb] = __builtin_nontemporal_load((const V*)(base + min(kb, KB - 1) * kb_stride));
@@ -962,7 +1004,9 @@ void reduce_dq_kernel(const unsigned* __restrict__ dqp, bf16* __restrict__ dq, i
 #pragma unroll
       for (int e = 0; e < 4 * NC; e++) acc[e] += (float)x[kb][e];
     }
-  bf16* out = dq + (sl * N + row) * D + 4 * (lane >> 4);
+  const unsigned bi = sl / (unsigned)H;
+  bf16* out = dq + L.slice((int)(bi / (unsigned)N), (int)(bi % (unsigned)N), (int)(sl % (unsigned)H)) +
+              (int64_t)row * L.sT + 4 * (lane >> 4);
 #pragma unroll
   for (int u = 0; u < NC; u++) {
     bf16x4 r;
@@ -1010,9 +1054,10 @@ struct Plan {
 
 constexpr int64_t kAlign = 256;
 
+// (the last bound keeps every grid and the 16-query tile index of the dq reduction in 32 bits)
 bool shape_ok(int64_t B, int64_t N, int64_t H, int64_t D) {
   return B >= 1 && N >= 1 && H >= 1 && (D == 16 || D == 32) && N <= TRI_ATTN_MAX_N && B <= (1 << 20) &&
-         H <= (1 << 12);
+         H <= (1 << 12) && B * N * H * (round_up(N, 128) / 16) <= INT32_MAX;
 }
 
 Plan make_plan(int64_t B, int64_t N, int64_t H, int64_t D) {
@@ -1042,6 +1087,23 @@ Plan make_plan(int64_t B, int64_t N, int64_t H, int64_t D) {
 
 bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
+// Strides of the token tensors for each layout.  Only the addressing differs: every kernel
+// runs the same work in the same order, so a layout changes no result bit.
+bool make_layout(int layout, const Plan& P, TokLayout* L) {
+  const int64_t N = P.N, H = P.H, D = P.D;
+  switch (layout) {
+    case TRI_ATTN_LAYOUT_SLICE_HEAD: *L = {N * H * N * D, H * N * D, N * D, (int)D}; break;
+    case TRI_ATTN_LAYOUT_PAIR_START: *L = {N * N * H * D, N * H * D, D, (int)(H * D)}; break;
+    case TRI_ATTN_LAYOUT_PAIR_END: *L = {N * N * H * D, H * D, D, (int)(N * H * D)}; break;
+    default: return false;
+  }
+  return true;
+}
+
+// The buffer descriptors address a slice-head's rows with 32-bit offsets, including the
+// padded rows up to the next multiple of 128 (those read as zeros).
+bool layout_fits(const TokLayout& L, const Plan& P) { return (P.Jp * L.sT + P.D) * 2 <= INT32_MAX; }
+
 struct Range { const void* p; int64_t n; bool out; };
 
 bool overlaps(const Range* r, int n) {
@@ -1060,9 +1122,10 @@ bool overlaps(const Range* r, int n) {
 
 unsigned grid_xcd(int64_t ntiles) { return (unsigned)(round_up(ntiles, kXcd)); }
 
-template <int D>
-tri_attn_status launch_fwd(unsigned stages, const Plan& P, const void* q, const void* k, const void* v, const void* bias,
-                           const uint8_t* mask, void* o, float* lse, void* res, void* ws, hipStream_t st) {
+template <int D, bool STRIDED>
+tri_attn_status launch_fwd(unsigned stages, const Plan& P, const TokLayout& L, const void* q, const void* k,
+                           const void* v, const void* bias, const uint8_t* mask, void* o, float* lse, void* res,
+                           void* ws, hipStream_t st) {
   const float alpha = 1.0f / sqrtf((float)D);
   float* biasF = (float*)ws;
   const int64_t nb = P.B * P.H * P.Jp * P.Kp;
@@ -1072,20 +1135,21 @@ tri_attn_status launch_fwd(unsigned stages, const Plan& P, const void* q, const 
   const int64_t ntiles = P.B * P.H * P.N * ((P.N + 127) / 128);
   if (!(stages & TRI_ATTN_STAGE_MAIN)) {
   } else if (mask)
-    hipLaunchKernelGGL((fwd_kernel<D, true>), dim3(grid_xcd(ntiles)), dim3(256), 0, st, (const bf16*)q,
+    hipLaunchKernelGGL((fwd_kernel<D, true, STRIDED>), dim3(grid_xcd(ntiles)), dim3(256), 0, st, (const bf16*)q,
                        (const bf16*)k, (const bf16*)v, biasF, mask, (bf16*)o, lse, (bf16*)res, (int)P.B, (int)P.N,
-                       (int)P.H, alpha);
+                       (int)P.H, alpha, L);
   else
-    hipLaunchKernelGGL((fwd_kernel<D, false>), dim3(grid_xcd(ntiles)), dim3(256), 0, st, (const bf16*)q,
+    hipLaunchKernelGGL((fwd_kernel<D, false, STRIDED>), dim3(grid_xcd(ntiles)), dim3(256), 0, st, (const bf16*)q,
                        (const bf16*)k, (const bf16*)v, biasF, mask, (bf16*)o, lse, (bf16*)res, (int)P.B, (int)P.N,
-                       (int)P.H, alpha);
+                       (int)P.H, alpha, L);
   return hipGetLastError() == hipSuccess ? TRI_ATTN_SUCCESS : TRI_ATTN_ERROR_LAUNCH;
 }
 
-template <int D>
-tri_attn_status launch_bwd(unsigned stages, const Plan& P, const void* q, const void* k, const void* v, const void* bias,
-                           const uint8_t* mask, const void* o, const float* lse, const void* res, const void* dO,
-                           void* dq, void* dk, void* dv, float* dbias, void* ws, hipStream_t st) {
+template <int D, bool STRIDED>
+tri_attn_status launch_bwd(unsigned stages, const Plan& P, const TokLayout& L, const void* q, const void* k,
+                           const void* v, const void* bias, const uint8_t* mask, const void* o, const float* lse,
+                           const void* res, const void* dO, void* dq, void* dk, void* dv, float* dbias, void* ws,
+                           hipStream_t st) {
   const float alpha = 1.0f / sqrtf((float)D);
   char* base = (char*)ws;
   bf16* biasB = (bf16*)base;
@@ -1097,22 +1161,22 @@ tri_attn_status launch_bwd(unsigned stages, const Plan& P, const void* q, const 
     hipLaunchKernelGGL(bias_prep_bwd_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, st,
                        (const bf16*)bias, (_Float16*)biasB, (int)P.N, (int)P.KB, (int)(P.Jp / 128), nb);
     const int64_t nrows = P.B * P.N * P.H;
-    hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3((unsigned)(nrows * P.Jp * (D / 8) / 256)), dim3(256), 0, st,
-                       (const bf16*)dO, (const bf16*)o, (const bf16*)res, lse, LDg, (int)P.N, (int)P.Jp,
-                       nrows);
+    hipLaunchKernelGGL((bwd_pre_kernel<D, STRIDED>), dim3((unsigned)(nrows * P.Jp * (D / 8) / 256)), dim3(256), 0, st,
+                       (const bf16*)dO, (const bf16*)o, (const bf16*)res, lse, LDg, (int)P.N, (int)P.H,
+                       (int)P.Jp, L);
   }
   if (stages & TRI_ATTN_STAGE_MAIN) {
     const int64_t ntiles = P.B * P.H * P.ngroups * P.KB;
     auto launch = [&](auto ns_) {
       constexpr int NS = decltype(ns_)::value;
       if (mask)
-        hipLaunchKernelGGL((bwd_kernel<D, true, NS>), dim3(grid_xcd(ntiles)), dim3(512), 0, st, (const bf16*)q,
+        hipLaunchKernelGGL((bwd_kernel<D, true, NS, STRIDED>), dim3(grid_xcd(ntiles)), dim3(512), 0, st, (const bf16*)q,
                            (const bf16*)k, (const bf16*)v, (const bf16*)dO, biasB, mask, LDg, dqp, dbp, (bf16*)dk,
-                           (bf16*)dv, (int)P.B, (int)P.N, (int)P.H, (int)P.G, (int)P.ngroups, alpha);
+                           (bf16*)dv, (int)P.B, (int)P.N, (int)P.H, (int)P.G, (int)P.ngroups, alpha, L);
       else
-        hipLaunchKernelGGL((bwd_kernel<D, false, NS>), dim3(grid_xcd(ntiles)), dim3(512), 0, st, (const bf16*)q,
+        hipLaunchKernelGGL((bwd_kernel<D, false, NS, STRIDED>), dim3(grid_xcd(ntiles)), dim3(512), 0, st, (const bf16*)q,
                            (const bf16*)k, (const bf16*)v, (const bf16*)dO, biasB, mask, LDg, dqp, dbp, (bf16*)dk,
-                           (bf16*)dv, (int)P.B, (int)P.N, (int)P.H, (int)P.G, (int)P.ngroups, alpha);
+                           (bf16*)dv, (int)P.B, (int)P.N, (int)P.H, (int)P.G, (int)P.ngroups, alpha, L);
     };
     switch (P.Jp / 128) {  // 128-query steps per slice (shape_ok bounds N by TRI_ATTN_MAX_N)
       case 1: launch(std::integral_constant<int, 1>{}); break;
@@ -1125,8 +1189,8 @@ tri_attn_status launch_bwd(unsigned stages, const Plan& P, const void* q, const 
   }
   if (stages & TRI_ATTN_STAGE_FINAL) {
     const int64_t nslots = P.B * P.N * P.H * (P.Jp / 16) * 64;
-    hipLaunchKernelGGL(reduce_dq_kernel<D>, dim3((unsigned)((nslots + 255) / 256)), dim3(256), 0, st, dqp,
-                       (bf16*)dq, (int)P.KB, (int)P.N, (int)(P.Jp / 16), nslots, alpha);
+    hipLaunchKernelGGL((reduce_dq_kernel<D, STRIDED>), dim3((unsigned)((nslots + 255) / 256)), dim3(256), 0, st, dqp,
+                       (bf16*)dq, (int)P.KB, (int)P.N, (int)P.H, (int)(P.Jp / 16), nslots, alpha, L);
     const int64_t nbias = P.B * P.H * P.N * P.N;
     if (nbias % 4 == 0)
       hipLaunchKernelGGL(reduce_dbias_kernel<true>, dim3((unsigned)((nbias / 4 + 255) / 256)), dim3(256), 0, st, dbp,
@@ -1164,15 +1228,18 @@ size_t tri_attn_bwd_workspace_bytes(int64_t B, int64_t N, int64_t H, int64_t D) 
   return (size_t)make_plan(B, N, H, D).bwd_bytes;
 }
 
-tri_attn_status tri_attn_fwd_stages(unsigned stages, int64_t B, int64_t N, int64_t H, int64_t D, const void* q,
-                                    const void* k, const void* v, const void* bias, const uint8_t* key_mask, void* o,
-                                    float* lse, void* residual, void* workspace, size_t workspace_bytes,
-                                    hipStream_t stream) {
+tri_attn_status tri_attn_fwd_ex(unsigned stages, int layout, int64_t B, int64_t N, int64_t H, int64_t D,
+                                const void* q, const void* k, const void* v, const void* bias,
+                                const uint8_t* key_mask, void* o, float* lse, void* residual, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
   if (stages & ~TRI_ATTN_STAGE_ALL) return TRI_ATTN_ERROR_INVALID_VALUE;
   if (B < 1 || N < 1 || H < 1) return TRI_ATTN_ERROR_INVALID_VALUE;
   if (!shape_ok(B, N, H, D)) return TRI_ATTN_ERROR_UNSUPPORTED;
   if (!q || !k || !v || !bias || !o || !lse) return TRI_ATTN_ERROR_INVALID_VALUE;
   const Plan P = make_plan(B, N, H, D);
+  TokLayout L;
+  if (!make_layout(layout, P, &L)) return TRI_ATTN_ERROR_INVALID_VALUE;
+  if (!layout_fits(L, P)) return TRI_ATTN_ERROR_UNSUPPORTED;
   const int64_t tb = P.elems * 2, bb = B * H * N * N * 2, lb = P.rows * 4, mb = B * N * N;
   const Range rs[] = {{q, tb, false}, {k, tb, false}, {v, tb, false}, {bias, bb, false}, {key_mask, mb, false},
                       {o, tb, true}, {lse, lb, true}, {residual, tb, true}, {workspace, (int64_t)workspace_bytes, true}};
@@ -1181,8 +1248,23 @@ tri_attn_status tri_attn_fwd_stages(unsigned stages, int64_t B, int64_t N, int64
       (residual && !aligned16(residual)) || (workspace && !aligned16(workspace)))
     return TRI_ATTN_ERROR_MISALIGNED;
   if (!workspace || workspace_bytes < (size_t)P.bias_f32_bytes) return TRI_ATTN_ERROR_WORKSPACE;
-  return D == 16 ? launch_fwd<16>(stages, P, q, k, v, bias, key_mask, o, lse, residual, workspace, stream)
-                 : launch_fwd<32>(stages, P, q, k, v, bias, key_mask, o, lse, residual, workspace, stream);
+  auto go = [&](auto d_, auto strided_) {
+    return launch_fwd<decltype(d_)::value, decltype(strided_)::value>(stages, P, L, q, k, v, bias, key_mask, o, lse,
+                                                                        residual, workspace, stream);
+  };
+  const bool strided = layout != TRI_ATTN_LAYOUT_SLICE_HEAD;
+  if (D == 16) return strided ? go(std::integral_constant<int, 16>{}, std::true_type{})
+                              : go(std::integral_constant<int, 16>{}, std::false_type{});
+  return strided ? go(std::integral_constant<int, 32>{}, std::true_type{})
+                 : go(std::integral_constant<int, 32>{}, std::false_type{});
+}
+
+tri_attn_status tri_attn_fwd_stages(unsigned stages, int64_t B, int64_t N, int64_t H, int64_t D, const void* q,
+                                    const void* k, const void* v, const void* bias, const uint8_t* key_mask, void* o,
+                                    float* lse, void* residual, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
+  return tri_attn_fwd_ex(stages, TRI_ATTN_LAYOUT_SLICE_HEAD, B, N, H, D, q, k, v, bias, key_mask, o, lse, residual,
+                         workspace, workspace_bytes, stream);
 }
 
 tri_attn_status tri_attn_fwd(int64_t B, int64_t N, int64_t H, int64_t D, const void* q, const void* k, const void* v,
@@ -1192,16 +1274,19 @@ tri_attn_status tri_attn_fwd(int64_t B, int64_t N, int64_t H, int64_t D, const v
                              workspace_bytes, stream);
 }
 
-tri_attn_status tri_attn_bwd_stages(unsigned stages, int64_t B, int64_t N, int64_t H, int64_t D, const void* q,
-                                    const void* k, const void* v, const void* bias, const uint8_t* key_mask,
-                                    const void* o, const float* lse, const void* residual, const void* dO, void* dq,
-                                    void* dk, void* dv, float* dbias, void* workspace, size_t workspace_bytes,
-                                    hipStream_t stream) {
+tri_attn_status tri_attn_bwd_ex(unsigned stages, int layout, int64_t B, int64_t N, int64_t H, int64_t D,
+                                const void* q, const void* k, const void* v, const void* bias,
+                                const uint8_t* key_mask, const void* o, const float* lse, const void* residual,
+                                const void* dO, void* dq, void* dk, void* dv, float* dbias, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
   if (stages & ~TRI_ATTN_STAGE_ALL) return TRI_ATTN_ERROR_INVALID_VALUE;
   if (B < 1 || N < 1 || H < 1) return TRI_ATTN_ERROR_INVALID_VALUE;
   if (!shape_ok(B, N, H, D)) return TRI_ATTN_ERROR_UNSUPPORTED;
   if (!q || !k || !v || !bias || !o || !lse || !dO || !dq || !dk || !dv || !dbias) return TRI_ATTN_ERROR_INVALID_VALUE;
   const Plan P = make_plan(B, N, H, D);
+  TokLayout L;
+  if (!make_layout(layout, P, &L)) return TRI_ATTN_ERROR_INVALID_VALUE;
+  if (!layout_fits(L, P)) return TRI_ATTN_ERROR_UNSUPPORTED;
   const int64_t tb = P.elems * 2, bb = B * H * N * N * 2, lb = P.rows * 4, mb = B * N * N, db = B * H * N * N * 4;
   const Range rs[] = {{q, tb, false},  {k, tb, false},  {v, tb, false},   {bias, bb, false},
                       {key_mask, mb, false}, {o, tb, false}, {lse, lb, false}, {residual, tb, false},
@@ -1213,10 +1298,25 @@ tri_attn_status tri_attn_bwd_stages(unsigned stages, int64_t B, int64_t N, int64
       !aligned16(dbias) || (workspace && !aligned16(workspace)))
     return TRI_ATTN_ERROR_MISALIGNED;
   if (!workspace || workspace_bytes < (size_t)P.bwd_bytes) return TRI_ATTN_ERROR_WORKSPACE;
-  return D == 16 ? launch_bwd<16>(stages, P, q, k, v, bias, key_mask, o, lse, residual, dO, dq, dk, dv, dbias,
-                                  workspace, stream)
-                 : launch_bwd<32>(stages, P, q, k, v, bias, key_mask, o, lse, residual, dO, dq, dk, dv, dbias,
-                                  workspace, stream);
+  auto go = [&](auto d_, auto strided_) {
+    return launch_bwd<decltype(d_)::value, decltype(strided_)::value>(stages, P, L, q, k, v, bias, key_mask, o, lse,
+                                                                        residual, dO, dq, dk, dv, dbias, workspace,
+                                                                        stream);
+  };
+  const bool strided = layout != TRI_ATTN_LAYOUT_SLICE_HEAD;
+  if (D == 16) return strided ? go(std::integral_constant<int, 16>{}, std::true_type{})
+                              : go(std::integral_constant<int, 16>{}, std::false_type{});
+  return strided ? go(std::integral_constant<int, 32>{}, std::true_type{})
+                 : go(std::integral_constant<int, 32>{}, std::false_type{});
+}
+
+tri_attn_status tri_attn_bwd_stages(unsigned stages, int64_t B, int64_t N, int64_t H, int64_t D, const void* q,
+                                    const void* k, const void* v, const void* bias, const uint8_t* key_mask,
+                                    const void* o, const float* lse, const void* residual, const void* dO, void* dq,
+                                    void* dk, void* dv, float* dbias, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
+  return tri_attn_bwd_ex(stages, TRI_ATTN_LAYOUT_SLICE_HEAD, B, N, H, D, q, k, v, bias, key_mask, o, lse, residual,
+                         dO, dq, dk, dv, dbias, workspace, workspace_bytes, stream);
 }
 
 tri_attn_status tri_attn_bwd(int64_t B, int64_t N, int64_t H, int64_t D, const void* q, const void* k, const void* v,
