@@ -1,4 +1,5 @@
-"""FP64 CPU oracle for starting-node triangle attention (test infrastructure only).
+"""FP64 CPU oracles for starting-node triangle attention and the triangle multiplication
+core (test infrastructure only).
 
 Only tests, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline leg may
 import this package.  The GPU product path never calls it and shares no code
@@ -20,9 +21,14 @@ Sources:
   with alpha = 1/sqrt(d), the bias indexed [b,h,j,k] and shared by every slice,
   and the key mask adding -1e9 to masked keys.
 
-Every function here is pinned by tests under ``tests/test_oracle.py`` (closed
-forms, invariants, a library attention routine with autograd, central finite
-differences); none is "parity unpinned".
+The triangle multiplication core (``tri_mul_oracle``) follows the kongchang.com
+article on fast_trimul, section "什么是三角乘法更新"; its reading is stated in that
+module.
+
+Every function here is pinned by tests under ``tests/test_oracle.py`` and
+``tests/test_tri_mul_oracle.py`` (closed forms, invariants, a library attention
+routine with autograd, explicit loops, central finite differences); none is
+"parity unpinned".
 """
 from .tri_attn_oracle import (  # noqa: F401
     MASK_NEG,
@@ -31,4 +37,10 @@ from .tri_attn_oracle import (  # noqa: F401
     forward64,
     slice_backward64,
     slice_forward64,
+)
+from .tri_mul_oracle import (  # noqa: F401
+    DIRECTIONS,
+    tri_mul_backward64,
+    tri_mul_forward64,
+    tri_mul_loops64,
 )
