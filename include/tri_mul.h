@@ -1,0 +1,78 @@
+/*
+ * tri_mul.h — C ABI of the triangle multiplication core in libtriattn.so (gfx950, MI355X).
+ *
+ * The triangle multiplicative update of AlphaFold-family models lets each residue pair (i, j)
+ * gather information through a third residue k, along the rows or the columns of the pair
+ * representation, by elementwise gating, an outer product and a reduction over one index
+ * (kongchang.com article on fast_trimul, section "什么是三角乘法更新").  TurboPairFormer
+ * (arXiv 2610.05854, Abstract) runs triangle multiplication kernels next to its attention
+ * kernel.  These entry points compute the cubic core of that update, for pair tensors a and
+ * b that already carry their gating:
+ *
+ *   TRI_MUL_OUTGOING:  x[b,i,j,c] = sum_k a[b,i,k,c] * b[b,j,k,c]
+ *   TRI_MUL_INCOMING:  x[b,i,j,c] = sum_k a[b,k,i,c] * b[b,k,j,c]
+ *
+ * and its gradients (x is bilinear in a and b):
+ *
+ *   OUTGOING:  da[i,k,c] = sum_j dx[i,j,c] b[j,k,c]     db[j,k,c] = sum_i dx[i,j,c] a[i,k,c]
+ *   INCOMING:  da[k,i,c] = sum_j dx[i,j,c] b[k,j,c]     db[k,j,c] = sum_i dx[i,j,c] a[k,i,c]
+ *
+ * The projections, gating and normalisations around the core belong to the surrounding
+ * module and are not part of these calls.
+ *
+ * Memory (caller-owned DEVICE memory, row-major, contiguous, 16-byte aligned):
+ *   a, b, x, dx, da, db : bf16 [B, N, N, C], index [b, first pair index, second pair index, c]
+ *
+ * Arithmetic: bf16 products accumulated in FP32 on the matrix cores, one channel at a time;
+ * each output is rounded once to bf16 (round to nearest even).  Every sum runs in a fixed
+ * order that depends only on the shape: repeated calls give bitwise-identical outputs.
+ *
+ * Conventions: arguments are validated synchronously and nothing is launched on error; work
+ * is enqueued on `stream`; outputs are overwritten and must not overlap the inputs; the
+ * calls allocate nothing and need no workspace.
+ */
+#ifndef TRI_MUL_H
+#define TRI_MUL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#include "tri_attn.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TRI_MUL_OUTGOING = 0, /* reduce over the second pair index: rows i and j of the pair tensor */
+  TRI_MUL_INCOMING = 1  /* reduce over the first pair index: columns i and j */
+} tri_mul_direction;
+
+/* Largest N accepted (element offsets inside one batch stay below 2^31 for C <= 1024). */
+#define TRI_MUL_MAX_N 1024
+
+/*
+ * Forward: x from a and b.
+ * Errors: TRI_ATTN_ERROR_INVALID_VALUE (NULL pointer, B/N/C < 1, unknown direction, x
+ * overlapping a or b); TRI_ATTN_ERROR_UNSUPPORTED (C not a multiple of 8, C > 1024,
+ * N > TRI_MUL_MAX_N, B > 2^16); TRI_ATTN_ERROR_MISALIGNED (a pointer not 16-byte aligned);
+ * TRI_ATTN_ERROR_LAUNCH.
+ */
+tri_attn_status tri_mul_fwd(int direction, int64_t B, int64_t N, int64_t C,
+                            const void *a, const void *b, void *x, hipStream_t stream);
+
+/*
+ * Backward: da and db from a, b and the output gradient dx (same errors as tri_mul_fwd;
+ * da and db must not overlap each other or the inputs).
+ */
+tri_attn_status tri_mul_bwd(int direction, int64_t B, int64_t N, int64_t C,
+                            const void *a, const void *b, const void *dx, void *da, void *db,
+                            hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TRI_MUL_H */

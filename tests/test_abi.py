@@ -23,14 +23,17 @@ def lib():
 
 
 def _declared_functions():
-    text = open(os.path.join(ROOT, "include", "tri_attn.h")).read()
-    return sorted(set(re.findall(r"\b(tri_attn_\w+)\s*\(", text)))
+    names = set()
+    for h in ("tri_attn.h", "tri_mul.h"):
+        text = open(os.path.join(ROOT, "include", h)).read()
+        names |= set(re.findall(r"\b(tri_(?:attn|mul)_\w+)\s*\(", text))
+    return sorted(names)
 
 
 def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
-    assert {"tri_attn_fwd", "tri_attn_bwd", "tri_attn_fwd_workspace_bytes",
-            "tri_attn_bwd_workspace_bytes", "tri_attn_status_string"} <= set(names)
+    assert {"tri_attn_fwd", "tri_attn_bwd", "tri_attn_fwd_workspace_bytes", "tri_attn_bwd_workspace_bytes",
+            "tri_attn_status_string", "tri_attn_fwd_ex", "tri_attn_bwd_ex", "tri_mul_fwd", "tri_mul_bwd"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -152,3 +155,25 @@ def test_layout_validation(lib):
         assert f(2, shape=(1, 768, 64, 32)) == UNSUPPORTED
         assert f(1, shape=(1, 768, 64, 32), wsb=16) == WORKSPACE  # pair_start rows are H*D apart
         assert f(0, shape=(1, 768, 64, 32), wsb=16) == WORKSPACE
+
+
+def test_tri_mul_validation(lib):
+    a, b, x, dx, da, db = _ptrs(6)
+    fwd = lambda d, B, N, C, **k: ta.tri_mul_fwd(d, B, N, C, k.get("a", a), k.get("b", b), k.get("x", x), 0)
+    bwd = lambda d, B, N, C, **k: ta.tri_mul_bwd(d, B, N, C, k.get("a", a), k.get("b", b), k.get("dx", dx),
+                                                 k.get("da", da), k.get("db", db), 0)
+    for f in (fwd, bwd):
+        assert f(2, 1, 64, 32) == INVALID          # unknown direction
+        assert f(-1, 1, 64, 32) == INVALID
+        assert f(0, 0, 64, 32) == INVALID
+        assert f(0, 1, 0, 32) == INVALID
+        assert f(1, 1, 64, 0) == INVALID
+        assert f(0, 1, 64, 12) == UNSUPPORTED      # C not a multiple of 8
+        assert f(0, 1, 64, 1032) == UNSUPPORTED
+        assert f(1, 1, 1025, 32) == UNSUPPORTED
+        assert f(0, 1, 64, 32, a=0) == INVALID
+        assert f(0, 1, 64, 32, a=a + 8) == MISALIGNED
+    assert fwd(0, 1, 64, 32, x=a + 64) == INVALID  # output overlaps an input
+    assert bwd(0, 1, 64, 32, db=da + 1024) == INVALID
+    assert bwd(1, 1, 64, 32, da=dx) == INVALID
+    assert bwd(0, 1, 64, 32, dx=0) == INVALID

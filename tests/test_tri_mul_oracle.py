@@ -13,7 +13,6 @@ import pytest
 import oracle
 
 
-
 def _rand(shape, seed):
     return np.random.default_rng(seed).standard_normal(shape)
 

@@ -104,3 +104,22 @@ def make_inputs(B: int, N: int, H: int, D: int, *, bias_std: float = 1.0, mask_t
 
 def workload_inputs(w: Workload) -> dict:
     return make_inputs(w.B, w.N, w.H, w.D, bias_std=w.bias_std, mask_tail=w.mask_tail, seed=w.seed)
+
+
+def make_pair_inputs(B: int, N: int, C: int, *, seed: int = 0, scale: float = 1.0) -> dict:
+    """Pair tensors for the triangle multiplication core: a, b, dx drawn in that order from
+    PCG64(seed), standard normal float32 times `scale`, then RNE to bf16; uint16 bit arrays of
+    shape [B, N, N, C] (channels last)."""
+    rng = np.random.default_rng(seed)
+    out = {}
+    for name in ("a", "b", "dx"):
+        out[name] = f32_to_bf16_bits(rng.standard_normal((B, N, N, C), dtype=np.float32) * np.float32(scale))
+    return out
+
+
+# triangle multiplication workloads: the crop of the attention headline with AlphaFold3's
+# hidden width of the multiplicative update (128 channels), and a small case
+TRIMUL_WORKLOADS = {
+    "trimul_n768_c128": dict(B=1, N=768, C=128, seed=2024),
+    "trimul_n64_c128": dict(B=1, N=64, C=128, seed=2025),
+}

@@ -21,9 +21,12 @@ __all__ = [
     "TriAttnError", "load_library", "tri_attn_status_string", "tri_attn_fwd_workspace_bytes",
     "tri_attn_bwd_workspace_bytes", "tri_attn_fwd", "tri_attn_bwd", "tri_attn_fwd_stages", "tri_attn_bwd_stages",
     "tri_attn_fwd_ex", "tri_attn_bwd_ex", "triangle_attention", "TRI_ATTN_MAX_N", "LAYOUTS",
+    "tri_mul_fwd", "tri_mul_bwd", "triangle_multiplication", "TRI_MUL_DIRECTIONS", "TRI_MUL_MAX_N",
 ]
 
 TRI_ATTN_MAX_N = 768
+TRI_MUL_MAX_N = 1024
+TRI_MUL_DIRECTIONS = {"outgoing": 0, "incoming": 1}
 _lib = None
 
 
@@ -60,6 +63,10 @@ def load_library(path: str = LIB_PATH):
     lib.tri_attn_fwd_ex.restype = ctypes.c_int
     lib.tri_attn_bwd_ex.argtypes = [ctypes.c_uint, ctypes.c_int] + lib.tri_attn_bwd.argtypes
     lib.tri_attn_bwd_ex.restype = ctypes.c_int
+    lib.tri_mul_fwd.argtypes = [ctypes.c_int, i64, i64, i64, vp, vp, vp, vp]
+    lib.tri_mul_fwd.restype = ctypes.c_int
+    lib.tri_mul_bwd.argtypes = [ctypes.c_int, i64, i64, i64, vp, vp, vp, vp, vp, vp]
+    lib.tri_mul_bwd.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -144,6 +151,17 @@ def tri_attn_bwd_ex(stages, layout, B, N, H, D, q, k, v, bias, key_mask, o, lse,
                                               int(workspace_bytes), _stream(stream)))
 
 
+def tri_mul_fwd(direction, B, N, C, a, b, x, stream=None) -> int:
+    """Marshal to the C entry point (include/tri_mul.h); returns the status code."""
+    return int(load_library().tri_mul_fwd(direction, B, N, C, _ptr(a), _ptr(b), _ptr(x), _stream(stream)))
+
+
+def tri_mul_bwd(direction, B, N, C, a, b, dx, da, db, stream=None) -> int:
+    """Marshal to the C entry point (include/tri_mul.h); returns the status code."""
+    return int(load_library().tri_mul_bwd(direction, B, N, C, _ptr(a), _ptr(b), _ptr(dx), _ptr(da), _ptr(db),
+                                          _stream(stream)))
+
+
 def _check(status: int, where: str):
     if status != 0:
         raise TriAttnError(status, where)
@@ -220,3 +238,40 @@ def triangle_attention(q, k, v, bias, key_mask=None, residual_compensation=True,
     [b, slice, key], in the orientation of the attended axis, or None.
     """
     return _TriAttnFn.apply(q, k, v, bias, key_mask, residual_compensation, layout)
+
+
+def _mul_shape(a, b, direction):
+    if direction not in TRI_MUL_DIRECTIONS:
+        raise ValueError(f"direction must be one of {sorted(TRI_MUL_DIRECTIONS)}")
+    if a.dim() != 4 or a.shape[1] != a.shape[2] or tuple(b.shape) != tuple(a.shape):
+        raise ValueError("a and b must both be [B, N, N, C]")
+    return tuple(a.shape)
+
+
+class _TriMulFn(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, a, b, direction):
+        B, N, _, C = _mul_shape(a, b, direction)
+        x = torch.empty_like(a)
+        _check(tri_mul_fwd(TRI_MUL_DIRECTIONS[direction], B, N, C, a, b, x), "tri_mul_fwd")
+        ctx.save_for_backward(a, b)
+        ctx.direction = direction
+        return x
+
+    @staticmethod
+    def backward(ctx, dx):
+        a, b = ctx.saved_tensors
+        B, N, _, C = a.shape
+        da, db = torch.empty_like(a), torch.empty_like(b)
+        _check(tri_mul_bwd(TRI_MUL_DIRECTIONS[ctx.direction], B, N, C, a, b, dx.contiguous(), da, db),
+               "tri_mul_bwd")
+        return da, db, None
+
+
+def triangle_multiplication(a, b, direction="outgoing"):
+    """Cubic core of the triangle multiplicative update, differentiable in a and b.
+
+    a, b: contiguous bf16 [B, N, N, C] on one GPU (C a multiple of 8).
+    outgoing: x[b,i,j,c] = sum_k a[b,i,k,c] b[b,j,k,c];  incoming: x[b,i,j,c] = sum_k a[b,k,i,c] b[b,k,j,c].
+    """
+    return _TriMulFn.apply(a, b, direction)

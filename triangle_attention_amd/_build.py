@@ -7,7 +7,7 @@ import subprocess
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG_DIR)
-SRC = os.path.join(PKG_DIR, "csrc", "tri_attn.hip")
+SRCS = [os.path.join(PKG_DIR, "csrc", f) for f in ("tri_attn.hip", "tri_mul.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libtriattn.so")
 
@@ -29,7 +29,7 @@ def hipcc() -> str:
 def build(verbose: bool = False, extra_flags=()) -> str:
     """Always recompiles; writes the library atomically and returns its path."""
     tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, "-I", INCLUDE, SRC, "-o", tmp]
+    cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, "-I", INCLUDE, *SRCS, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     log = "\n".join(x for x in (res.stdout + res.stderr).splitlines() if "packed-fp32-ops" not in x)
     if res.returncode != 0:

@@ -1,0 +1,252 @@
+// tri_mul.hip — the triangle multiplication core on gfx950 (MI355X), part of libtriattn.so.
+//
+// Triangle multiplicative update (kongchang.com article on fast_trimul, section
+// "什么是三角乘法更新"): each pair (i, j) gathers information through a third index k by an
+// outer product and a reduction over k, along the rows (outgoing) or the columns (incoming)
+// of the pair representation.  The cubic core computed here, for pair tensors [B, N, N, C]
+// with channels last:
+//   outgoing  x[i,j,c] = sum_k a[i,k,c] b[j,k,c]      incoming  x[i,j,c] = sum_k a[k,i,c] b[k,j,c]
+// and the gradients of both.  All six products are one operation with different strides:
+//   OUT[r, s, c] = sum_t P[r, t, c] * Q[s, t, c]
+// where P and Q address their row index r (s) and reduction index t with strides that are
+// either C (the second pair index) or N*C (the first), and OUT[r, s, c] sits at r*N*C + s*C + c.
+//
+// Kernel design.  Each channel is an independent N x N x N product, so a work-group takes a
+// 64 x 64 output tile of 8 adjacent channels (one 16-byte chunk per pair entry) and each of its
+// 8 waves owns one channel: four 32x32 accumulator tiles on v_mfma_f32_32x32x16_bf16.  The
+// reduction runs in steps of 32.  Every thread loads 4 chunks (4 consecutive t of one row, 8
+// channels each) of P and of Q for the next step while the current step's products run, then
+// transposes them in registers into per-channel rows of 4 t (8 bytes) and writes them to the
+// other half of a double-buffered LDS stage, laid out [channel][row][t] with the 16-byte
+// chunks of each 64-byte row XOR-swizzled so that the operand reads (16 rows at one t-offset
+// per pass) and the writes are free of bank conflicts.  One barrier per step.  The output
+// tile goes through LDS once more, to [row][col][channel], so that the stores are 16-byte
+// chunks of the channels-last layout.  The C/8 channel groups of one output tile get adjacent
+// tile ids, and each XCD runs a contiguous range of ids, so the work-groups that split a pair
+// row by channel run together and meet in that XCD's L2.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tri_mul.h"
+
+namespace {
+
+typedef __bf16 bf16;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) bf16x8 lbf16x8;
+typedef __attribute__((address_space(3))) u32x2 lu32x2;
+typedef __attribute__((address_space(3))) u32x4 lu32x4;
+typedef __attribute__((address_space(3))) bf16 lbf16;
+
+constexpr int kXcd = 8;        // XCDs per MI355X; work-groups are dispatched round-robin over them
+constexpr int RT = 64;         // output rows (and columns) per tile
+constexpr int TT = 32;         // reduction step
+constexpr int CB = 8;          // channels per work-group (one 16-byte chunk)
+constexpr int kThreads = 512;  // 8 waves, one channel each
+constexpr int kStage = CB * RT * TT * 2;  // bytes of one operand's stage tile (32 KiB)
+
+// element strides (within one batch) of the row and reduction indices of P and Q, and of the
+// row and column indices of the output
+struct MulStrides {
+  int64_t pR, pT, qR, qT, oR, oS;
+};
+
+__device__ __forceinline__ int64_t xcd_tile(int64_t ntiles) {
+  const int64_t per = (ntiles + kXcd - 1) / kXcd;
+  return (int64_t)(blockIdx.x % kXcd) * per + blockIdx.x / kXcd;
+}
+
+// Byte offset of (channel cc, row r, reduction t) in a stage tile: rows of 32 t (64 bytes),
+// 16-byte chunk index XOR-swizzled with (r / 4) % 4.
+__device__ __forceinline__ int stage_off(int cc, int r, int t) {
+  return cc * (RT * TT * 2) + r * (TT * 2) + ((((t >> 3) ^ (r >> 2)) & 3) << 4) + (t & 7) * 2;
+}
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__global__ __launch_bounds__(kThreads, 1)
+void tri_mul_kernel(const bf16* __restrict__ P, const bf16* __restrict__ Q, bf16* __restrict__ out, int B, int N,
+                    int C, MulStrides S) {
+  __shared__ __attribute__((aligned(16))) char lds[4 * kStage];  // 2 buffers x (P, Q) = 128 KiB
+  const int nT = (N + RT - 1) / RT, nCG = C / CB;
+  const int64_t ntiles = (int64_t)B * nT * nT * nCG;
+  const int64_t tile = xcd_tile(ntiles);
+  if (tile >= ntiles) return;
+  const int cg = (int)(tile % nCG);
+  int64_t rest = tile / nCG;
+  const int st = (int)(rest % nT); rest /= nT;
+  const int rt = (int)(rest % nT);
+  const int b = (int)(rest / nT);
+  const int64_t base = (int64_t)b * N * N * C + cg * CB;
+
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
+  // loader role: row lr of the tile, reduction quad tq (t = 4 tq .. 4 tq + 3 of the step)
+  const int lr = tid >> 3, tq = tid & 7;
+  const int pr = rt * RT + lr, qs = st * RT + lr;
+  const bool pok = pr < N, qok = qs < N;
+  const bf16* pRow = P + base + (int64_t)(pok ? pr : 0) * S.pR;
+  const bf16* qRow = Q + base + (int64_t)(qok ? qs : 0) * S.qR;
+
+  u32x4 pv[4], qv[4];
+  auto load = [&](int t0) {
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      const int t = t0 + 4 * tq + e;
+      const bool tok = t < N;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      pv[e] = (pok && tok) ? *(const u32x4*)(pRow + (int64_t)t * S.pT) : z;
+      qv[e] = (qok && tok) ? *(const u32x4*)(qRow + (int64_t)t * S.qT) : z;
+    }
+  };
+  // 4 chunks (t = 4tq..4tq+3) x 8 channels -> 8 channel rows of 4 t; dword d of a chunk holds
+  // channels 2d (low half) and 2d + 1 (high half)
+  auto store = [&](int buf) {
+    char* Pt = lds + buf * 2 * kStage;
+    char* Qt = Pt + kStage;
+#pragma unroll
+    for (int d = 0; d < 4; d++) {
+      const u32x2 plo = {(pv[0][d] & 0xFFFFu) | (pv[1][d] << 16), (pv[2][d] & 0xFFFFu) | (pv[3][d] << 16)};
+      const u32x2 phi = {(pv[0][d] >> 16) | (pv[1][d] & 0xFFFF0000u), (pv[2][d] >> 16) | (pv[3][d] & 0xFFFF0000u)};
+      const u32x2 qlo = {(qv[0][d] & 0xFFFFu) | (qv[1][d] << 16), (qv[2][d] & 0xFFFFu) | (qv[3][d] << 16)};
+      const u32x2 qhi = {(qv[0][d] >> 16) | (qv[1][d] & 0xFFFF0000u), (qv[2][d] >> 16) | (qv[3][d] & 0xFFFF0000u)};
+      *(lu32x2*)(Pt + stage_off(2 * d, lr, 4 * tq)) = plo;
+      *(lu32x2*)(Pt + stage_off(2 * d + 1, lr, 4 * tq)) = phi;
+      *(lu32x2*)(Qt + stage_off(2 * d, lr, 4 * tq)) = qlo;
+      *(lu32x2*)(Qt + stage_off(2 * d + 1, lr, 4 * tq)) = qhi;
+    }
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; i++)
+#pragma unroll
+    for (int j = 0; j < 2; j++) acc[i][j] = f32x16{};
+
+  const int nsteps = (N + TT - 1) / TT;
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int s = 0; s < nsteps; s++) {
+    const bool more = s + 1 < nsteps;
+    if (more) load((s + 1) * TT);  // in flight while this step's products run
+    const char* Pt = lds + (s & 1) * 2 * kStage;
+    const char* Qt = Pt + kStage;
+#pragma unroll
+    for (int kk = 0; kk < 2; kk++) {
+      // A operand: row l%32 (+32), reduction 16 kk + 8 (l/32) .. +7; B operand likewise
+      const int t = kk * 16 + 8 * (l >> 5);
+      const bf16x8 a0 = *(const lbf16x8*)(Pt + stage_off(w, l & 31, t));
+      const bf16x8 a1 = *(const lbf16x8*)(Pt + stage_off(w, 32 + (l & 31), t));
+      const bf16x8 b0 = *(const lbf16x8*)(Qt + stage_off(w, l & 31, t));
+      const bf16x8 b1 = *(const lbf16x8*)(Qt + stage_off(w, 32 + (l & 31), t));
+      acc[0][0] = mfma32(a0, b0, acc[0][0]);
+      acc[0][1] = mfma32(a0, b1, acc[0][1]);
+      acc[1][0] = mfma32(a1, b0, acc[1][0]);
+      acc[1][1] = mfma32(a1, b1, acc[1][1]);
+    }
+    if (more) store((s + 1) & 1);  // that buffer's last readers passed the previous barrier
+    __syncthreads();
+  }
+
+  // output tile through LDS as [row][col][channel] bf16 (64 KiB, the stage buffers' space)
+  lbf16* E = (lbf16*)lds;
+#pragma unroll
+  for (int i = 0; i < 2; i++)
+#pragma unroll
+    for (int j = 0; j < 2; j++)
+#pragma unroll
+      for (int e = 0; e < 16; e++) {
+        const int r = i * 32 + 8 * (e >> 2) + 4 * (l >> 5) + (e & 3);
+        const int c = j * 32 + (l & 31);
+        E[(r * RT + c) * CB + w] = (bf16)acc[i][j][e];
+      }
+  __syncthreads();
+  bf16* ob = out + base;
+#pragma unroll
+  for (int e = 0; e < RT * RT / kThreads; e++) {
+    const int q = tid + e * kThreads;
+    const int r = q / RT, c = q % RT;
+    const int gr = rt * RT + r, gc = st * RT + c;
+    if (gr < N && gc < N)
+      *(u32x4*)(ob + (int64_t)gr * S.oR + (int64_t)gc * S.oS) = *(const lu32x4*)(E + q * CB);
+  }
+}
+
+unsigned grid_xcd(int64_t ntiles) { return (unsigned)((ntiles + kXcd - 1) / kXcd * kXcd); }
+
+struct Range { const void* p; int64_t n; };
+bool overlap(Range x, Range y) {
+  const uintptr_t a0 = (uintptr_t)x.p, a1 = a0 + (uintptr_t)x.n, b0 = (uintptr_t)y.p, b1 = b0 + (uintptr_t)y.n;
+  return a0 < b1 && b0 < a1;
+}
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+tri_attn_status check_shape(int direction, int64_t B, int64_t N, int64_t C) {
+  if (direction != TRI_MUL_OUTGOING && direction != TRI_MUL_INCOMING) return TRI_ATTN_ERROR_INVALID_VALUE;
+  if (B < 1 || N < 1 || C < 1) return TRI_ATTN_ERROR_INVALID_VALUE;
+  if (C % CB != 0 || C > 1024 || N > TRI_MUL_MAX_N || B > (1 << 16)) return TRI_ATTN_ERROR_UNSUPPORTED;
+  return TRI_ATTN_SUCCESS;
+}
+
+tri_attn_status launch(const void* p, const void* q, void* o, int64_t B, int64_t N, int64_t C, MulStrides S,
+                       hipStream_t st) {
+  const int64_t nT = (N + RT - 1) / RT;
+  const int64_t ntiles = B * nT * nT * (C / CB);
+  hipLaunchKernelGGL(tri_mul_kernel, dim3(grid_xcd(ntiles)), dim3(kThreads), 0, st, (const bf16*)p, (const bf16*)q,
+                     (bf16*)o, (int)B, (int)N, (int)C, S);
+  return hipGetLastError() == hipSuccess ? TRI_ATTN_SUCCESS : TRI_ATTN_ERROR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+tri_attn_status tri_mul_fwd(int direction, int64_t B, int64_t N, int64_t C, const void* a, const void* b, void* x,
+                            hipStream_t stream) {
+  const tri_attn_status st = check_shape(direction, B, N, C);
+  if (st != TRI_ATTN_SUCCESS) return st;
+  if (!a || !b || !x) return TRI_ATTN_ERROR_INVALID_VALUE;
+  const int64_t bytes = B * N * N * C * 2;
+  if (overlap({x, bytes}, {a, bytes}) || overlap({x, bytes}, {b, bytes})) return TRI_ATTN_ERROR_INVALID_VALUE;
+  if (!aligned16(a) || !aligned16(b) || !aligned16(x)) return TRI_ATTN_ERROR_MISALIGNED;
+  const int64_t NC = N * C;
+  // outgoing: P[r=i,t=k] = a[i,k], Q[s=j,t=k] = b[j,k]; incoming: P[r=i,t=k] = a[k,i], Q = b[k,j]
+  const MulStrides S = direction == TRI_MUL_OUTGOING ? MulStrides{NC, C, NC, C, NC, C}
+                                                     : MulStrides{C, NC, C, NC, NC, C};
+  return launch(a, b, x, B, N, C, S, stream);
+}
+
+tri_attn_status tri_mul_bwd(int direction, int64_t B, int64_t N, int64_t C, const void* a, const void* b,
+                            const void* dx, void* da, void* db, hipStream_t stream) {
+  const tri_attn_status st = check_shape(direction, B, N, C);
+  if (st != TRI_ATTN_SUCCESS) return st;
+  if (!a || !b || !dx || !da || !db) return TRI_ATTN_ERROR_INVALID_VALUE;
+  const int64_t bytes = B * N * N * C * 2;
+  const Range ins[] = {{a, bytes}, {b, bytes}, {dx, bytes}};
+  for (const Range& r : ins)
+    if (overlap({da, bytes}, r) || overlap({db, bytes}, r)) return TRI_ATTN_ERROR_INVALID_VALUE;
+  if (overlap({da, bytes}, {db, bytes})) return TRI_ATTN_ERROR_INVALID_VALUE;
+  if (!aligned16(a) || !aligned16(b) || !aligned16(dx) || !aligned16(da) || !aligned16(db))
+    return TRI_ATTN_ERROR_MISALIGNED;
+  const int64_t NC = N * C;
+  tri_attn_status r1, r2;
+  if (direction == TRI_MUL_OUTGOING) {
+    // da[i,k] = sum_j dx[i,j] b[j,k]: P[r=i,t=j] = dx[i,j], Q[s=k,t=j] = b[j,k]
+    r1 = launch(dx, b, da, B, N, C, MulStrides{NC, C, C, NC, NC, C}, stream);
+    // db[j,k] = sum_i dx[i,j] a[i,k]: P[r=j,t=i] = dx[i,j], Q[s=k,t=i] = a[i,k]
+    r2 = launch(dx, a, db, B, N, C, MulStrides{C, NC, C, NC, NC, C}, stream);
+  } else {
+    // da[k,i] = sum_j b[k,j] dx[i,j]: P[r=k,t=j] = b[k,j], Q[s=i,t=j] = dx[i,j]
+    r1 = launch(b, dx, da, B, N, C, MulStrides{NC, C, NC, C, NC, C}, stream);
+    // db[k,j] = sum_i a[k,i] dx[i,j]: P[r=k,t=i] = a[k,i], Q[s=j,t=i] = dx[i,j]
+    r2 = launch(a, dx, db, B, N, C, MulStrides{NC, C, C, NC, NC, C}, stream);
+  }
+  return r1 != TRI_ATTN_SUCCESS ? r1 : r2;
+}
+
+}  // extern "C"
