@@ -20,8 +20,16 @@
  * The projections, gating and normalisations around the core belong to the surrounding
  * module and are not part of these calls.
  *
- * Memory (caller-owned DEVICE memory, row-major, contiguous, 16-byte aligned):
- *   a, b, x, dx, da, db : bf16 [B, N, N, C], index [b, first pair index, second pair index, c]
+ * Memory (caller-owned DEVICE memory, row-major, contiguous, 16-byte aligned), in one of two
+ * layouts shared by all six tensors of a call:
+ *   TRI_MUL_CHANNELS_LAST   bf16 [B, N, N, C], index [b, first pair index, second pair index, c]
+ *                           (the layout of the pair representation); C a multiple of 8
+ *   TRI_MUL_CHANNELS_FIRST  bf16 [B, C, N, N], index [b, c, first pair index, second pair index]
+ *                           (each channel a plain N x N matrix); N a multiple of 8
+ * The channels-first form is the fast one: every load is a run of contiguous elements of one
+ * channel.  In the channels-last form a work-group reads 8 channels, 16 bytes of each pair
+ * entry, which spends most of each cache line it touches; it serves callers that hold the
+ * pair layout and cannot have the projections write channels first.
  *
  * Arithmetic: bf16 products accumulated in FP32 on the matrix cores, one channel at a time;
  * each output is rounded once to bf16 (round to nearest even).  Every sum runs in a fixed
@@ -50,24 +58,30 @@ typedef enum {
   TRI_MUL_INCOMING = 1  /* reduce over the first pair index: columns i and j */
 } tri_mul_direction;
 
+typedef enum {
+  TRI_MUL_CHANNELS_LAST = 0,
+  TRI_MUL_CHANNELS_FIRST = 1
+} tri_mul_layout;
+
 /* Largest N accepted (element offsets inside one batch stay below 2^31 for C <= 1024). */
 #define TRI_MUL_MAX_N 1024
 
 /*
  * Forward: x from a and b.
- * Errors: TRI_ATTN_ERROR_INVALID_VALUE (NULL pointer, B/N/C < 1, unknown direction, x
- * overlapping a or b); TRI_ATTN_ERROR_UNSUPPORTED (C not a multiple of 8, C > 1024,
- * N > TRI_MUL_MAX_N, B > 2^16); TRI_ATTN_ERROR_MISALIGNED (a pointer not 16-byte aligned);
+ * Errors: TRI_ATTN_ERROR_INVALID_VALUE (NULL pointer, B/N/C < 1, unknown direction or layout,
+ * x overlapping a or b); TRI_ATTN_ERROR_UNSUPPORTED (C > 1024, N > TRI_MUL_MAX_N, B > 2^16,
+ * C not a multiple of 8 in the channels-last layout, N not a multiple of 8 in the
+ * channels-first layout); TRI_ATTN_ERROR_MISALIGNED (a pointer not 16-byte aligned);
  * TRI_ATTN_ERROR_LAUNCH.
  */
-tri_attn_status tri_mul_fwd(int direction, int64_t B, int64_t N, int64_t C,
+tri_attn_status tri_mul_fwd(int direction, int layout, int64_t B, int64_t N, int64_t C,
                             const void *a, const void *b, void *x, hipStream_t stream);
 
 /*
  * Backward: da and db from a, b and the output gradient dx (same errors as tri_mul_fwd;
  * da and db must not overlap each other or the inputs).
  */
-tri_attn_status tri_mul_bwd(int direction, int64_t B, int64_t N, int64_t C,
+tri_attn_status tri_mul_bwd(int direction, int layout, int64_t B, int64_t N, int64_t C,
                             const void *a, const void *b, const void *dx, void *da, void *db,
                             hipStream_t stream);
 

@@ -159,20 +159,25 @@ def test_layout_validation(lib):
 
 def test_tri_mul_validation(lib):
     a, b, x, dx, da, db = _ptrs(6)
-    fwd = lambda d, B, N, C, **k: ta.tri_mul_fwd(d, B, N, C, k.get("a", a), k.get("b", b), k.get("x", x), 0)
-    bwd = lambda d, B, N, C, **k: ta.tri_mul_bwd(d, B, N, C, k.get("a", a), k.get("b", b), k.get("dx", dx),
-                                                 k.get("da", da), k.get("db", db), 0)
+    fwd = lambda d, B, N, C, lay=0, **k: ta.tri_mul_fwd(d, lay, B, N, C, k.get("a", a), k.get("b", b),
+                                                          k.get("x", x), 0)
+    bwd = lambda d, B, N, C, lay=0, **k: ta.tri_mul_bwd(d, lay, B, N, C, k.get("a", a), k.get("b", b),
+                                                          k.get("dx", dx), k.get("da", da), k.get("db", db), 0)
+    assert ta.TRI_MUL_LAYOUTS == {"channels_last": 0, "channels_first": 1}
     for f in (fwd, bwd):
         assert f(2, 1, 64, 32) == INVALID          # unknown direction
         assert f(-1, 1, 64, 32) == INVALID
+        assert f(0, 1, 64, 32, lay=2) == INVALID   # unknown layout
         assert f(0, 0, 64, 32) == INVALID
         assert f(0, 1, 0, 32) == INVALID
         assert f(1, 1, 64, 0) == INVALID
-        assert f(0, 1, 64, 12) == UNSUPPORTED      # C not a multiple of 8
+        assert f(0, 1, 64, 12) == UNSUPPORTED      # channels last: C a multiple of 8
+        assert f(0, 1, 60, 16, lay=1) == UNSUPPORTED  # channels first: N a multiple of 8
         assert f(0, 1, 64, 1032) == UNSUPPORTED
         assert f(1, 1, 1025, 32) == UNSUPPORTED
         assert f(0, 1, 64, 32, a=0) == INVALID
         assert f(0, 1, 64, 32, a=a + 8) == MISALIGNED
+        assert f(0, 1, 64, 12, lay=1, a=a + 8) == MISALIGNED  # channels first accepts any C
     assert fwd(0, 1, 64, 32, x=a + 64) == INVALID  # output overlaps an input
     assert bwd(0, 1, 64, 32, db=da + 1024) == INVALID
     assert bwd(1, 1, 64, 32, da=dx) == INVALID

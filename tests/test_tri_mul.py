@@ -1,4 +1,5 @@
-"""GPU parity of the triangle multiplication core (include/tri_mul.h) against the FP64 oracle.
+"""GPU parity of the triangle multiplication core (include/tri_mul.h) against the FP64 oracle,
+in both layouts (channels last [B, N, N, C] and channels first [B, C, N, N]).
 
 Definition (kongchang.com article on fast_trimul, section "什么是三角乘法更新"; reading in
 ``oracle/tri_mul_oracle.py``): outgoing x[i,j,c] = sum_k a[i,k,c] b[j,k,c], incoming
@@ -26,14 +27,26 @@ def _bits(t):
     return t.view(torch.int16)
 
 
-def _run(ta, a, b, dx, direction):
+def cf(t):  # channels last -> channels first
+    return t.permute(0, 3, 1, 2).contiguous()
+
+
+def cl(t):  # channels first -> channels last
+    return t.permute(0, 2, 3, 1).contiguous()
+
+
+def _run(ta, a, b, dx, direction, layout="channels_last"):
+    """a, b, dx channels last; returns channels-last outputs computed in `layout`."""
     B, N, _, C = a.shape
-    d = ta.TRI_MUL_DIRECTIONS[direction]
+    d, lay = ta.TRI_MUL_DIRECTIONS[direction], ta.TRI_MUL_LAYOUTS[layout]
+    if layout == "channels_first":
+        a, b, dx = cf(a), cf(b), cf(dx)
     x, da, db = torch.empty_like(a), torch.empty_like(a), torch.empty_like(a)
-    assert ta.tri_mul_fwd(d, B, N, C, a, b, x) == 0
-    assert ta.tri_mul_bwd(d, B, N, C, a, b, dx, da, db) == 0
+    assert ta.tri_mul_fwd(d, lay, B, N, C, a, b, x) == 0
+    assert ta.tri_mul_bwd(d, lay, B, N, C, a, b, dx, da, db) == 0
     torch.cuda.synchronize()
-    return dict(x=x, da=da, db=db)
+    out = dict(x=x, da=da, db=db)
+    return {n: cl(v) for n, v in out.items()} if layout == "channels_first" else out
 
 
 def _bound_check(name, got, ref, absref):
@@ -46,10 +59,10 @@ def _bound_check(name, got, ref, absref):
     assert e <= TOL_RRMSE, (name, e)
 
 
-def _check(inp, direction, channels=None):
+def _check(inp, direction, channels=None, layout="channels_last"):
     import triangle_attention_amd as ta
     dev = {n: to_dev(inp[n]) for n in ("a", "b", "dx")}
-    out = _run(ta, dev["a"], dev["b"], dev["dx"], direction)
+    out = _run(ta, dev["a"], dev["b"], dev["dx"], direction, layout)
     x64 = {n: bf16_bits_to_f64(inp[n]) for n in ("a", "b", "dx")}
     if channels is not None:  # channels are independent: check a subset at large sizes
         x64 = {n: v[..., channels] for n, v in x64.items()}
@@ -82,23 +95,48 @@ SMALL = [
 @pytest.mark.parametrize("direction", ["outgoing", "incoming"])
 @pytest.mark.parametrize("B,N,C", SMALL)
 def test_tri_mul_parity_small(B, N, C, direction):
-    print(f"tri_mul {direction} B={B} N={N} C={C}", flush=True)
+    print(f"tri_mul channels_last {direction} B={B} N={N} C={C}", flush=True)
     inp = make_pair_inputs(B, N, C, seed=7 * N + C)
     _check(inp, direction)
 
 
+# channels first: N a multiple of 8 (one 128 x 128 tile, ragged tiles, several tiles; any C)
+SMALL_CF = [(1, 8, 3), (1, 40, 8), (2, 136, 5), (1, 200, 4), (1, 264, 2)]
+
+
 @pytest.mark.parametrize("direction", ["outgoing", "incoming"])
-def test_tri_mul_parity_full_size_sampled_channels(direction):
+@pytest.mark.parametrize("B,N,C", SMALL_CF)
+def test_tri_mul_parity_small_channels_first(B, N, C, direction):
+    print(f"tri_mul channels_first {direction} B={B} N={N} C={C}", flush=True)
+    inp = make_pair_inputs(B, N, C, seed=11 * N + C)
+    _check(inp, direction, layout="channels_first")
+
+
+@pytest.mark.parametrize("layout", ["channels_last", "channels_first"])
+@pytest.mark.parametrize("direction", ["outgoing", "incoming"])
+def test_tri_mul_parity_full_size_sampled_channels(direction, layout):
     w = TRIMUL_WORKLOADS["trimul_n768_c128"]
-    print(f"tri_mul {direction} full size {w}", flush=True)
+    print(f"tri_mul {layout} {direction} full size {w}", flush=True)
     inp = make_pair_inputs(w["B"], w["N"], w["C"], seed=w["seed"])
     # one channel from each of four channel groups, including the last channel
-    _check(inp, direction, channels=[0, 45, 90, 127])
+    _check(inp, direction, channels=[0, 45, 90, 127], layout=layout)
+
+
+def test_tri_mul_layouts_agree_bitwise():
+    # both kernels add the same 16-term products in the same ascending order per element
+    import triangle_attention_amd as ta
+    inp = make_pair_inputs(1, 136, 16, seed=5)
+    a, b, dx = (to_dev(inp[n]) for n in ("a", "b", "dx"))
+    for direction in ("outgoing", "incoming"):
+        last = _run(ta, a, b, dx, direction, "channels_last")
+        first = _run(ta, a, b, dx, direction, "channels_first")
+        for n in ("x", "da", "db"):
+            assert torch.equal(_bits(last[n]), _bits(first[n])), (direction, n)
 
 
 def test_tri_mul_deterministic_and_autograd():
     import triangle_attention_amd as ta
-    inp = make_pair_inputs(1, 150, 32, seed=99)
+    inp = make_pair_inputs(1, 152, 32, seed=99)  # N a multiple of 8 (channels first)
     a, b, dx = (to_dev(inp[n]) for n in ("a", "b", "dx"))
     for direction in ("outgoing", "incoming"):
         first = _run(ta, a, b, dx, direction)
@@ -113,3 +151,12 @@ def test_tri_mul_deterministic_and_autograd():
         assert torch.equal(_bits(x.detach()), _bits(first["x"]))
         assert torch.equal(_bits(al.grad), _bits(first["da"]))
         assert torch.equal(_bits(bl.grad), _bits(first["db"]))
+        # channels first through the autograd wrapper
+        ref = _run(ta, a, b, dx, direction, "channels_first")
+        al, bl = cf(a).requires_grad_(True), cf(b).requires_grad_(True)
+        x = ta.triangle_multiplication(al, bl, direction, layout="channels_first")
+        x.backward(cf(dx))
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(cl(x.detach())), _bits(ref["x"]))
+        assert torch.equal(_bits(cl(al.grad)), _bits(ref["da"]))
+        assert torch.equal(_bits(cl(bl.grad)), _bits(ref["db"]))

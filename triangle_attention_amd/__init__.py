@@ -21,12 +21,14 @@ __all__ = [
     "TriAttnError", "load_library", "tri_attn_status_string", "tri_attn_fwd_workspace_bytes",
     "tri_attn_bwd_workspace_bytes", "tri_attn_fwd", "tri_attn_bwd", "tri_attn_fwd_stages", "tri_attn_bwd_stages",
     "tri_attn_fwd_ex", "tri_attn_bwd_ex", "triangle_attention", "TRI_ATTN_MAX_N", "LAYOUTS",
-    "tri_mul_fwd", "tri_mul_bwd", "triangle_multiplication", "TRI_MUL_DIRECTIONS", "TRI_MUL_MAX_N",
+    "tri_mul_fwd", "tri_mul_bwd", "triangle_multiplication", "TRI_MUL_DIRECTIONS", "TRI_MUL_LAYOUTS",
+    "TRI_MUL_MAX_N",
 ]
 
 TRI_ATTN_MAX_N = 768
 TRI_MUL_MAX_N = 1024
 TRI_MUL_DIRECTIONS = {"outgoing": 0, "incoming": 1}
+TRI_MUL_LAYOUTS = {"channels_last": 0, "channels_first": 1}
 _lib = None
 
 
@@ -63,9 +65,9 @@ def load_library(path: str = LIB_PATH):
     lib.tri_attn_fwd_ex.restype = ctypes.c_int
     lib.tri_attn_bwd_ex.argtypes = [ctypes.c_uint, ctypes.c_int] + lib.tri_attn_bwd.argtypes
     lib.tri_attn_bwd_ex.restype = ctypes.c_int
-    lib.tri_mul_fwd.argtypes = [ctypes.c_int, i64, i64, i64, vp, vp, vp, vp]
+    lib.tri_mul_fwd.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, vp, vp, vp, vp]
     lib.tri_mul_fwd.restype = ctypes.c_int
-    lib.tri_mul_bwd.argtypes = [ctypes.c_int, i64, i64, i64, vp, vp, vp, vp, vp, vp]
+    lib.tri_mul_bwd.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, vp, vp, vp, vp, vp, vp]
     lib.tri_mul_bwd.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -151,15 +153,15 @@ def tri_attn_bwd_ex(stages, layout, B, N, H, D, q, k, v, bias, key_mask, o, lse,
                                               int(workspace_bytes), _stream(stream)))
 
 
-def tri_mul_fwd(direction, B, N, C, a, b, x, stream=None) -> int:
+def tri_mul_fwd(direction, layout, B, N, C, a, b, x, stream=None) -> int:
     """Marshal to the C entry point (include/tri_mul.h); returns the status code."""
-    return int(load_library().tri_mul_fwd(direction, B, N, C, _ptr(a), _ptr(b), _ptr(x), _stream(stream)))
+    return int(load_library().tri_mul_fwd(direction, layout, B, N, C, _ptr(a), _ptr(b), _ptr(x), _stream(stream)))
 
 
-def tri_mul_bwd(direction, B, N, C, a, b, dx, da, db, stream=None) -> int:
+def tri_mul_bwd(direction, layout, B, N, C, a, b, dx, da, db, stream=None) -> int:
     """Marshal to the C entry point (include/tri_mul.h); returns the status code."""
-    return int(load_library().tri_mul_bwd(direction, B, N, C, _ptr(a), _ptr(b), _ptr(dx), _ptr(da), _ptr(db),
-                                          _stream(stream)))
+    return int(load_library().tri_mul_bwd(direction, layout, B, N, C, _ptr(a), _ptr(b), _ptr(dx), _ptr(da),
+                                          _ptr(db), _stream(stream)))
 
 
 def _check(status: int, where: str):
@@ -240,38 +242,47 @@ def triangle_attention(q, k, v, bias, key_mask=None, residual_compensation=True,
     return _TriAttnFn.apply(q, k, v, bias, key_mask, residual_compensation, layout)
 
 
-def _mul_shape(a, b, direction):
+def _mul_shape(a, b, direction, layout):
     if direction not in TRI_MUL_DIRECTIONS:
         raise ValueError(f"direction must be one of {sorted(TRI_MUL_DIRECTIONS)}")
-    if a.dim() != 4 or a.shape[1] != a.shape[2] or tuple(b.shape) != tuple(a.shape):
-        raise ValueError("a and b must both be [B, N, N, C]")
-    return tuple(a.shape)
+    if layout not in TRI_MUL_LAYOUTS:
+        raise ValueError(f"layout must be one of {sorted(TRI_MUL_LAYOUTS)}")
+    if a.dim() != 4 or tuple(b.shape) != tuple(a.shape):
+        raise ValueError("a and b must have the same 4-dimensional shape")
+    if layout == "channels_last":
+        B, N, N2, C = a.shape
+    else:
+        B, C, N, N2 = a.shape
+    if N2 != N:
+        raise ValueError("the two pair indices must have equal extents")
+    return B, N, C
 
 
 class _TriMulFn(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, a, b, direction):
-        B, N, _, C = _mul_shape(a, b, direction)
+    def forward(ctx, a, b, direction, layout):
+        B, N, C = _mul_shape(a, b, direction, layout)
         x = torch.empty_like(a)
-        _check(tri_mul_fwd(TRI_MUL_DIRECTIONS[direction], B, N, C, a, b, x), "tri_mul_fwd")
+        _check(tri_mul_fwd(TRI_MUL_DIRECTIONS[direction], TRI_MUL_LAYOUTS[layout], B, N, C, a, b, x), "tri_mul_fwd")
         ctx.save_for_backward(a, b)
-        ctx.direction = direction
+        ctx.direction, ctx.layout, ctx.shape = direction, layout, (B, N, C)
         return x
 
     @staticmethod
     def backward(ctx, dx):
         a, b = ctx.saved_tensors
-        B, N, _, C = a.shape
+        B, N, C = ctx.shape
         da, db = torch.empty_like(a), torch.empty_like(b)
-        _check(tri_mul_bwd(TRI_MUL_DIRECTIONS[ctx.direction], B, N, C, a, b, dx.contiguous(), da, db),
-               "tri_mul_bwd")
-        return da, db, None
+        _check(tri_mul_bwd(TRI_MUL_DIRECTIONS[ctx.direction], TRI_MUL_LAYOUTS[ctx.layout], B, N, C, a, b,
+                           dx.contiguous(), da, db), "tri_mul_bwd")
+        return da, db, None, None
 
 
-def triangle_multiplication(a, b, direction="outgoing"):
+def triangle_multiplication(a, b, direction="outgoing", layout="channels_last"):
     """Cubic core of the triangle multiplicative update, differentiable in a and b.
 
-    a, b: contiguous bf16 [B, N, N, C] on one GPU (C a multiple of 8).
     outgoing: x[b,i,j,c] = sum_k a[b,i,k,c] b[b,j,k,c];  incoming: x[b,i,j,c] = sum_k a[b,k,i,c] b[b,k,j,c].
+    layout "channels_last": a, b contiguous bf16 [B, N, N, C] (C a multiple of 8);
+    layout "channels_first": [B, C, N, N] (N a multiple of 8), the faster form.
     """
-    return _TriMulFn.apply(a, b, direction)
+    return _TriMulFn.apply(a, b, direction, layout)

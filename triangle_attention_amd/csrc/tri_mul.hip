@@ -177,6 +177,154 @@ void tri_mul_kernel(const bf16* __restrict__ P, const bf16* __restrict__ Q, bf16
   }
 }
 
+// ------------------------------------------------------------------ channels-first layout
+// With a, b, x (and the gradients) laid out [B, C, N, N], each channel is a plain N x N matrix
+// and the product of one channel is an ordinary matrix product whose operands are either
+// contiguous along the reduction index t ("t-major": element (r, t) at r*N + t) or along the
+// row index r ("r-major": at t*N + r).  A work-group computes a 128 x 128 output tile of one
+// channel with 4 waves (64 x 64 each, four 32x32x16 accumulator tiles), in reduction steps of
+// 32 staged through double-buffered LDS.  Loads are 16-byte chunks along the contiguous index.
+// A t-major operand is stored [row][t] (64-byte rows, XOR-swizzled chunks) and read with
+// ds_read_b128; an r-major operand is stored as loaded, [t][row] (rows padded to 320 bytes so
+// that the transposing reads of a 16-lane group hit distinct banks) and read with
+// ds_read_b64_tr_b16, which hands each lane 4 consecutive t of its row.  The output tile goes
+// through LDS to leave as full 256-byte row segments.
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 ls16x4;
+
+constexpr int GT = 128;          // output tile edge
+constexpr int GK = 32;           // reduction step
+constexpr int kGThreads = 256;   // 4 waves
+constexpr int kRowT = GK * 2;    // bytes per row of a t-major stage tile
+constexpr int kRowR = 320;       // bytes per t-row of an r-major stage tile (256 + 64 padding)
+constexpr int kOpBytes = GK * kRowR;  // stage bytes per operand (the larger of the two forms)
+
+template <bool TMAJ>
+__device__ __forceinline__ bf16x8 frag(const char* X, int row, int t, int l) {
+  if (TMAJ) {
+    return *(const lbf16x8*)(X + row * kRowT + ((((t >> 3) ^ (row >> 2)) & 3) << 4));
+  } else {
+    // lanes of a 16-lane group share (row - l%16, t); lane u addresses t-row t + u/4, column
+    // row - l%16 + 4 (u%4) and receives rows t..t+3 of column row
+    const int u = l & 15;
+    const char* p = X + (t + (u >> 2)) * kRowR + (row - u + 4 * (u & 3)) * 2;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ls16x4*)p);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ls16x4*)(p + 4 * kRowR));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+}
+
+template <bool PT, bool QT>
+__global__ __launch_bounds__(kGThreads, 2)
+void tri_mul_cf_kernel(const bf16* __restrict__ P, const bf16* __restrict__ Q, bf16* __restrict__ out, int B, int N,
+                       int C) {
+  __shared__ __attribute__((aligned(16))) char lds[4 * kOpBytes];  // 2 stages x (P, Q)
+  const int nT = (N + GT - 1) / GT;
+  const int64_t ntiles = (int64_t)B * C * nT * nT;
+  const int64_t tile = xcd_tile(ntiles);
+  if (tile >= ntiles) return;
+  const int st = (int)(tile % nT);
+  int64_t rest = tile / nT;
+  const int rt = (int)(rest % nT);
+  const int64_t bc = rest / nT;  // b * C + c
+  const int64_t base = bc * N * N;
+  const bf16* Pc = P + base;
+  const bf16* Qc = Q + base;
+  const int r0 = rt * GT, s0 = st * GT;
+
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
+
+  // loader: 512 chunks of 16 bytes per operand and step, 2 per thread
+  u32x4 pv[2], qv[2];
+  auto load1 = [&](const bf16* X, int x0, bool tmaj, int t0, int e) -> u32x4 {
+    const int ch = tid + e * kGThreads;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    if (tmaj) {  // [128 rows][4 chunks of 8 t]
+      const int row = x0 + (ch >> 2), t = t0 + (ch & 3) * 8;
+      return (row < N && t < N) ? *(const u32x4*)(X + (int64_t)row * N + t) : z;
+    } else {     // [32 t][16 chunks of 8 rows]
+      const int t = t0 + (ch >> 4), row = x0 + (ch & 15) * 8;
+      return (row < N && t < N) ? *(const u32x4*)(X + (int64_t)t * N + row) : z;
+    }
+  };
+  auto load = [&](int t0) {
+#pragma unroll
+    for (int e = 0; e < 2; e++) {
+      pv[e] = load1(Pc, r0, PT, t0, e);
+      qv[e] = load1(Qc, s0, QT, t0, e);
+    }
+  };
+  auto put1 = [&](char* X, bool tmaj, int e, u32x4 v) {
+    const int ch = tid + e * kGThreads;
+    if (tmaj) {
+      const int row = ch >> 2, q = ch & 3;
+      *(lu32x4*)(X + row * kRowT + (((q ^ (row >> 2)) & 3) << 4)) = v;
+    } else {
+      *(lu32x4*)(X + (ch >> 4) * kRowR + (ch & 15) * 16) = v;
+    }
+  };
+  auto store = [&](int buf) {
+    char* Pt = lds + buf * 2 * kOpBytes;
+#pragma unroll
+    for (int e = 0; e < 2; e++) {
+      put1(Pt, PT, e, pv[e]);
+      put1(Pt + kOpBytes, QT, e, qv[e]);
+    }
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; i++)
+#pragma unroll
+    for (int j = 0; j < 2; j++) acc[i][j] = f32x16{};
+  const int wr = (w >> 1) * 64, wc = (w & 1) * 64;  // this wave's 64 x 64 sub-tile
+
+  const int nsteps = (N + GK - 1) / GK;
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int s = 0; s < nsteps; s++) {
+    const bool more = s + 1 < nsteps;
+    if (more) load((s + 1) * GK);
+    const char* Pt = lds + (s & 1) * 2 * kOpBytes;
+    const char* Qt = Pt + kOpBytes;
+#pragma unroll
+    for (int kk = 0; kk < 2; kk++) {
+      const int t = kk * 16 + 8 * (l >> 5);
+      const bf16x8 a0 = frag<PT>(Pt, wr + (l & 31), t, l), a1 = frag<PT>(Pt, wr + 32 + (l & 31), t, l);
+      const bf16x8 b0 = frag<QT>(Qt, wc + (l & 31), t, l), b1 = frag<QT>(Qt, wc + 32 + (l & 31), t, l);
+      acc[0][0] = mfma32(a0, b0, acc[0][0]);
+      acc[0][1] = mfma32(a0, b1, acc[0][1]);
+      acc[1][0] = mfma32(a1, b0, acc[1][0]);
+      acc[1][1] = mfma32(a1, b1, acc[1][1]);
+    }
+    if (more) store((s + 1) & 1);
+    __syncthreads();
+  }
+
+  // output tile through LDS: [128 rows][128 columns] bf16 (32 KiB)
+  lbf16* E = (lbf16*)lds;
+#pragma unroll
+  for (int i = 0; i < 2; i++)
+#pragma unroll
+    for (int j = 0; j < 2; j++)
+#pragma unroll
+      for (int e = 0; e < 16; e++) {
+        const int r = wr + i * 32 + 8 * (e >> 2) + 4 * (l >> 5) + (e & 3);
+        const int c = wc + j * 32 + (l & 31);
+        E[r * GT + c] = (bf16)acc[i][j][e];
+      }
+  __syncthreads();
+  bf16* oc = out + base;
+#pragma unroll
+  for (int e = 0; e < GT * GT / 8 / kGThreads; e++) {
+    const int ch = tid + e * kGThreads;
+    const int r = ch >> 4, c = (ch & 15) * 8;
+    if (r0 + r < N && s0 + c < N) *(u32x4*)(oc + (int64_t)(r0 + r) * N + s0 + c) = *(const lu32x4*)(E + r * GT + c);
+  }
+}
+
 unsigned grid_xcd(int64_t ntiles) { return (unsigned)((ntiles + kXcd - 1) / kXcd * kXcd); }
 
 struct Range { const void* p; int64_t n; };
@@ -186,10 +334,13 @@ bool overlap(Range x, Range y) {
 }
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-tri_attn_status check_shape(int direction, int64_t B, int64_t N, int64_t C) {
+tri_attn_status check_shape(int direction, int layout, int64_t B, int64_t N, int64_t C) {
   if (direction != TRI_MUL_OUTGOING && direction != TRI_MUL_INCOMING) return TRI_ATTN_ERROR_INVALID_VALUE;
+  if (layout != TRI_MUL_CHANNELS_LAST && layout != TRI_MUL_CHANNELS_FIRST) return TRI_ATTN_ERROR_INVALID_VALUE;
   if (B < 1 || N < 1 || C < 1) return TRI_ATTN_ERROR_INVALID_VALUE;
-  if (C % CB != 0 || C > 1024 || N > TRI_MUL_MAX_N || B > (1 << 16)) return TRI_ATTN_ERROR_UNSUPPORTED;
+  if (C > 1024 || N > TRI_MUL_MAX_N || B > (1 << 16)) return TRI_ATTN_ERROR_UNSUPPORTED;
+  if (layout == TRI_MUL_CHANNELS_LAST && C % CB != 0) return TRI_ATTN_ERROR_UNSUPPORTED;
+  if (layout == TRI_MUL_CHANNELS_FIRST && N % 8 != 0) return TRI_ATTN_ERROR_UNSUPPORTED;
   return TRI_ATTN_SUCCESS;
 }
 
@@ -202,18 +353,35 @@ tri_attn_status launch(const void* p, const void* q, void* o, int64_t B, int64_t
   return hipGetLastError() == hipSuccess ? TRI_ATTN_SUCCESS : TRI_ATTN_ERROR_LAUNCH;
 }
 
+// channels-first: OUT_c = P_c-product-Q_c with P, Q t-major (PT, QT) or r-major
+tri_attn_status launch_cf(bool pt, bool qt, const void* p, const void* q, void* o, int64_t B, int64_t N, int64_t C,
+                          hipStream_t st) {
+  const int64_t nT = (N + GT - 1) / GT;
+  const dim3 grid(grid_xcd(B * C * nT * nT)), block(kGThreads);
+  const bf16 *P = (const bf16*)p, *Q = (const bf16*)q;
+  bf16* O = (bf16*)o;
+  if (pt && qt) hipLaunchKernelGGL((tri_mul_cf_kernel<true, true>), grid, block, 0, st, P, Q, O, (int)B, (int)N, (int)C);
+  else if (pt) hipLaunchKernelGGL((tri_mul_cf_kernel<true, false>), grid, block, 0, st, P, Q, O, (int)B, (int)N, (int)C);
+  else if (qt) hipLaunchKernelGGL((tri_mul_cf_kernel<false, true>), grid, block, 0, st, P, Q, O, (int)B, (int)N, (int)C);
+  else hipLaunchKernelGGL((tri_mul_cf_kernel<false, false>), grid, block, 0, st, P, Q, O, (int)B, (int)N, (int)C);
+  return hipGetLastError() == hipSuccess ? TRI_ATTN_SUCCESS : TRI_ATTN_ERROR_LAUNCH;
+}
+
 }  // namespace
 
 extern "C" {
 
-tri_attn_status tri_mul_fwd(int direction, int64_t B, int64_t N, int64_t C, const void* a, const void* b, void* x,
-                            hipStream_t stream) {
-  const tri_attn_status st = check_shape(direction, B, N, C);
+tri_attn_status tri_mul_fwd(int direction, int layout, int64_t B, int64_t N, int64_t C, const void* a, const void* b,
+                            void* x, hipStream_t stream) {
+  const tri_attn_status st = check_shape(direction, layout, B, N, C);
   if (st != TRI_ATTN_SUCCESS) return st;
   if (!a || !b || !x) return TRI_ATTN_ERROR_INVALID_VALUE;
   const int64_t bytes = B * N * N * C * 2;
   if (overlap({x, bytes}, {a, bytes}) || overlap({x, bytes}, {b, bytes})) return TRI_ATTN_ERROR_INVALID_VALUE;
   if (!aligned16(a) || !aligned16(b) || !aligned16(x)) return TRI_ATTN_ERROR_MISALIGNED;
+  if (layout == TRI_MUL_CHANNELS_FIRST)  // outgoing: a, b t-major; incoming: both r-major
+    return direction == TRI_MUL_OUTGOING ? launch_cf(true, true, a, b, x, B, N, C, stream)
+                                         : launch_cf(false, false, a, b, x, B, N, C, stream);
   const int64_t NC = N * C;
   // outgoing: P[r=i,t=k] = a[i,k], Q[s=j,t=k] = b[j,k]; incoming: P[r=i,t=k] = a[k,i], Q = b[k,j]
   const MulStrides S = direction == TRI_MUL_OUTGOING ? MulStrides{NC, C, NC, C, NC, C}
@@ -221,9 +389,9 @@ tri_attn_status tri_mul_fwd(int direction, int64_t B, int64_t N, int64_t C, cons
   return launch(a, b, x, B, N, C, S, stream);
 }
 
-tri_attn_status tri_mul_bwd(int direction, int64_t B, int64_t N, int64_t C, const void* a, const void* b,
-                            const void* dx, void* da, void* db, hipStream_t stream) {
-  const tri_attn_status st = check_shape(direction, B, N, C);
+tri_attn_status tri_mul_bwd(int direction, int layout, int64_t B, int64_t N, int64_t C, const void* a,
+                            const void* b, const void* dx, void* da, void* db, hipStream_t stream) {
+  const tri_attn_status st = check_shape(direction, layout, B, N, C);
   if (st != TRI_ATTN_SUCCESS) return st;
   if (!a || !b || !dx || !da || !db) return TRI_ATTN_ERROR_INVALID_VALUE;
   const int64_t bytes = B * N * N * C * 2;
@@ -235,6 +403,16 @@ tri_attn_status tri_mul_bwd(int direction, int64_t B, int64_t N, int64_t C, cons
     return TRI_ATTN_ERROR_MISALIGNED;
   const int64_t NC = N * C;
   tri_attn_status r1, r2;
+  if (layout == TRI_MUL_CHANNELS_FIRST) {
+    if (direction == TRI_MUL_OUTGOING) {
+      r1 = launch_cf(true, false, dx, b, da, B, N, C, stream);   // da[i,k] = sum_j dx[i,j] b[j,k]
+      r2 = launch_cf(false, false, dx, a, db, B, N, C, stream);  // db[j,k] = sum_i dx[i,j] a[i,k]
+    } else {
+      r1 = launch_cf(true, true, b, dx, da, B, N, C, stream);    // da[k,i] = sum_j b[k,j] dx[i,j]
+      r2 = launch_cf(true, false, a, dx, db, B, N, C, stream);   // db[k,j] = sum_i a[k,i] dx[i,j]
+    }
+    return r1 != TRI_ATTN_SUCCESS ? r1 : r2;
+  }
   if (direction == TRI_MUL_OUTGOING) {
     // da[i,k] = sum_j dx[i,j] b[j,k]: P[r=i,t=j] = dx[i,j], Q[s=k,t=j] = b[j,k]
     r1 = launch(dx, b, da, B, N, C, MulStrides{NC, C, C, NC, NC, C}, stream);
