@@ -12,6 +12,10 @@ kernel) against the published dense bf16 MFMA peak, with its duration from HIP e
 recorded on the launch stream around that kernel in every timed step.
 
 Prints one JSON line.  Only one GPU is used: --gpus above 1 exits with a message.
+
+With --op trimul the same contract covers the triangle multiplication core instead: a step is
+the forward and backward of both directions (outgoing, incoming) at the trimul workload,
+credited with 2*B*N^3*C flop per forward product and twice that per backward.
 """
 from __future__ import annotations
 
@@ -32,6 +36,8 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X published dense bf16 MFMA peak (2.5 PFLOP/s)
 HEADLINE = "n768_h4_d32"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_main_traffic.json")
 KERNEL_SRC = os.path.join(ROOT, "triangle_attention_amd", "csrc", "tri_attn.hip")
+TRIMUL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "trimul_traffic.json")
+TRIMUL_SRC = os.path.join(ROOT, "triangle_attention_amd", "csrc", "tri_mul.hip")
 
 
 def _parse():
@@ -44,22 +50,27 @@ def _parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle CPU-baseline budget (0 = skip)")
     ap.add_argument("--graph", action="store_true",
                     help="also time the whole fwd+bwd step captured in one HIP graph (small-N launch latency)")
+    ap.add_argument("--op", choices=("attention", "trimul"), default="attention")
+    ap.add_argument("--trimul-workload", default="trimul_n768_c128")
+    ap.add_argument("--trimul-layout", choices=("channels_first", "channels_last"), default="channels_first")
     return ap.parse_args()
 
 
-def _src_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+def _src_hash(path: str = KERNEL_SRC) -> str:
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def _traffic(bytes_alg: float):
-    """HBM bytes per launch of the backward main kernel from committed rocprofv3 counter runs,
+def _traffic(bytes_alg: float, path: str = TRAFFIC_FILE, src: str = KERNEL_SRC, key: str | None = None):
+    """HBM bytes per launch of the dominant kernel from committed rocprofv3 counter runs,
     valid only while the kernel source is the one the counters were taken on."""
     try:
-        t = json.load(open(TRAFFIC_FILE))
+        t = json.load(open(path))
     except (OSError, ValueError):
         return None
-    if t.get("source_sha256_16") != _src_hash():
+    if t.get("source_sha256_16") != _src_hash(src):
         return None
+    if key is not None:
+        t = t.get(key) or {}
     return t.get("hbm_bytes_per_launch")
 
 
@@ -91,6 +102,114 @@ def cpu_baseline(w, inp, budget_s: float):
             "sample": f"{done} of {w.N} slices x {w.H} heads of {w.name}, fwd+bwd in FP64 ({dt:.1f} s)"}
 
 
+def trimul_cpu_baseline(a64, b64, dx64, budget_s: float):
+    """The FP64 trimul oracle as it stands, both directions fwd+bwd, one channel at a time."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    B, N, _, C = a64.shape
+    t0 = time.perf_counter()
+    done = 0
+    for c in range(C):
+        sl = (Ellipsis, slice(c, c + 1))
+        for direction in ("outgoing", "incoming"):
+            oracle.tri_mul_forward64(a64[sl], b64[sl], direction)
+            oracle.tri_mul_backward64(a64[sl], b64[sl], dx64[sl], direction)
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = 12.0 * B * N ** 3 * done
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {C} channels, both directions fwd+bwd in FP64 ({dt:.1f} s)"}
+
+
+def main_trimul(args):
+    import torch
+    import triangle_attention_amd as ta
+    from tri_synth import TRIMUL_WORKLOADS, bf16_bits_to_f64, make_pair_inputs
+
+    w = TRIMUL_WORKLOADS[args.trimul_workload]
+    B, N, C = w["B"], w["N"], w["C"]
+    inp = make_pair_inputs(B, N, C, seed=w["seed"])
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    first = args.trimul_layout == "channels_first"
+
+    def dt(bits):
+        t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+        return t.permute(0, 3, 1, 2).contiguous() if first else t
+
+    a, b, dx = dt(inp["a"]), dt(inp["b"]), dt(inp["dx"])
+    outs = {d: [torch.empty_like(a) for _ in range(3)] for d in ("outgoing", "incoming")}
+    lay = ta.TRI_MUL_LAYOUTS[args.trimul_layout]
+    stream = torch.cuda.current_stream()
+
+    def mk(direction, fwd):
+        d = ta.TRI_MUL_DIRECTIONS[direction]
+        x, da, db = outs[direction]
+
+        def call():
+            sh = torch.cuda.current_stream().cuda_stream
+            st = (ta.tri_mul_fwd(d, lay, B, N, C, a, b, x, sh) if fwd
+                  else ta.tri_mul_bwd(d, lay, B, N, C, a, b, dx, da, db, sh))
+            if st:
+                raise ta.TriAttnError(st, "tri_mul")
+        return call
+
+    calls = [mk("outgoing", True), mk("outgoing", False), mk("incoming", True), mk("incoming", False)]
+    names = ["out_fwd", "out_bwd", "in_fwd", "in_bwd"]
+    for _ in range(args.warmup):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]
+    t_wall = time.perf_counter()
+    for s in range(args.steps):
+        ev[s][0].record(stream)
+        for n_, c in enumerate(calls):
+            c()
+            ev[s][n_ + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms_per_step = ev[0][0].elapsed_time(ev[-1][-1]) / args.steps
+    stage_ms = {names[n_]: float(np.mean([ev[s][n_].elapsed_time(ev[s][n_ + 1]) for s in range(args.steps)]))
+                for n_ in range(len(calls))}
+    prod = 2.0 * B * N ** 3 * C  # flop of one product (one forward; a backward runs two)
+    flops = 2 * (prod + 2 * prod)
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    # dominant kernel: one product launch (the forward call is one launch); its algorithmic
+    # HBM bytes are the two operands read once and the output written once
+    launch_ms = 0.5 * (stage_ms["out_fwd"] + stage_ms["in_fwd"])
+    alg_bytes = 3.0 * B * N * N * C * 2
+    gbs = alg_bytes / (launch_ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s",
+                "frac": round(gbs / 8000.0, 4),
+                "traffic": _traffic(None, TRIMUL_TRAFFIC_FILE, TRIMUL_SRC, key=f"{args.trimul_layout}_fwd"),
+                "kernel": f"tri_mul {'channels-first' if first else 'channels-last'} product (one launch)",
+                "per_launch_bytes": alg_bytes, "per_launch_flop": prod, "avg_launch_ms": round(launch_ms, 4),
+                "mfma_tflops": round(prod / (launch_ms * 1e-3) / 1e12, 1),
+                "mfma_frac": round(prod / (launch_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    cpu = None
+    if args.cpu_seconds > 0:
+        a64, b64, dx64 = (bf16_bits_to_f64(inp[n]) for n in ("a", "b", "dx"))
+        cpu = trimul_cpu_baseline(a64, b64, dx64, args.cpu_seconds)
+    out = {
+        "metric": "triangle-multiplication core fwd+bwd TFLOPS (outgoing + incoming), 1 GPU",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": args.trimul_workload, "B": B, "N": N, "C": C, "layout": args.trimul_layout},
+        "pct_of_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "stages_ms": {k_: round(v_, 4) for k_, v_ in stage_ms.items()},
+        "wall_s_timed_region": round(wall, 4), "roofline": roofline, "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = _parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -98,6 +217,9 @@ def main():
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}, "
               f"WORLD_SIZE {world}).", file=sys.stderr)
         sys.exit(2)
+    if args.op == "trimul":
+        main_trimul(args)
+        return
 
     import torch
     import triangle_attention_amd as ta

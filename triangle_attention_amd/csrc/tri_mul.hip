@@ -185,10 +185,11 @@ void tri_mul_kernel(const bf16* __restrict__ P, const bf16* __restrict__ Q, bf16
 // channel with 4 waves (64 x 64 each, four 32x32x16 accumulator tiles), in reduction steps of
 // 32 staged through double-buffered LDS.  Loads are 16-byte chunks along the contiguous index.
 // A t-major operand is stored [row][t] (64-byte rows, XOR-swizzled chunks) and read with
-// ds_read_b128; an r-major operand is stored as loaded, [t][row] (rows padded to 320 bytes so
-// that the transposing reads of a 16-lane group hit distinct banks) and read with
-// ds_read_b64_tr_b16, which hands each lane 4 consecutive t of its row.  The output tile goes
-// through LDS to leave as full 256-byte row segments.
+// ds_read_b128; an r-major operand is stored as loaded, [t][row] (256-byte rows whose 64-byte
+// blocks are XOR-swizzled by t % 4, so that the transposing reads of 32 lanes, 4 t-rows x 64
+// bytes, hit distinct banks) and read with ds_read_b64_tr_b16, which hands each lane 4
+// consecutive t of its row.  The output tile goes through LDS to leave as full 256-byte row
+// segments.
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 ls16x4;
@@ -197,7 +198,7 @@ constexpr int GT = 128;          // output tile edge
 constexpr int GK = 32;           // reduction step
 constexpr int kGThreads = 256;   // 4 waves
 constexpr int kRowT = GK * 2;    // bytes per row of a t-major stage tile
-constexpr int kRowR = 320;       // bytes per t-row of an r-major stage tile (256 + 64 padding)
+constexpr int kRowR = 256;       // bytes per t-row of an r-major stage tile
 constexpr int kOpBytes = GK * kRowR;  // stage bytes per operand (the larger of the two forms)
 
 template <bool TMAJ>
@@ -208,15 +209,17 @@ __device__ __forceinline__ bf16x8 frag(const char* X, int row, int t, int l) {
     // lanes of a 16-lane group share (row - l%16, t); lane u addresses t-row t + u/4, column
     // row - l%16 + 4 (u%4) and receives rows t..t+3 of column row
     const int u = l & 15;
-    const char* p = X + (t + (u >> 2)) * kRowR + (row - u + 4 * (u & 3)) * 2;
+    const int tt = t + (u >> 2), cb = (row - u + 4 * (u & 3)) * 2;  // t-row, byte in the row
+    const char* p = X + tt * kRowR + (cb ^ ((tt & 3) << 6));
+    const char* p4 = X + (tt + 4) * kRowR + (cb ^ (((tt + 4) & 3) << 6));
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ls16x4*)p);
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ls16x4*)(p + 4 * kRowR));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ls16x4*)p4);
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   }
 }
 
 template <bool PT, bool QT>
-__global__ __launch_bounds__(kGThreads, 2)
+__global__ __launch_bounds__(kGThreads, 4)
 void tri_mul_cf_kernel(const bf16* __restrict__ P, const bf16* __restrict__ Q, bf16* __restrict__ out, int B, int N,
                        int C) {
   __shared__ __attribute__((aligned(16))) char lds[4 * kOpBytes];  // 2 stages x (P, Q)
@@ -261,7 +264,8 @@ void tri_mul_cf_kernel(const bf16* __restrict__ P, const bf16* __restrict__ Q, b
       const int row = ch >> 2, q = ch & 3;
       *(lu32x4*)(X + row * kRowT + (((q ^ (row >> 2)) & 3) << 4)) = v;
     } else {
-      *(lu32x4*)(X + (ch >> 4) * kRowR + (ch & 15) * 16) = v;
+      const int tt = ch >> 4;
+      *(lu32x4*)(X + tt * kRowR + (((ch & 15) * 16) ^ ((tt & 3) << 6))) = v;
     }
   };
   auto store = [&](int buf) {

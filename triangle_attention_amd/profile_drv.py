@@ -2,6 +2,8 @@
 
   python3 -m triangle_attention_amd.profile_drv attn [workload] [reps]
       forward + backward of a synthetic workload through the C ABI, `reps` times
+  python3 -m triangle_attention_amd.profile_drv mul [workload] [layout] [reps]
+      triangle multiplication core, both directions, forward + backward, `reps` times
   python3 -m triangle_attention_amd.profile_drv copy [mib] [reps]
       a plain device-to-device copy of `mib` MiB (torch's copy kernel), used to
       calibrate FETCH_SIZE / WRITE_SIZE against a known byte count
@@ -38,6 +40,32 @@ def _attn(name: str, reps: int):
     print(f"attn {name} x{reps} done", flush=True)
 
 
+def _mul(name: str, layout: str, reps: int):
+    import numpy as np
+    import torch
+
+    import triangle_attention_amd as ta
+    from tri_synth import TRIMUL_WORKLOADS, make_pair_inputs
+
+    w = TRIMUL_WORKLOADS[name]
+    B, N, C = w["B"], w["N"], w["C"]
+    inp = make_pair_inputs(B, N, C, seed=w["seed"])
+
+    def dev(bits):
+        t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+        return t.permute(0, 3, 1, 2).contiguous() if layout == "channels_first" else t
+
+    a, b, dx = dev(inp["a"]), dev(inp["b"]), dev(inp["dx"])
+    x, da, db = torch.empty_like(a), torch.empty_like(a), torch.empty_like(a)
+    lay = ta.TRI_MUL_LAYOUTS[layout]
+    for _ in range(reps):
+        for d in (0, 1):
+            assert ta.tri_mul_fwd(d, lay, B, N, C, a, b, x) == 0
+            assert ta.tri_mul_bwd(d, lay, B, N, C, a, b, dx, da, db) == 0
+    torch.cuda.synchronize()
+    print(f"mul {name} {layout} x{reps} done", flush=True)
+
+
 def _copy(mib: int, reps: int):
     import torch
 
@@ -53,6 +81,9 @@ def main(argv):
     what = argv[1] if len(argv) > 1 else "attn"
     if what == "copy":
         _copy(int(argv[2]) if len(argv) > 2 else 256, int(argv[3]) if len(argv) > 3 else 3)
+    elif what == "mul":
+        _mul(argv[2] if len(argv) > 2 else "trimul_n768_c128", argv[3] if len(argv) > 3 else "channels_first",
+             int(argv[4]) if len(argv) > 4 else 2)
     else:
         _attn(argv[2] if len(argv) > 2 else "n768_h4_d32", int(argv[3]) if len(argv) > 3 else 3)
 
