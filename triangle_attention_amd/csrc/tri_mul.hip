@@ -183,7 +183,8 @@ void tri_mul_kernel(const bf16* __restrict__ P, const bf16* __restrict__ Q, bf16
 // contiguous along the reduction index t ("t-major": element (r, t) at r*N + t) or along the
 // row index r ("r-major": at t*N + r).  A work-group computes a 128 x 128 output tile of one
 // channel with 4 waves (64 x 64 each, four 32x32x16 accumulator tiles), in reduction steps of
-// 32 staged through double-buffered LDS.  Loads are 16-byte chunks along the contiguous index.
+// 32 staged through a three-stage LDS ring filled by direct-to-LDS loads issued two steps
+// ahead.  Loads are 16-byte chunks along the contiguous index.
 // A t-major operand is stored [row][t] (64-byte rows, XOR-swizzled chunks) and read with
 // ds_read_b128; an r-major operand is stored as loaded, [t][row] (256-byte rows whose 64-byte
 // blocks are XOR-swizzled by t % 4, so that the transposing reads of 32 lanes, 4 t-rows x 64
@@ -218,11 +219,68 @@ __device__ __forceinline__ bf16x8 frag(const char* X, int row, int t, int l) {
   }
 }
 
+// Raw buffer descriptor over [base, base + bytes): loads at or past the end return zeros.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 raw_rsrc(const void* base, int bytes) {
+  const unsigned long long a = (unsigned long long)(uintptr_t)base;
+  i32x4 r = {__builtin_amdgcn_readfirstlane((int)(unsigned)a),
+             __builtin_amdgcn_readfirstlane((int)((unsigned)(a >> 32) & 0xFFFFu)),
+             __builtin_amdgcn_readfirstlane(bytes), 0x00020000};
+  return r;
+}
+// 16 bytes per lane from the buffer straight into LDS: lane l's bytes land at lds_wave_base + 16 l.
+// The statement is invisible to the compiler's wait-count tracking: the kernel waits for these
+// loads itself (vmcnt) before the barrier that publishes them.  It carries its own wait states
+// (one after the M0 write, five before a load whose scalar operands a vector instruction may
+// have just written).
+__device__ __forceinline__ void dma16(i32x4 rsrc, unsigned voff, int soff, unsigned lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %3\n\ts_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soff)),
+                  "s"(__builtin_amdgcn_readfirstlane(lds_wave_base)) : "memory", "m0");
+}
+// Barrier that orders LDS accesses only (it does not wait for the loads still in flight).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+constexpr unsigned kOob = 0x80000000u;  // a per-lane offset past any buffer: the load returns zeros
+
+// Per-lane offsets of one operand's stage loads.  Each wave issues two 1 KiB loads per operand
+// and step (lane l of load e fills 16-byte unit u = (2 w + e) * 64 + l of the stage tile), so the
+// lane decides which global chunk lands in that unit: the swizzled layouts are produced by the
+// choice of source.  t-major tile [128 rows][4 units]: unit u is row u/4, swizzled chunk u%4;
+// r-major tile [32 t][16 units]: unit u is t-row u/16, swizzled chunk u%16.
+struct StageLane {
+  unsigned off;  // byte offset of this lane's chunk relative to the step's tile origin
+  int t;         // reduction index of the chunk relative to the step (t-major) or t-row (r-major)
+  bool rok;      // the chunk's rows lie inside the matrix (r-major: columns < N)
+};
+template <bool TMAJ>
+__device__ __forceinline__ StageLane stage_lane(int u, int N, int x0) {
+  StageLane s;
+  if (TMAJ) {
+    const int row = u >> 2, q = (u & 3) ^ ((row >> 2) & 3);
+    s.off = (unsigned)((row * N + q * 8) * 2);
+    s.t = q * 8;
+    s.rok = true;  // rows past N lie past the buffer's end
+  } else {
+    const int t = u >> 4, q = (u & 15) ^ ((t & 3) << 2);
+    s.off = (unsigned)((t * N + q * 8) * 2);
+    s.t = t;
+    s.rok = x0 + q * 8 < N;
+  }
+  return s;
+}
+
 template <bool PT, bool QT>
-__global__ __launch_bounds__(kGThreads, 4)
+__global__ __launch_bounds__(kGThreads, 3)
 void tri_mul_cf_kernel(const bf16* __restrict__ P, const bf16* __restrict__ Q, bf16* __restrict__ out, int B, int N,
                        int C) {
-  __shared__ __attribute__((aligned(16))) char lds[4 * kOpBytes];  // 2 stages x (P, Q)
+  constexpr int kStages = 3;                 // loads run two steps ahead of the products
+  constexpr int kStageB = 2 * GK * kRowR;   // P and Q tiles of one step (8 KiB each)
+  __shared__ __attribute__((aligned(16))) char lds[kStages * kStageB];
   const int nT = (N + GT - 1) / GT;
   const int64_t ntiles = (int64_t)B * C * nT * nT;
   const int64_t tile = xcd_tile(ntiles);
@@ -232,48 +290,30 @@ void tri_mul_cf_kernel(const bf16* __restrict__ P, const bf16* __restrict__ Q, b
   const int rt = (int)(rest % nT);
   const int64_t bc = rest / nT;  // b * C + c
   const int64_t base = bc * N * N;
-  const bf16* Pc = P + base;
-  const bf16* Qc = Q + base;
   const int r0 = rt * GT, s0 = st * GT;
 
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
-
-  // loader: 512 chunks of 16 bytes per operand and step, 2 per thread
-  u32x4 pv[2], qv[2];
-  auto load1 = [&](const bf16* X, int x0, bool tmaj, int t0, int e) -> u32x4 {
-    const int ch = tid + e * kGThreads;
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    if (tmaj) {  // [128 rows][4 chunks of 8 t]
-      const int row = x0 + (ch >> 2), t = t0 + (ch & 3) * 8;
-      return (row < N && t < N) ? *(const u32x4*)(X + (int64_t)row * N + t) : z;
-    } else {     // [32 t][16 chunks of 8 rows]
-      const int t = t0 + (ch >> 4), row = x0 + (ch & 15) * 8;
-      return (row < N && t < N) ? *(const u32x4*)(X + (int64_t)t * N + row) : z;
-    }
-  };
-  auto load = [&](int t0) {
+  const i32x4 rp = raw_rsrc(P + base, N * N * 2), rq = raw_rsrc(Q + base, N * N * 2);
+  const unsigned lds0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(const __attribute__((address_space(3))) char*)lds);
+  StageLane lp[2], lq[2];
+#pragma unroll
+  for (int e = 0; e < 2; e++) {
+    lp[e] = stage_lane<PT>((2 * w + e) * 64 + l, N, r0);
+    lq[e] = stage_lane<QT>((2 * w + e) * 64 + l, N, s0);
+  }
+  // issue the loads of reduction step s into stage buffer s % 3
+  auto issue = [&](int s) {
+    const int t0 = s * GK;
+    const unsigned dst = lds0 + (s % kStages) * kStageB + (2 * w) * 1024;
+    // tile origin: (row x0, t0) of a t-major operand, (t-row t0, column x0) of an r-major one
+    const int sp = PT ? (r0 * N + t0) * 2 : (t0 * N + r0) * 2;
+    const int sq = QT ? (s0 * N + t0) * 2 : (t0 * N + s0) * 2;
 #pragma unroll
     for (int e = 0; e < 2; e++) {
-      pv[e] = load1(Pc, r0, PT, t0, e);
-      qv[e] = load1(Qc, s0, QT, t0, e);
-    }
-  };
-  auto put1 = [&](char* X, bool tmaj, int e, u32x4 v) {
-    const int ch = tid + e * kGThreads;
-    if (tmaj) {
-      const int row = ch >> 2, q = ch & 3;
-      *(lu32x4*)(X + row * kRowT + (((q ^ (row >> 2)) & 3) << 4)) = v;
-    } else {
-      const int tt = ch >> 4;
-      *(lu32x4*)(X + tt * kRowR + (((ch & 15) * 16) ^ ((tt & 3) << 6))) = v;
-    }
-  };
-  auto store = [&](int buf) {
-    char* Pt = lds + buf * 2 * kOpBytes;
-#pragma unroll
-    for (int e = 0; e < 2; e++) {
-      put1(Pt, PT, e, pv[e]);
-      put1(Pt + kOpBytes, QT, e, qv[e]);
+      const bool pok = PT ? t0 + lp[e].t < N : lp[e].rok;
+      const bool qok = QT ? t0 + lq[e].t < N : lq[e].rok;
+      dma16(rp, pok ? lp[e].off : kOob, sp, dst + e * 1024);
+      dma16(rq, qok ? lq[e].off : kOob, sq, dst + GK * kRowR + e * 1024);
     }
   };
 
@@ -285,14 +325,16 @@ void tri_mul_cf_kernel(const bf16* __restrict__ P, const bf16* __restrict__ Q, b
   const int wr = (w >> 1) * 64, wc = (w & 1) * 64;  // this wave's 64 x 64 sub-tile
 
   const int nsteps = (N + GK - 1) / GK;
-  load(0);
-  store(0);
-  __syncthreads();
+  issue(0);
+  if (nsteps > 1) issue(1);
+  if (nsteps > 1) __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4): step 0's four loads have landed
+  else __builtin_amdgcn_s_waitcnt(0x0F70);
+  lds_barrier();
   for (int s = 0; s < nsteps; s++) {
-    const bool more = s + 1 < nsteps;
-    if (more) load((s + 1) * GK);
-    const char* Pt = lds + (s & 1) * 2 * kOpBytes;
-    const char* Qt = Pt + kOpBytes;
+    // stage (s+2) % 3 was last read in step s-1, which every wave finished before the barrier
+    if (s + 2 < nsteps) issue(s + 2);
+    const char* Pt = lds + (s % kStages) * kStageB;
+    const char* Qt = Pt + GK * kRowR;
 #pragma unroll
     for (int kk = 0; kk < 2; kk++) {
       const int t = kk * 16 + 8 * (l >> 5);
@@ -303,11 +345,13 @@ void tri_mul_cf_kernel(const bf16* __restrict__ P, const bf16* __restrict__ Q, b
       acc[1][0] = mfma32(a1, b0, acc[1][0]);
       acc[1][1] = mfma32(a1, b1, acc[1][1]);
     }
-    if (more) store((s + 1) & 1);
-    __syncthreads();
+    // step s+1's loads have landed for this wave once only step s+2's (if issued) are pending
+    if (s + 2 < nsteps) __builtin_amdgcn_s_waitcnt(0x0F74);
+    else __builtin_amdgcn_s_waitcnt(0x0F70);
+    lds_barrier();
   }
 
-  // output tile through LDS: [128 rows][128 columns] bf16 (32 KiB)
+  // output tile through LDS: [128 rows][128 columns] bf16 (32 KiB; no load is in flight)
   lbf16* E = (lbf16*)lds;
 #pragma unroll
   for (int i = 0; i < 2; i++)
