@@ -181,28 +181,30 @@ void tri_mul_kernel(const bf16* __restrict__ P, const bf16* __restrict__ Q, bf16
 // With a, b, x (and the gradients) laid out [B, C, N, N], each channel is a plain N x N matrix
 // and the product of one channel is an ordinary matrix product whose operands are either
 // contiguous along the reduction index t ("t-major": element (r, t) at r*N + t) or along the
-// row index r ("r-major": at t*N + r).  A work-group computes a 128 x 128 output tile of one
-// channel with 4 waves (64 x 64 each, four 32x32x16 accumulator tiles), in reduction steps of
+// row index r ("r-major": at t*N + r).  A work-group computes a 128 x 256 output tile of one
+// channel with 4 waves (64 x 128 each, eight 32x32x16 accumulator tiles: six operand reads per
+// eight products), in reduction steps of
 // 32 staged through a three-stage LDS ring filled by direct-to-LDS loads issued two steps
 // ahead.  Loads are 16-byte chunks along the contiguous index.
 // A t-major operand is stored [row][t] (64-byte rows, XOR-swizzled chunks) and read with
 // ds_read_b128; an r-major operand is stored as loaded, [t][row] (256-byte rows whose 64-byte
 // blocks are XOR-swizzled by t % 4, so that the transposing reads of 32 lanes, 4 t-rows x 64
 // bytes, hit distinct banks) and read with ds_read_b64_tr_b16, which hands each lane 4
-// consecutive t of its row.  The output tile goes through LDS to leave as full 256-byte row
+// consecutive t of its row.  The output tile goes through LDS to leave as full 512-byte row
 // segments.
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 ls16x4;
 
-constexpr int GT = 128;          // output tile edge
+constexpr int GR = 128;          // output tile rows (P side)
+constexpr int GS = 256;          // output tile columns (Q side)
 constexpr int GK = 32;           // reduction step
-constexpr int kGThreads = 256;   // 4 waves
+constexpr int kGThreads = 256;   // 4 waves, 64 x 128 outputs each
 constexpr int kRowT = GK * 2;    // bytes per row of a t-major stage tile
-constexpr int kRowR = 256;       // bytes per t-row of an r-major stage tile
-constexpr int kOpBytes = GK * kRowR;  // stage bytes per operand (the larger of the two forms)
 
-template <bool TMAJ>
+// Operand fragment for a 32x32x16 product: the 8 consecutive t (from t) of tile row `row`.
+// W is the operand's tile width (rows of a t-major tile, columns of an r-major one).
+template <bool TMAJ, int W>
 __device__ __forceinline__ bf16x8 frag(const char* X, int row, int t, int l) {
   if (TMAJ) {
     return *(const lbf16x8*)(X + row * kRowT + ((((t >> 3) ^ (row >> 2)) & 3) << 4));
@@ -211,8 +213,8 @@ __device__ __forceinline__ bf16x8 frag(const char* X, int row, int t, int l) {
     // row - l%16 + 4 (u%4) and receives rows t..t+3 of column row
     const int u = l & 15;
     const int tt = t + (u >> 2), cb = (row - u + 4 * (u & 3)) * 2;  // t-row, byte in the row
-    const char* p = X + tt * kRowR + (cb ^ ((tt & 3) << 6));
-    const char* p4 = X + (tt + 4) * kRowR + (cb ^ (((tt + 4) & 3) << 6));
+    const char* p = X + tt * (W * 2) + (cb ^ ((tt & 3) << 6));
+    const char* p4 = X + (tt + 4) * (W * 2) + (cb ^ (((tt + 4) & 3) << 6));
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ls16x4*)p);
     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ls16x4*)p4);
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -247,17 +249,17 @@ __device__ __forceinline__ void lds_barrier() {
 }
 constexpr unsigned kOob = 0x80000000u;  // a per-lane offset past any buffer: the load returns zeros
 
-// Per-lane offsets of one operand's stage loads.  Each wave issues two 1 KiB loads per operand
-// and step (lane l of load e fills 16-byte unit u = (2 w + e) * 64 + l of the stage tile), so the
-// lane decides which global chunk lands in that unit: the swizzled layouts are produced by the
-// choice of source.  t-major tile [128 rows][4 units]: unit u is row u/4, swizzled chunk u%4;
-// r-major tile [32 t][16 units]: unit u is t-row u/16, swizzled chunk u%16.
+// Per-lane offsets of one operand's stage loads.  The waves issue 1 KiB loads (lane l of load i
+// fills 16-byte unit u = 64 i + l of the stage tile), so each lane decides which global chunk
+// lands in that unit: the swizzled layouts come from the choice of source.  t-major tile
+// [W rows][4 units]: unit u is row u/4, swizzled chunk u%4; r-major tile [32 t][W/8 units]:
+// unit u is t-row u/(W/8), swizzled chunk u%(W/8) (64-byte blocks XOR t%4).
 struct StageLane {
   unsigned off;  // byte offset of this lane's chunk relative to the step's tile origin
-  int t;         // reduction index of the chunk relative to the step (t-major) or t-row (r-major)
-  bool rok;      // the chunk's rows lie inside the matrix (r-major: columns < N)
+  int t;         // reduction index of the chunk relative to the step (t-major only)
+  bool rok;      // r-major: the chunk's columns lie inside the matrix
 };
-template <bool TMAJ>
+template <bool TMAJ, int W>
 __device__ __forceinline__ StageLane stage_lane(int u, int N, int x0) {
   StageLane s;
   if (TMAJ) {
@@ -266,7 +268,8 @@ __device__ __forceinline__ StageLane stage_lane(int u, int N, int x0) {
     s.t = q * 8;
     s.rok = true;  // rows past N lie past the buffer's end
   } else {
-    const int t = u >> 4, q = (u & 15) ^ ((t & 3) << 2);
+    constexpr int U = W / 8;  // units per t-row
+    const int t = u / U, q = (u % U) ^ ((t & 3) << 2);
     s.off = (unsigned)((t * N + q * 8) * 2);
     s.t = t;
     s.rok = x0 + q * 8 < N;
@@ -275,101 +278,108 @@ __device__ __forceinline__ StageLane stage_lane(int u, int N, int x0) {
 }
 
 template <bool PT, bool QT>
-__global__ __launch_bounds__(kGThreads, 3)
+__global__ __launch_bounds__(kGThreads, 2)
 void tri_mul_cf_kernel(const bf16* __restrict__ P, const bf16* __restrict__ Q, bf16* __restrict__ out, int B, int N,
                        int C) {
-  constexpr int kStages = 3;                 // loads run two steps ahead of the products
-  constexpr int kStageB = 2 * GK * kRowR;   // P and Q tiles of one step (8 KiB each)
+  constexpr int kStages = 3;                       // loads run two steps ahead of the products
+  constexpr int kPB = GR * GK * 2, kQB = GS * GK * 2;  // stage bytes of P (8 KiB) and Q (16 KiB)
+  constexpr int kStageB = kPB + kQB;
+  constexpr int LP = kPB / 1024 / 4, LQ = kQB / 1024 / 4;  // 1 KiB loads per wave and step
   __shared__ __attribute__((aligned(16))) char lds[kStages * kStageB];
-  const int nT = (N + GT - 1) / GT;
-  const int64_t ntiles = (int64_t)B * C * nT * nT;
+  const int nR = (N + GR - 1) / GR, nS = (N + GS - 1) / GS;
+  const int64_t ntiles = (int64_t)B * C * nR * nS;
   const int64_t tile = xcd_tile(ntiles);
   if (tile >= ntiles) return;
-  const int st = (int)(tile % nT);
-  int64_t rest = tile / nT;
-  const int rt = (int)(rest % nT);
-  const int64_t bc = rest / nT;  // b * C + c
+  const int st = (int)(tile % nS);
+  int64_t rest = tile / nS;
+  const int rt = (int)(rest % nR);
+  const int64_t bc = rest / nR;  // b * C + c
   const int64_t base = bc * N * N;
-  const int r0 = rt * GT, s0 = st * GT;
+  const int r0 = rt * GR, s0 = st * GS;
 
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
   const i32x4 rp = raw_rsrc(P + base, N * N * 2), rq = raw_rsrc(Q + base, N * N * 2);
   const unsigned lds0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(const __attribute__((address_space(3))) char*)lds);
-  StageLane lp[2], lq[2];
+  StageLane lp[LP], lq[LQ];
 #pragma unroll
-  for (int e = 0; e < 2; e++) {
-    lp[e] = stage_lane<PT>((2 * w + e) * 64 + l, N, r0);
-    lq[e] = stage_lane<QT>((2 * w + e) * 64 + l, N, s0);
-  }
+  for (int e = 0; e < LP; e++) lp[e] = stage_lane<PT, GR>((LP * w + e) * 64 + l, N, r0);
+#pragma unroll
+  for (int e = 0; e < LQ; e++) lq[e] = stage_lane<QT, GS>((LQ * w + e) * 64 + l, N, s0);
   // issue the loads of reduction step s into stage buffer s % 3
   auto issue = [&](int s) {
     const int t0 = s * GK;
-    const unsigned dst = lds0 + (s % kStages) * kStageB + (2 * w) * 1024;
+    const unsigned dst = lds0 + (s % kStages) * kStageB;
     // tile origin: (row x0, t0) of a t-major operand, (t-row t0, column x0) of an r-major one
     const int sp = PT ? (r0 * N + t0) * 2 : (t0 * N + r0) * 2;
     const int sq = QT ? (s0 * N + t0) * 2 : (t0 * N + s0) * 2;
 #pragma unroll
-    for (int e = 0; e < 2; e++) {
-      const bool pok = PT ? t0 + lp[e].t < N : lp[e].rok;
-      const bool qok = QT ? t0 + lq[e].t < N : lq[e].rok;
-      dma16(rp, pok ? lp[e].off : kOob, sp, dst + e * 1024);
-      dma16(rq, qok ? lq[e].off : kOob, sq, dst + GK * kRowR + e * 1024);
+    for (int e = 0; e < LP; e++) {
+      const bool ok = PT ? t0 + lp[e].t < N : lp[e].rok;
+      dma16(rp, ok ? lp[e].off : kOob, sp, dst + (LP * w + e) * 1024);
+    }
+#pragma unroll
+    for (int e = 0; e < LQ; e++) {
+      const bool ok = QT ? t0 + lq[e].t < N : lq[e].rok;
+      dma16(rq, ok ? lq[e].off : kOob, sq, dst + kPB + (LQ * w + e) * 1024);
     }
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[2][4];
 #pragma unroll
   for (int i = 0; i < 2; i++)
 #pragma unroll
-    for (int j = 0; j < 2; j++) acc[i][j] = f32x16{};
-  const int wr = (w >> 1) * 64, wc = (w & 1) * 64;  // this wave's 64 x 64 sub-tile
+    for (int j = 0; j < 4; j++) acc[i][j] = f32x16{};
+  const int wr = (w >> 1) * 64, wc = (w & 1) * 128;  // this wave's 64 x 128 sub-tile
 
   const int nsteps = (N + GK - 1) / GK;
   issue(0);
   if (nsteps > 1) issue(1);
-  if (nsteps > 1) __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4): step 0's four loads have landed
+  if (nsteps > 1) __builtin_amdgcn_s_waitcnt(0x0F70 | (LP + LQ));  // step 0's loads have landed
   else __builtin_amdgcn_s_waitcnt(0x0F70);
   lds_barrier();
   for (int s = 0; s < nsteps; s++) {
     // stage (s+2) % 3 was last read in step s-1, which every wave finished before the barrier
     if (s + 2 < nsteps) issue(s + 2);
     const char* Pt = lds + (s % kStages) * kStageB;
-    const char* Qt = Pt + GK * kRowR;
+    const char* Qt = Pt + kPB;
 #pragma unroll
     for (int kk = 0; kk < 2; kk++) {
       const int t = kk * 16 + 8 * (l >> 5);
-      const bf16x8 a0 = frag<PT>(Pt, wr + (l & 31), t, l), a1 = frag<PT>(Pt, wr + 32 + (l & 31), t, l);
-      const bf16x8 b0 = frag<QT>(Qt, wc + (l & 31), t, l), b1 = frag<QT>(Qt, wc + 32 + (l & 31), t, l);
-      acc[0][0] = mfma32(a0, b0, acc[0][0]);
-      acc[0][1] = mfma32(a0, b1, acc[0][1]);
-      acc[1][0] = mfma32(a1, b0, acc[1][0]);
-      acc[1][1] = mfma32(a1, b1, acc[1][1]);
+      bf16x8 a[2], bq[4];
+#pragma unroll
+      for (int i = 0; i < 2; i++) a[i] = frag<PT, GR>(Pt, wr + 32 * i + (l & 31), t, l);
+#pragma unroll
+      for (int j = 0; j < 4; j++) bq[j] = frag<QT, GS>(Qt, wc + 32 * j + (l & 31), t, l);
+#pragma unroll
+      for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) acc[i][j] = mfma32(a[i], bq[j], acc[i][j]);
     }
     // step s+1's loads have landed for this wave once only step s+2's (if issued) are pending
-    if (s + 2 < nsteps) __builtin_amdgcn_s_waitcnt(0x0F74);
+    if (s + 2 < nsteps) __builtin_amdgcn_s_waitcnt(0x0F70 | (LP + LQ));
     else __builtin_amdgcn_s_waitcnt(0x0F70);
     lds_barrier();
   }
 
-  // output tile through LDS: [128 rows][128 columns] bf16 (32 KiB; no load is in flight)
+  // output tile through LDS: [128 rows][256 columns] bf16 (64 KiB; no load is in flight)
   lbf16* E = (lbf16*)lds;
 #pragma unroll
   for (int i = 0; i < 2; i++)
 #pragma unroll
-    for (int j = 0; j < 2; j++)
+    for (int j = 0; j < 4; j++)
 #pragma unroll
       for (int e = 0; e < 16; e++) {
         const int r = wr + i * 32 + 8 * (e >> 2) + 4 * (l >> 5) + (e & 3);
         const int c = wc + j * 32 + (l & 31);
-        E[r * GT + c] = (bf16)acc[i][j][e];
+        E[r * GS + c] = (bf16)acc[i][j][e];
       }
   __syncthreads();
   bf16* oc = out + base;
 #pragma unroll
-  for (int e = 0; e < GT * GT / 8 / kGThreads; e++) {
+  for (int e = 0; e < GR * GS / 8 / kGThreads; e++) {
     const int ch = tid + e * kGThreads;
-    const int r = ch >> 4, c = (ch & 15) * 8;
-    if (r0 + r < N && s0 + c < N) *(u32x4*)(oc + (int64_t)(r0 + r) * N + s0 + c) = *(const lu32x4*)(E + r * GT + c);
+    const int r = ch / (GS / 8), c = (ch % (GS / 8)) * 8;
+    if (r0 + r < N && s0 + c < N) *(u32x4*)(oc + (int64_t)(r0 + r) * N + s0 + c) = *(const lu32x4*)(E + r * GS + c);
   }
 }
 
@@ -404,8 +414,7 @@ tri_attn_status launch(const void* p, const void* q, void* o, int64_t B, int64_t
 // channels-first: OUT_c = P_c-product-Q_c with P, Q t-major (PT, QT) or r-major
 tri_attn_status launch_cf(bool pt, bool qt, const void* p, const void* q, void* o, int64_t B, int64_t N, int64_t C,
                           hipStream_t st) {
-  const int64_t nT = (N + GT - 1) / GT;
-  const dim3 grid(grid_xcd(B * C * nT * nT)), block(kGThreads);
+  const dim3 grid(grid_xcd(B * C * ((N + GR - 1) / GR) * ((N + GS - 1) / GS))), block(kGThreads);
   const bf16 *P = (const bf16*)p, *Q = (const bf16*)q;
   bf16* O = (bf16*)o;
   if (pt && qt) hipLaunchKernelGGL((tri_mul_cf_kernel<true, true>), grid, block, 0, st, P, Q, O, (int)B, (int)N, (int)C);
