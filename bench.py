@@ -53,6 +53,8 @@ def _parse():
     ap.add_argument("--op", choices=("attention", "trimul"), default="attention")
     ap.add_argument("--trimul-workload", default="trimul_n768_c128")
     ap.add_argument("--trimul-layout", choices=("channels_first", "channels_last"), default="channels_first")
+    ap.add_argument("--trimul-direct", action="store_true",
+                    help="channels last without a workspace (the in-place kernel instead of the layout change)")
     return ap.parse_args()
 
 
@@ -146,6 +148,8 @@ def main_trimul(args):
     a, b, dx = dt(inp["a"]), dt(inp["b"]), dt(inp["dx"])
     outs = {d: [torch.empty_like(a) for _ in range(3)] for d in ("outgoing", "incoming")}
     lay = ta.TRI_MUL_LAYOUTS[args.trimul_layout]
+    nws = 0 if args.trimul_direct else ta.tri_mul_workspace_bytes(lay, B, N, C)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
     stream = torch.cuda.current_stream()
 
     def mk(direction, fwd):
@@ -154,8 +158,8 @@ def main_trimul(args):
 
         def call():
             sh = torch.cuda.current_stream().cuda_stream
-            st = (ta.tri_mul_fwd(d, lay, B, N, C, a, b, x, sh) if fwd
-                  else ta.tri_mul_bwd(d, lay, B, N, C, a, b, dx, da, db, sh))
+            st = (ta.tri_mul_fwd(d, lay, B, N, C, a, b, x, ws, nws, stream=sh) if fwd
+                  else ta.tri_mul_bwd(d, lay, B, N, C, a, b, dx, da, db, ws, nws, stream=sh))
             if st:
                 raise ta.TriAttnError(st, "tri_mul")
         return call
@@ -202,7 +206,8 @@ def main_trimul(args):
         "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": args.trimul_workload, "B": B, "N": N, "C": C, "layout": args.trimul_layout},
+        "config": {"workload": args.trimul_workload, "B": B, "N": N, "C": C, "layout": args.trimul_layout,
+                   "channels_last_path": None if first else ("direct" if ws is None else "workspace")},
         "pct_of_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "stages_ms": {k_: round(v_, 4) for k_, v_ in stage_ms.items()},
         "wall_s_timed_region": round(wall, 4), "roofline": roofline, "cpu_baseline": cpu,

@@ -27,9 +27,13 @@
  *   TRI_MUL_CHANNELS_FIRST  bf16 [B, C, N, N], index [b, c, first pair index, second pair index]
  *                           (each channel a plain N x N matrix); N a multiple of 8
  * The channels-first form is the fast one: every load is a run of contiguous elements of one
- * channel.  In the channels-last form a work-group reads 8 channels, 16 bytes of each pair
- * entry, which spends most of each cache line it touches; it serves callers that hold the
- * pair layout and cannot have the projections write channels first.
+ * channel.  For the channels-last form there are two paths:
+ *   - with a workspace (tri_mul_workspace_bytes, N a multiple of 8): the inputs are copied
+ *     channels first into the workspace, the channels-first product runs, and the outputs are
+ *     copied back (one extra read and write of each tensor);
+ *   - without one (workspace NULL): a kernel that reads the pair layout in place, 8 channels
+ *     per work-group, which spends most of each cache line it touches (several times slower).
+ * Both paths, and the channels-first form, give bitwise-identical results on the same values.
  *
  * Arithmetic: bf16 products accumulated in FP32 on the matrix cores, one channel at a time;
  * each output is rounded once to bf16 (round to nearest even).  Every sum runs in a fixed
@@ -67,15 +71,26 @@ typedef enum {
 #define TRI_MUL_MAX_N 1024
 
 /*
+ * Bytes of device workspace for the fast channels-last path (the backward's five tensors
+ * channels first); 0 for the channels-first layout, for N not a multiple of 8 (no fast path),
+ * or for an invalid shape.  The same workspace serves the forward.  It is only valid for the
+ * call it is passed to.
+ */
+size_t tri_mul_workspace_bytes(int layout, int64_t B, int64_t N, int64_t C);
+
+/*
  * Forward: x from a and b.
  * Errors: TRI_ATTN_ERROR_INVALID_VALUE (NULL pointer, B/N/C < 1, unknown direction or layout,
  * x overlapping a or b); TRI_ATTN_ERROR_UNSUPPORTED (C > 1024, N > TRI_MUL_MAX_N, B > 2^16,
  * C not a multiple of 8 in the channels-last layout, N not a multiple of 8 in the
  * channels-first layout); TRI_ATTN_ERROR_MISALIGNED (a pointer not 16-byte aligned);
- * TRI_ATTN_ERROR_LAUNCH.
+ * TRI_ATTN_ERROR_WORKSPACE (channels last, a workspace smaller than tri_mul_workspace_bytes);
+ * TRI_ATTN_ERROR_LAUNCH.  workspace may be NULL (see the layouts above); it is ignored in the
+ * channels-first layout and must not overlap any tensor.
  */
 tri_attn_status tri_mul_fwd(int direction, int layout, int64_t B, int64_t N, int64_t C,
-                            const void *a, const void *b, void *x, hipStream_t stream);
+                            const void *a, const void *b, void *x,
+                            void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Backward: da and db from a, b and the output gradient dx (same errors as tri_mul_fwd;
@@ -83,7 +98,7 @@ tri_attn_status tri_mul_fwd(int direction, int layout, int64_t B, int64_t N, int
  */
 tri_attn_status tri_mul_bwd(int direction, int layout, int64_t B, int64_t N, int64_t C,
                             const void *a, const void *b, const void *dx, void *da, void *db,
-                            hipStream_t stream);
+                            void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -159,10 +159,12 @@ def test_layout_validation(lib):
 
 def test_tri_mul_validation(lib):
     a, b, x, dx, da, db = _ptrs(6)
+    ws = _ptrs(1, base=1 << 46)[0]
     fwd = lambda d, B, N, C, lay=0, **k: ta.tri_mul_fwd(d, lay, B, N, C, k.get("a", a), k.get("b", b),
-                                                          k.get("x", x), 0)
+                                                          k.get("x", x), k.get("ws"), k.get("wsb", 0), stream=0)
     bwd = lambda d, B, N, C, lay=0, **k: ta.tri_mul_bwd(d, lay, B, N, C, k.get("a", a), k.get("b", b),
-                                                          k.get("dx", dx), k.get("da", da), k.get("db", db), 0)
+                                                          k.get("dx", dx), k.get("da", da), k.get("db", db),
+                                                          k.get("ws"), k.get("wsb", 0), stream=0)
     assert ta.TRI_MUL_LAYOUTS == {"channels_last": 0, "channels_first": 1}
     for f in (fwd, bwd):
         assert f(2, 1, 64, 32) == INVALID          # unknown direction
@@ -178,6 +180,17 @@ def test_tri_mul_validation(lib):
         assert f(0, 1, 64, 32, a=0) == INVALID
         assert f(0, 1, 64, 32, a=a + 8) == MISALIGNED
         assert f(0, 1, 64, 12, lay=1, a=a + 8) == MISALIGNED  # channels first accepts any C
+    # channels last: the workspace holds five channels-first tensors; too small is an error,
+    # overlapping a tensor is invalid, and N not a multiple of 8 needs none
+    need = ta.tri_mul_workspace_bytes(0, 1, 64, 32)
+    assert need >= 5 * 64 * 64 * 32 * 2 and need % 256 == 0
+    assert ta.tri_mul_workspace_bytes(1, 1, 64, 32) == 0
+    assert ta.tri_mul_workspace_bytes(0, 1, 60, 32) == 0
+    assert ta.tri_mul_workspace_bytes(0, 1, 64, 12) == 0
+    for f in (fwd, bwd):
+        assert f(0, 1, 64, 32, ws=ws, wsb=need - 256) == WORKSPACE
+        assert f(0, 1, 64, 32, ws=a, wsb=need) == INVALID
+        assert f(0, 1, 64, 32, ws=ws + 8, wsb=need) == MISALIGNED
     assert fwd(0, 1, 64, 32, x=a + 64) == INVALID  # output overlaps an input
     assert bwd(0, 1, 64, 32, db=da + 1024) == INVALID
     assert bwd(1, 1, 64, 32, da=dx) == INVALID

@@ -35,15 +35,18 @@ def cl(t):  # channels first -> channels last
     return t.permute(0, 2, 3, 1).contiguous()
 
 
-def _run(ta, a, b, dx, direction, layout="channels_last"):
-    """a, b, dx channels last; returns channels-last outputs computed in `layout`."""
+def _run(ta, a, b, dx, direction, layout="channels_last", workspace=False):
+    """a, b, dx channels last; returns channels-last outputs computed in `layout` (channels last:
+    through the workspace path if `workspace`, else the in-place kernel)."""
     B, N, _, C = a.shape
     d, lay = ta.TRI_MUL_DIRECTIONS[direction], ta.TRI_MUL_LAYOUTS[layout]
     if layout == "channels_first":
         a, b, dx = cf(a), cf(b), cf(dx)
     x, da, db = torch.empty_like(a), torch.empty_like(a), torch.empty_like(a)
-    assert ta.tri_mul_fwd(d, lay, B, N, C, a, b, x) == 0
-    assert ta.tri_mul_bwd(d, lay, B, N, C, a, b, dx, da, db) == 0
+    nws = ta.tri_mul_workspace_bytes(lay, B, N, C) if workspace else 0
+    ws = torch.empty(nws, dtype=torch.uint8, device=a.device) if nws else None
+    assert ta.tri_mul_fwd(d, lay, B, N, C, a, b, x, ws, nws) == 0
+    assert ta.tri_mul_bwd(d, lay, B, N, C, a, b, dx, da, db, ws, nws) == 0
     torch.cuda.synchronize()
     out = dict(x=x, da=da, db=db)
     return {n: cl(v) for n, v in out.items()} if layout == "channels_first" else out
@@ -122,16 +125,19 @@ def test_tri_mul_parity_full_size_sampled_channels(direction, layout):
     _check(inp, direction, channels=[0, 45, 90, 127], layout=layout)
 
 
-def test_tri_mul_layouts_agree_bitwise():
-    # both kernels add the same 16-term products in the same ascending order per element
+@pytest.mark.parametrize("B,N,C", [(1, 136, 16), (2, 72, 24), (1, 264, 8)])
+def test_tri_mul_layouts_agree_bitwise(B, N, C):
+    # every path adds the same 16-term products in the same ascending order per element
     import triangle_attention_amd as ta
-    inp = make_pair_inputs(1, 136, 16, seed=5)
+    inp = make_pair_inputs(B, N, C, seed=5 + N)
     a, b, dx = (to_dev(inp[n]) for n in ("a", "b", "dx"))
     for direction in ("outgoing", "incoming"):
         last = _run(ta, a, b, dx, direction, "channels_last")
+        staged = _run(ta, a, b, dx, direction, "channels_last", workspace=True)
         first = _run(ta, a, b, dx, direction, "channels_first")
         for n in ("x", "da", "db"):
             assert torch.equal(_bits(last[n]), _bits(first[n])), (direction, n)
+            assert torch.equal(_bits(staged[n]), _bits(first[n])), (direction, n, "workspace")
 
 
 def test_tri_mul_deterministic_and_autograd():

@@ -21,7 +21,7 @@ __all__ = [
     "TriAttnError", "load_library", "tri_attn_status_string", "tri_attn_fwd_workspace_bytes",
     "tri_attn_bwd_workspace_bytes", "tri_attn_fwd", "tri_attn_bwd", "tri_attn_fwd_stages", "tri_attn_bwd_stages",
     "tri_attn_fwd_ex", "tri_attn_bwd_ex", "triangle_attention", "TRI_ATTN_MAX_N", "LAYOUTS",
-    "tri_mul_fwd", "tri_mul_bwd", "triangle_multiplication", "TRI_MUL_DIRECTIONS", "TRI_MUL_LAYOUTS",
+    "tri_mul_fwd", "tri_mul_bwd", "tri_mul_workspace_bytes", "triangle_multiplication", "TRI_MUL_DIRECTIONS", "TRI_MUL_LAYOUTS",
     "TRI_MUL_MAX_N",
 ]
 
@@ -65,9 +65,11 @@ def load_library(path: str = LIB_PATH):
     lib.tri_attn_fwd_ex.restype = ctypes.c_int
     lib.tri_attn_bwd_ex.argtypes = [ctypes.c_uint, ctypes.c_int] + lib.tri_attn_bwd.argtypes
     lib.tri_attn_bwd_ex.restype = ctypes.c_int
-    lib.tri_mul_fwd.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, vp, vp, vp, vp]
+    lib.tri_mul_workspace_bytes.argtypes = [ctypes.c_int, i64, i64, i64]
+    lib.tri_mul_workspace_bytes.restype = sz
+    lib.tri_mul_fwd.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, vp, vp, vp, vp, sz, vp]
     lib.tri_mul_fwd.restype = ctypes.c_int
-    lib.tri_mul_bwd.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, vp, vp, vp, vp, vp, vp]
+    lib.tri_mul_bwd.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.tri_mul_bwd.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -153,15 +155,21 @@ def tri_attn_bwd_ex(stages, layout, B, N, H, D, q, k, v, bias, key_mask, o, lse,
                                               int(workspace_bytes), _stream(stream)))
 
 
-def tri_mul_fwd(direction, layout, B, N, C, a, b, x, stream=None) -> int:
+def tri_mul_workspace_bytes(layout, B, N, C) -> int:
+    return int(load_library().tri_mul_workspace_bytes(layout, B, N, C))
+
+
+def tri_mul_fwd(direction, layout, B, N, C, a, b, x, workspace=None, workspace_bytes=0, stream=None) -> int:
     """Marshal to the C entry point (include/tri_mul.h); returns the status code."""
-    return int(load_library().tri_mul_fwd(direction, layout, B, N, C, _ptr(a), _ptr(b), _ptr(x), _stream(stream)))
+    return int(load_library().tri_mul_fwd(direction, layout, B, N, C, _ptr(a), _ptr(b), _ptr(x), _ptr(workspace),
+                                          int(workspace_bytes), _stream(stream)))
 
 
-def tri_mul_bwd(direction, layout, B, N, C, a, b, dx, da, db, stream=None) -> int:
+def tri_mul_bwd(direction, layout, B, N, C, a, b, dx, da, db, workspace=None, workspace_bytes=0,
+                stream=None) -> int:
     """Marshal to the C entry point (include/tri_mul.h); returns the status code."""
     return int(load_library().tri_mul_bwd(direction, layout, B, N, C, _ptr(a), _ptr(b), _ptr(dx), _ptr(da),
-                                          _ptr(db), _stream(stream)))
+                                          _ptr(db), _ptr(workspace), int(workspace_bytes), _stream(stream)))
 
 
 def _check(status: int, where: str):
@@ -258,12 +266,19 @@ def _mul_shape(a, b, direction, layout):
     return B, N, C
 
 
+def _mul_workspace(layout, B, N, C, device):
+    n = tri_mul_workspace_bytes(TRI_MUL_LAYOUTS[layout], B, N, C)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
 class _TriMulFn(torch.autograd.Function):
     @staticmethod
     def forward(ctx, a, b, direction, layout):
         B, N, C = _mul_shape(a, b, direction, layout)
         x = torch.empty_like(a)
-        _check(tri_mul_fwd(TRI_MUL_DIRECTIONS[direction], TRI_MUL_LAYOUTS[layout], B, N, C, a, b, x), "tri_mul_fwd")
+        ws = _mul_workspace(layout, B, N, C, a.device)
+        _check(tri_mul_fwd(TRI_MUL_DIRECTIONS[direction], TRI_MUL_LAYOUTS[layout], B, N, C, a, b, x, ws,
+                           0 if ws is None else ws.numel()), "tri_mul_fwd")
         ctx.save_for_backward(a, b)
         ctx.direction, ctx.layout, ctx.shape = direction, layout, (B, N, C)
         return x
@@ -273,8 +288,9 @@ class _TriMulFn(torch.autograd.Function):
         a, b = ctx.saved_tensors
         B, N, C = ctx.shape
         da, db = torch.empty_like(a), torch.empty_like(b)
+        ws = _mul_workspace(ctx.layout, B, N, C, a.device)
         _check(tri_mul_bwd(TRI_MUL_DIRECTIONS[ctx.direction], TRI_MUL_LAYOUTS[ctx.layout], B, N, C, a, b,
-                           dx.contiguous(), da, db), "tri_mul_bwd")
+                           dx.contiguous(), da, db, ws, 0 if ws is None else ws.numel()), "tri_mul_bwd")
         return da, db, None, None
 
 

@@ -187,7 +187,7 @@ void tri_mul_kernel(const bf16* __restrict__ P, const bf16* __restrict__ Q, bf16
 // 32 staged through a three-stage LDS ring filled by direct-to-LDS loads issued two steps
 // ahead.  Loads are 16-byte chunks along the contiguous index.
 // A t-major operand is stored [row][t] (64-byte rows, XOR-swizzled chunks) and read with
-// ds_read_b128; an r-major operand is stored as loaded, [t][row] (256-byte rows whose 64-byte
+// ds_read_b128; an r-major operand is stored as loaded, [t][row] (rows of 256 or 512 bytes whose 64-byte
 // blocks are XOR-swizzled by t % 4, so that the transposing reads of 32 lanes, 4 t-rows x 64
 // bytes, hit distinct banks) and read with ds_read_b64_tr_b16, which hands each lane 4
 // consecutive t of its row.  The output tile goes through LDS to leave as full 512-byte row
@@ -383,9 +383,45 @@ void tri_mul_cf_kernel(const bf16* __restrict__ P, const bf16* __restrict__ Q, b
   }
 }
 
+// ------------------------------------------------------------------ layout change
+// out[b][k][r] = in[b][r][k] for an R x K bf16 matrix per batch: channels last -> channels first
+// with (R, K) = (N*N, C), and back with (C, N*N).  A work-group moves a 64 x 64 tile through LDS
+// (padded rows); every global access is a run of 64 consecutive elements per wave.
+constexpr int TP = 64;
+__global__ __launch_bounds__(256)
+void transpose_kernel(const bf16* __restrict__ in, bf16* __restrict__ out, int64_t R, int64_t K, int64_t tilesR,
+                      int64_t tilesK) {
+  __shared__ unsigned short T[TP][TP + 1];
+  const int64_t per = tilesR * tilesK;
+  const int64_t b = blockIdx.x / per, rem = blockIdx.x % per;
+  const int64_t r0 = (rem / tilesK) * TP, k0 = (rem % tilesK) * TP;
+  const unsigned short* src = (const unsigned short*)in + b * R * K;
+  unsigned short* dst = (unsigned short*)out + b * R * K;
+  const int c = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < TP / 4; i++) {  // rows r0 + 4 i + w, columns k0 + c
+    const int rr = 4 * i + w;
+    if (r0 + rr < R && k0 + c < K) T[rr][c] = src[(r0 + rr) * K + k0 + c];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < TP / 4; i++) {  // output rows k0 + 4 i + w, columns r0 + c
+    const int kk = 4 * i + w;
+    if (k0 + kk < K && r0 + c < R) dst[(k0 + kk) * R + r0 + c] = T[c][kk];
+  }
+}
+
+void transpose(const void* in, void* out, int64_t B, int64_t R, int64_t K, hipStream_t st) {
+  const int64_t tr = (R + TP - 1) / TP, tk = (K + TP - 1) / TP;
+  hipLaunchKernelGGL(transpose_kernel, dim3((unsigned)(B * tr * tk)), dim3(256), 0, st, (const bf16*)in, (bf16*)out,
+                     R, K, tr, tk);
+}
+
 unsigned grid_xcd(int64_t ntiles) { return (unsigned)((ntiles + kXcd - 1) / kXcd * kXcd); }
 
 struct Range { const void* p; int64_t n; };
+constexpr int64_t kWsAlign = 256;
+int64_t ws_tensor_bytes(int64_t B, int64_t N, int64_t C) { return (B * N * N * C * 2 + kWsAlign - 1) / kWsAlign * kWsAlign; }
 bool overlap(Range x, Range y) {
   const uintptr_t a0 = (uintptr_t)x.p, a1 = a0 + (uintptr_t)x.n, b0 = (uintptr_t)y.p, b1 = b0 + (uintptr_t)y.n;
   return a0 < b1 && b0 < a1;
@@ -428,17 +464,39 @@ tri_attn_status launch_cf(bool pt, bool qt, const void* p, const void* q, void* 
 
 extern "C" {
 
+size_t tri_mul_workspace_bytes(int layout, int64_t B, int64_t N, int64_t C) {
+  if (check_shape(TRI_MUL_OUTGOING, layout, B, N, C) != TRI_ATTN_SUCCESS) return 0;
+  if (layout == TRI_MUL_CHANNELS_FIRST || N % 8 != 0) return 0;
+  return (size_t)(5 * ws_tensor_bytes(B, N, C));  // the backward's a, b, dx, da, db channels first
+}
+
 tri_attn_status tri_mul_fwd(int direction, int layout, int64_t B, int64_t N, int64_t C, const void* a, const void* b,
-                            void* x, hipStream_t stream) {
+                            void* x, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   const tri_attn_status st = check_shape(direction, layout, B, N, C);
   if (st != TRI_ATTN_SUCCESS) return st;
   if (!a || !b || !x) return TRI_ATTN_ERROR_INVALID_VALUE;
   const int64_t bytes = B * N * N * C * 2;
   if (overlap({x, bytes}, {a, bytes}) || overlap({x, bytes}, {b, bytes})) return TRI_ATTN_ERROR_INVALID_VALUE;
-  if (!aligned16(a) || !aligned16(b) || !aligned16(x)) return TRI_ATTN_ERROR_MISALIGNED;
+  const Range ws{workspace, (int64_t)workspace_bytes};
+  if (workspace && (overlap(ws, {a, bytes}) || overlap(ws, {b, bytes}) || overlap(ws, {x, bytes})))
+    return TRI_ATTN_ERROR_INVALID_VALUE;
+  if (!aligned16(a) || !aligned16(b) || !aligned16(x) || (workspace && !aligned16(workspace)))
+    return TRI_ATTN_ERROR_MISALIGNED;
   if (layout == TRI_MUL_CHANNELS_FIRST)  // outgoing: a, b t-major; incoming: both r-major
     return direction == TRI_MUL_OUTGOING ? launch_cf(true, true, a, b, x, B, N, C, stream)
                                          : launch_cf(false, false, a, b, x, B, N, C, stream);
+  if (workspace && N % 8 == 0) {  // channels last through the workspace: change layout, run the channels-first product
+    if (workspace_bytes < tri_mul_workspace_bytes(layout, B, N, C)) return TRI_ATTN_ERROR_WORKSPACE;
+    const int64_t tb = ws_tensor_bytes(B, N, C);
+    char* w = (char*)workspace;
+    transpose(a, w, B, N * N, C, stream);
+    transpose(b, w + tb, B, N * N, C, stream);
+    const tri_attn_status r = direction == TRI_MUL_OUTGOING ? launch_cf(true, true, w, w + tb, w + 2 * tb, B, N, C, stream)
+                                                            : launch_cf(false, false, w, w + tb, w + 2 * tb, B, N, C, stream);
+    if (r != TRI_ATTN_SUCCESS) return r;
+    transpose(w + 2 * tb, x, B, C, N * N, stream);
+    return hipGetLastError() == hipSuccess ? TRI_ATTN_SUCCESS : TRI_ATTN_ERROR_LAUNCH;
+  }
   const int64_t NC = N * C;
   // outgoing: P[r=i,t=k] = a[i,k], Q[s=j,t=k] = b[j,k]; incoming: P[r=i,t=k] = a[k,i], Q = b[k,j]
   const MulStrides S = direction == TRI_MUL_OUTGOING ? MulStrides{NC, C, NC, C, NC, C}
@@ -447,7 +505,8 @@ tri_attn_status tri_mul_fwd(int direction, int layout, int64_t B, int64_t N, int
 }
 
 tri_attn_status tri_mul_bwd(int direction, int layout, int64_t B, int64_t N, int64_t C, const void* a,
-                            const void* b, const void* dx, void* da, void* db, hipStream_t stream) {
+                            const void* b, const void* dx, void* da, void* db, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
   const tri_attn_status st = check_shape(direction, layout, B, N, C);
   if (st != TRI_ATTN_SUCCESS) return st;
   if (!a || !b || !dx || !da || !db) return TRI_ATTN_ERROR_INVALID_VALUE;
@@ -456,19 +515,42 @@ tri_attn_status tri_mul_bwd(int direction, int layout, int64_t B, int64_t N, int
   for (const Range& r : ins)
     if (overlap({da, bytes}, r) || overlap({db, bytes}, r)) return TRI_ATTN_ERROR_INVALID_VALUE;
   if (overlap({da, bytes}, {db, bytes})) return TRI_ATTN_ERROR_INVALID_VALUE;
-  if (!aligned16(a) || !aligned16(b) || !aligned16(dx) || !aligned16(da) || !aligned16(db))
+  const Range ws{workspace, (int64_t)workspace_bytes};
+  if (workspace) {
+    const Range all[] = {{a, bytes}, {b, bytes}, {dx, bytes}, {da, bytes}, {db, bytes}};
+    for (const Range& r : all)
+      if (overlap(ws, r)) return TRI_ATTN_ERROR_INVALID_VALUE;
+  }
+  if (!aligned16(a) || !aligned16(b) || !aligned16(dx) || !aligned16(da) || !aligned16(db) ||
+      (workspace && !aligned16(workspace)))
     return TRI_ATTN_ERROR_MISALIGNED;
   const int64_t NC = N * C;
   tri_attn_status r1, r2;
-  if (layout == TRI_MUL_CHANNELS_FIRST) {
+  auto cf_pair = [&](const void* A, const void* Bv, const void* DX, void* DA, void* DB) {
     if (direction == TRI_MUL_OUTGOING) {
-      r1 = launch_cf(true, false, dx, b, da, B, N, C, stream);   // da[i,k] = sum_j dx[i,j] b[j,k]
-      r2 = launch_cf(false, false, dx, a, db, B, N, C, stream);  // db[j,k] = sum_i dx[i,j] a[i,k]
+      r1 = launch_cf(true, false, DX, Bv, DA, B, N, C, stream);   // da[i,k] = sum_j dx[i,j] b[j,k]
+      r2 = launch_cf(false, false, DX, A, DB, B, N, C, stream);   // db[j,k] = sum_i dx[i,j] a[i,k]
     } else {
-      r1 = launch_cf(true, true, b, dx, da, B, N, C, stream);    // da[k,i] = sum_j b[k,j] dx[i,j]
-      r2 = launch_cf(true, false, a, dx, db, B, N, C, stream);   // db[k,j] = sum_i a[k,i] dx[i,j]
+      r1 = launch_cf(true, true, Bv, DX, DA, B, N, C, stream);    // da[k,i] = sum_j b[k,j] dx[i,j]
+      r2 = launch_cf(true, false, A, DX, DB, B, N, C, stream);    // db[k,j] = sum_i a[k,i] dx[i,j]
     }
+  };
+  if (layout == TRI_MUL_CHANNELS_FIRST) {
+    cf_pair(a, b, dx, da, db);
     return r1 != TRI_ATTN_SUCCESS ? r1 : r2;
+  }
+  if (workspace && N % 8 == 0) {  // channels last through the workspace
+    if (workspace_bytes < tri_mul_workspace_bytes(layout, B, N, C)) return TRI_ATTN_ERROR_WORKSPACE;
+    const int64_t tb = ws_tensor_bytes(B, N, C);
+    char* w = (char*)workspace;
+    transpose(a, w, B, N * N, C, stream);
+    transpose(b, w + tb, B, N * N, C, stream);
+    transpose(dx, w + 2 * tb, B, N * N, C, stream);
+    cf_pair(w, w + tb, w + 2 * tb, w + 3 * tb, w + 4 * tb);
+    if (r1 != TRI_ATTN_SUCCESS || r2 != TRI_ATTN_SUCCESS) return r1 != TRI_ATTN_SUCCESS ? r1 : r2;
+    transpose(w + 3 * tb, da, B, C, N * N, stream);
+    transpose(w + 4 * tb, db, B, C, N * N, stream);
+    return hipGetLastError() == hipSuccess ? TRI_ATTN_SUCCESS : TRI_ATTN_ERROR_LAUNCH;
   }
   if (direction == TRI_MUL_OUTGOING) {
     // da[i,k] = sum_j dx[i,j] b[j,k]: P[r=i,t=j] = dx[i,j], Q[s=k,t=j] = b[j,k]

@@ -58,10 +58,12 @@ def _mul(name: str, layout: str, reps: int):
     a, b, dx = dev(inp["a"]), dev(inp["b"]), dev(inp["dx"])
     x, da, db = torch.empty_like(a), torch.empty_like(a), torch.empty_like(a)
     lay = ta.TRI_MUL_LAYOUTS[layout]
+    nws = ta.tri_mul_workspace_bytes(lay, B, N, C)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda") if nws else None
     for _ in range(reps):
         for d in (0, 1):
-            assert ta.tri_mul_fwd(d, lay, B, N, C, a, b, x) == 0
-            assert ta.tri_mul_bwd(d, lay, B, N, C, a, b, dx, da, db) == 0
+            assert ta.tri_mul_fwd(d, lay, B, N, C, a, b, x, ws, nws) == 0
+            assert ta.tri_mul_bwd(d, lay, B, N, C, a, b, dx, da, db, ws, nws) == 0
     torch.cuda.synchronize()
     print(f"mul {name} {layout} x{reps} done", flush=True)
 
