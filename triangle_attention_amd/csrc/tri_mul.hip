@@ -384,30 +384,42 @@ void tri_mul_cf_kernel(const bf16* __restrict__ P, const bf16* __restrict__ Q, b
 }
 
 // ------------------------------------------------------------------ layout change
-// out[b][k][r] = in[b][r][k] for an R x K bf16 matrix per batch: channels last -> channels first
-// with (R, K) = (N*N, C), and back with (C, N*N).  A work-group moves a 64 x 64 tile through LDS
-// (padded rows); every global access is a run of 64 consecutive elements per wave.
+// out[b][k][r] = in[b][r][k] for an R x K bf16 matrix per batch (R and K multiples of 8):
+// channels last -> channels first with (R, K) = (N*N, C), and back with (C, N*N).  A work-group
+// moves a 64 x 64 tile through LDS: 16-byte loads along k, then each thread gathers 8
+// consecutive r of one k from LDS and stores them as one 16-byte chunk, so that both sides are
+// runs of whole 128-byte segments.
 constexpr int TP = 64;
+constexpr int TPS = TP + 8;  // LDS row stride (elements): 144-byte rows keep the chunks aligned
 __global__ __launch_bounds__(256)
 void transpose_kernel(const bf16* __restrict__ in, bf16* __restrict__ out, int64_t R, int64_t K, int64_t tilesR,
                       int64_t tilesK) {
-  __shared__ unsigned short T[TP][TP + 1];
+  __shared__ __attribute__((aligned(16))) unsigned short T[TP * TPS];
   const int64_t per = tilesR * tilesK;
   const int64_t b = blockIdx.x / per, rem = blockIdx.x % per;
   const int64_t r0 = (rem / tilesK) * TP, k0 = (rem % tilesK) * TP;
   const unsigned short* src = (const unsigned short*)in + b * R * K;
   unsigned short* dst = (unsigned short*)out + b * R * K;
-  const int c = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int tid = threadIdx.x;
 #pragma unroll
-  for (int i = 0; i < TP / 4; i++) {  // rows r0 + 4 i + w, columns k0 + c
-    const int rr = 4 * i + w;
-    if (r0 + rr < R && k0 + c < K) T[rr][c] = src[(r0 + rr) * K + k0 + c];
+  for (int e = 0; e < 2; e++) {  // chunk (row r, k-chunk kc): 8 threads per 128-byte row segment
+    const int ch = tid + e * 256, r = ch >> 3, kc = ch & 7;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (r0 + r < R && k0 + kc * 8 < K) v = *(const u32x4*)(src + (r0 + r) * K + k0 + kc * 8);
+    *(__attribute__((address_space(3))) u32x4*)(T + r * TPS + kc * 8) = v;
   }
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < TP / 4; i++) {  // output rows k0 + 4 i + w, columns r0 + c
-    const int kk = 4 * i + w;
-    if (k0 + kk < K && r0 + c < R) dst[(k0 + kk) * R + r0 + c] = T[c][kk];
+  for (int e = 0; e < 2; e++) {  // output chunk (row k, r-chunk rc)
+    const int ch = tid + e * 256, k = ch >> 3, rc = ch & 7;
+    if (k0 + k < K && r0 + rc * 8 < R) {
+      unsigned w[4];
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+        w[i] = (unsigned)T[(rc * 8 + 2 * i) * TPS + k] | ((unsigned)T[(rc * 8 + 2 * i + 1) * TPS + k] << 16);
+      const u32x4 v = {w[0], w[1], w[2], w[3]};
+      *(u32x4*)(dst + (k0 + k) * R + r0 + rc * 8) = v;
+    }
   }
 }
 
