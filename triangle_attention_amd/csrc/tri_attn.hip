@@ -335,6 +335,9 @@ void fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   const int64_t ntiles = (int64_t)B * H * N * QT;
   const int64_t tile = xcd_tile(ntiles);
   if (tile >= ntiles) return;
+  // Tile order: query tiles fastest, then slices, then heads, so that the work-groups on one
+  // XCD share one head's prepared bias tiles in its L2 (also in the strided layouts, where
+  // putting the heads first was measured 1.7x slower: the bias tiles of all heads no longer fit).
   const int qt = (int)(tile % QT);
   int64_t rest = tile / QT;
   const int i = (int)(rest % N); rest /= N;
@@ -606,11 +609,23 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   const int64_t ntiles = (int64_t)B * H * ngroups * KB;
   const int64_t tile = xcd_tile(ntiles);
   if (tile >= ntiles) return;
-  const int kb = (int)(tile % KB);
-  int64_t rest = tile / KB;
-  const int grp = (int)(rest % ngroups); rest /= ngroups;
-  const int h = (int)(rest % H);
-  const int b = (int)(rest / H);
+  // Tile order: the key blocks of one (head, slice group) adjacent, so that they run together
+  // on one XCD and share its L2 for the slices' Q and dO rows.  In a strided layout the heads
+  // of one token row also share cache lines, so there the heads come fastest.
+  int kb, grp, h, b;
+  if (STRIDED) {
+    h = (int)(tile % H);
+    int64_t rest = tile / H;
+    kb = (int)(rest % KB); rest /= KB;
+    grp = (int)(rest % ngroups);
+    b = (int)(rest / ngroups);
+  } else {
+    kb = (int)(tile % KB);
+    int64_t rest = tile / KB;
+    grp = (int)(rest % ngroups); rest /= ngroups;
+    h = (int)(rest % H);
+    b = (int)(rest / H);
+  }
   const int i_begin = grp * G, i_end = min(N, i_begin + G);
 
   // the wave index is uniform; readfirstlane lets the compiler keep everything derived
