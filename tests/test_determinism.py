@@ -61,3 +61,27 @@ def test_compensation_ablation_small():
     print("rel-RMSE with residual", with_r, "without", without, flush=True)
     # the compensated correction must not be worse on the gradient that sees D most directly
     assert with_r["dbias"] <= without["dbias"]
+
+
+def test_bitwise_with_concurrent_work_on_another_stream():
+    """Results do not depend on what else the GPU runs: the same call while another stream keeps
+    the device busy with unrelated products (both streams at the default priority)."""
+    inp = make_inputs(1, 200, 2, 32, seed=5, bias_std=2.0)
+    ref = run_gpu(inp)
+    x = torch.randn(2048, 2048, device="cuda")
+    side, main = torch.cuda.Stream(), torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    main.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        y = x
+        for _ in range(40):
+            y = torch.tanh(y @ x)  # float32, contiguous operands
+    with torch.cuda.stream(main):
+        out = run_gpu(inp)
+    torch.cuda.synchronize()
+    assert torch.isfinite(y).all()
+    for n in OUTS:
+        a, b = ref[n], out[n]
+        va = a.view(torch.int32) if a.dtype == torch.float32 else a.view(torch.int16)
+        vb = b.view(torch.int32) if b.dtype == torch.float32 else b.view(torch.int16)
+        assert torch.equal(va, vb), n
