@@ -22,7 +22,8 @@
  *
  * Conventions shared by every entry point:
  *   - All pointers are device pointers, 16-byte aligned (key_mask: any alignment).
- *   - Supported shapes: D in {16, 32}; 1 <= N <= TRI_ATTN_MAX_N; B, H >= 1.
+ *   - Supported shapes: D in {16, 32}; B, H >= 1; 1 <= N <= TRI_ATTN_MAX_N for the backward
+ *     (and the forward that feeds it), 1 <= N <= TRI_ATTN_FWD_MAX_N for the forward alone.
  *   - The library allocates no memory and keeps no state between calls.  Scratch
  *     space comes from the caller through (workspace, workspace_bytes), sized by the
  *     matching *_workspace_bytes function, and is only valid for the call it is passed to.
@@ -49,13 +50,18 @@
 extern "C" {
 #endif
 
+/* Largest N of the backward: its work-group keeps the pair-bias gradient of all N queries of
+ * its 64-key block in registers. */
 #define TRI_ATTN_MAX_N 768
+/* Largest N of the forward alone (inference on longer crops): the forward streams keys and has
+ * no such per-query state. */
+#define TRI_ATTN_FWD_MAX_N 4096
 
 typedef enum {
   TRI_ATTN_SUCCESS = 0,
   TRI_ATTN_ERROR_INVALID_VALUE = 1, /* NULL required pointer, B/N/H < 1, output overlapping an input,
                                        unknown stage bits or layout */
-  TRI_ATTN_ERROR_UNSUPPORTED = 2,   /* D not in {16, 32}, N > TRI_ATTN_MAX_N, B > 2^20, H > 4096,
+  TRI_ATTN_ERROR_UNSUPPORTED = 2,   /* D not in {16, 32}, N above the call's limit, B > 2^20, H > 4096,
                                        B*N*H*ceil(N/128)*8 > 2^31 - 1, or a layout whose slice
                                        span exceeds 32-bit offsets */
   TRI_ATTN_ERROR_MISALIGNED = 3,    /* a tensor pointer that is not 16-byte aligned */

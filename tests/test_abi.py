@@ -52,9 +52,14 @@ def test_workspace_sizes(lib):
         assert f > 0 and b > 0 and f % 256 == 0 and b % 256 == 0
         # the backward holds one bf16 dq partial (2 bytes per element) per 64-key block
         assert b >= -(-N // 64) * B * N * H * N * D * 2
-    for bad in [(0, 8, 1, 16), (1, 0, 1, 16), (1, 8, 0, 16), (1, 8, 1, 64), (1, 769, 1, 16)]:
+    for bad in [(0, 8, 1, 16), (1, 0, 1, 16), (1, 8, 0, 16), (1, 8, 1, 64), (1, 4097, 1, 16)]:
         assert ta.tri_attn_fwd_workspace_bytes(*bad) == 0
         assert ta.tri_attn_bwd_workspace_bytes(*bad) == 0
+    # the forward alone reaches TRI_ATTN_FWD_MAX_N; the backward stops at TRI_ATTN_MAX_N
+    assert ta.TRI_ATTN_MAX_N == 768 and ta.TRI_ATTN_FWD_MAX_N == 4096
+    assert ta.tri_attn_fwd_workspace_bytes(1, 769, 1, 16) > 0
+    assert ta.tri_attn_fwd_workspace_bytes(1, 4096, 4, 32) > 0
+    assert ta.tri_attn_bwd_workspace_bytes(1, 769, 1, 16) == 0
     # the backward partial buffers grow with N (dq partials per 64-key block)
     assert ta.tri_attn_bwd_workspace_bytes(1, 768, 4, 32) > ta.tri_attn_bwd_workspace_bytes(1, 384, 4, 32)
 
@@ -84,7 +89,8 @@ def test_fwd_validation(lib):
     assert _fwd(shape=(1, 64, 0, 16)) == INVALID
     assert _fwd(shape=(1, 64, 4, 64)) == UNSUPPORTED
     assert _fwd(shape=(1, 64, 4, 8)) == UNSUPPORTED
-    assert _fwd(shape=(1, 769, 4, 16)) == UNSUPPORTED
+    assert _fwd(shape=(1, 4097, 4, 16)) == UNSUPPORTED
+    assert _fwd(shape=(1, 769, 4, 16), wsb=16) == WORKSPACE  # a forward-only crop past the backward's limit
     for idx in range(6):  # q, k, v, bias, o, lse are required
         p = _ptrs(8)
         p[idx] = 0
@@ -107,6 +113,7 @@ def test_fwd_validation(lib):
 
 def test_bwd_validation(lib):
     assert _bwd(shape=(1, 64, 4, 48)) == UNSUPPORTED
+    assert _bwd(shape=(1, 769, 4, 16), wsb=1 << 40) == UNSUPPORTED
     assert _bwd(shape=(2, 0, 4, 16)) == INVALID
     for idx in (0, 1, 2, 3, 4, 5, 7, 8, 9, 10, 11):  # every tensor except the residual is required
         p = _ptrs(14)

@@ -141,3 +141,33 @@ def test_workload_sampled_parity(name):
         assert float(out["dbias"][..., w.N - w.mask_tail:].abs().max()) == 0.0
         assert float(out["dk"][:, :, :, w.N - w.mask_tail:].float().abs().max()) == 0.0
         assert float(out["dv"][:, :, :, w.N - w.mask_tail:].float().abs().max()) == 0.0
+
+
+# forward alone on crops past the backward's limit (inference): sampled slices, element by element
+@pytest.mark.parametrize("B,N,H,D,masked", [(1, 1100, 1, 16, True), (1, 1536, 2, 32, False)])
+def test_forward_only_long_crops(B, N, H, D, masked):
+    import triangle_attention_amd as ta
+    from tri_synth import bf16_bits_to_f64
+    from ._util import mask_dev, to_dev
+    print(f"forward only B={B} N={N} H={H} D={D} masked={masked}", flush=True)
+    inp = make_inputs(B, N, H, D, seed=N + D, bias_std=2.0)
+    if masked:
+        rng = np.random.default_rng(N)
+        m = (rng.random((B, N, N)) > 0.3).astype(np.uint8)
+        m[:, :, 0] = 1
+        inp["key_mask"] = m
+    q, k, v, bias = (to_dev(inp[n]) for n in ("q", "k", "v", "bias"))
+    o, lse, res = ta.forward(q, k, v, bias, mask_dev(inp["key_mask"]))
+    torch.cuda.synchronize()
+    assert ta.tri_attn_bwd_workspace_bytes(B, N, H, D) == 0  # no backward at this N
+    o_, lse_ = f64(o), f64(lse)
+    rng = np.random.default_rng(N + 1)
+    for i in sorted(set(rng.integers(0, N, 2).tolist() + [N - 1])):
+        for h in range(H):
+            mrow = None if inp["key_mask"] is None else inp["key_mask"][0, i]
+            o64, l64, _ = oracle.slice_forward64(bf16_bits_to_f64(inp["q"][0, i, h]), bf16_bits_to_f64(inp["k"][0, i, h]),
+                                                 bf16_bits_to_f64(inp["v"][0, i, h]), bf16_bits_to_f64(inp["bias"][0, h]),
+                                                 mrow)
+            e = dict(o_maxabs=maxabs(o_[0, i, h], o64), o=rrmse(o_[0, i, h], o64), lse=maxabs(lse_[0, i, h], l64))
+            print(f"  slice {i} head {h}", {k_: f"{v_:.2e}" for k_, v_ in e.items()}, flush=True)
+            assert e["o_maxabs"] <= TOL_O_MAXABS and e["o"] <= TOL_O_RRMSE and e["lse"] <= TOL_LSE_MAXABS, e

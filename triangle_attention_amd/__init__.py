@@ -20,12 +20,13 @@ from ._build import LIB_PATH, build  # noqa: F401
 __all__ = [
     "TriAttnError", "load_library", "tri_attn_status_string", "tri_attn_fwd_workspace_bytes",
     "tri_attn_bwd_workspace_bytes", "tri_attn_fwd", "tri_attn_bwd", "tri_attn_fwd_stages", "tri_attn_bwd_stages",
-    "tri_attn_fwd_ex", "tri_attn_bwd_ex", "triangle_attention", "TRI_ATTN_MAX_N", "LAYOUTS",
+    "tri_attn_fwd_ex", "tri_attn_bwd_ex", "triangle_attention", "TRI_ATTN_MAX_N", "TRI_ATTN_FWD_MAX_N", "LAYOUTS",
     "tri_mul_fwd", "tri_mul_bwd", "tri_mul_workspace_bytes", "triangle_multiplication", "TRI_MUL_DIRECTIONS", "TRI_MUL_LAYOUTS",
     "TRI_MUL_MAX_N",
 ]
 
-TRI_ATTN_MAX_N = 768
+TRI_ATTN_MAX_N = 768        # backward (and a forward that feeds it)
+TRI_ATTN_FWD_MAX_N = 4096   # forward alone
 TRI_MUL_MAX_N = 1024
 TRI_MUL_DIRECTIONS = {"outgoing": 0, "incoming": 1}
 TRI_MUL_LAYOUTS = {"channels_last": 0, "channels_first": 1}

@@ -1070,8 +1070,10 @@ struct Plan {
 constexpr int64_t kAlign = 256;
 
 // (the last bound keeps every grid and the 16-query tile index of the dq reduction in 32 bits)
-bool shape_ok(int64_t B, int64_t N, int64_t H, int64_t D) {
-  return B >= 1 && N >= 1 && H >= 1 && (D == 16 || D == 32) && N <= TRI_ATTN_MAX_N && B <= (1 << 20) &&
+// max_n: TRI_ATTN_FWD_MAX_N for the forward, TRI_ATTN_MAX_N for the backward (whose work-group
+// keeps the pair-bias gradient of all N queries of its key block in registers)
+bool shape_ok(int64_t B, int64_t N, int64_t H, int64_t D, int64_t max_n) {
+  return B >= 1 && N >= 1 && H >= 1 && (D == 16 || D == 32) && N <= max_n && B <= (1 << 20) &&
          H <= (1 << 12) && B * N * H * (round_up(N, 128) / 16) <= INT32_MAX;
 }
 
@@ -1234,12 +1236,12 @@ const char* tri_attn_status_string(int status) {
 }
 
 size_t tri_attn_fwd_workspace_bytes(int64_t B, int64_t N, int64_t H, int64_t D) {
-  if (!shape_ok(B, N, H, D)) return 0;
+  if (!shape_ok(B, N, H, D, TRI_ATTN_FWD_MAX_N)) return 0;
   return (size_t)make_plan(B, N, H, D).bias_f32_bytes;
 }
 
 size_t tri_attn_bwd_workspace_bytes(int64_t B, int64_t N, int64_t H, int64_t D) {
-  if (!shape_ok(B, N, H, D)) return 0;
+  if (!shape_ok(B, N, H, D, TRI_ATTN_MAX_N)) return 0;
   return (size_t)make_plan(B, N, H, D).bwd_bytes;
 }
 
@@ -1249,7 +1251,7 @@ tri_attn_status tri_attn_fwd_ex(unsigned stages, int layout, int64_t B, int64_t 
                                 size_t workspace_bytes, hipStream_t stream) {
   if (stages & ~TRI_ATTN_STAGE_ALL) return TRI_ATTN_ERROR_INVALID_VALUE;
   if (B < 1 || N < 1 || H < 1) return TRI_ATTN_ERROR_INVALID_VALUE;
-  if (!shape_ok(B, N, H, D)) return TRI_ATTN_ERROR_UNSUPPORTED;
+  if (!shape_ok(B, N, H, D, TRI_ATTN_FWD_MAX_N)) return TRI_ATTN_ERROR_UNSUPPORTED;
   if (!q || !k || !v || !bias || !o || !lse) return TRI_ATTN_ERROR_INVALID_VALUE;
   const Plan P = make_plan(B, N, H, D);
   TokLayout L;
@@ -1296,7 +1298,7 @@ tri_attn_status tri_attn_bwd_ex(unsigned stages, int layout, int64_t B, int64_t 
                                 size_t workspace_bytes, hipStream_t stream) {
   if (stages & ~TRI_ATTN_STAGE_ALL) return TRI_ATTN_ERROR_INVALID_VALUE;
   if (B < 1 || N < 1 || H < 1) return TRI_ATTN_ERROR_INVALID_VALUE;
-  if (!shape_ok(B, N, H, D)) return TRI_ATTN_ERROR_UNSUPPORTED;
+  if (!shape_ok(B, N, H, D, TRI_ATTN_MAX_N)) return TRI_ATTN_ERROR_UNSUPPORTED;
   if (!q || !k || !v || !bias || !o || !lse || !dO || !dq || !dk || !dv || !dbias) return TRI_ATTN_ERROR_INVALID_VALUE;
   const Plan P = make_plan(B, N, H, D);
   TokLayout L;
