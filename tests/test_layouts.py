@@ -70,6 +70,8 @@ CASES = [
     (1, 200, 2, 32, True, False),
     (1, 450, 1, 16, False, True),
     (1, 384, 4, 32, True, True),
+    (1, 640, 2, 16, True, True),   # five query steps
+    (1, 768, 2, 32, False, True),  # six query steps: the largest backward instantiation
 ]
 
 
