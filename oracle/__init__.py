@@ -40,6 +40,8 @@ from .tri_attn_oracle import (  # noqa: F401
 )
 from .tri_mul_oracle import (  # noqa: F401
     DIRECTIONS,
+    gate_backward64,
+    gate_forward64,
     tri_mul_backward64,
     tri_mul_forward64,
     tri_mul_loops64,

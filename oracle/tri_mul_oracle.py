@@ -85,3 +85,30 @@ def tri_mul_loops64(a: np.ndarray, b: np.ndarray, direction: str = "outgoing") -
                             s += a[bb, k, i, c] * b[bb, k, j, c]
                     x[bb, i, j, c] = s
     return x
+
+
+# ---------------------------------------------------------------------------- input gating
+# The same section of the article names elementwise gating as the update's first step.  The
+# plainest reading, as in AlphaFold-family models: each operand of the product is a projection
+# of the pair representation gated elementwise by the sigmoid of another projection, and pair
+# entries outside the pair mask contribute nothing:
+#   a[b,i,j,c] = sigmoid(g[b,i,j,c]) * p[b,i,j,c] * mask[b,i,j]
+def _sigmoid64(x):
+    x = np.asarray(x, dtype=np.float64)
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+def gate_forward64(g, p, mask=None):
+    """a = sigmoid(g) * p (* mask[..., None]); g, p: [B, N, N, C]; mask: [B, N, N] or None."""
+    a = _sigmoid64(g) * np.asarray(p, dtype=np.float64)
+    if mask is not None:
+        a = a * np.asarray(mask, dtype=np.float64)[..., None]
+    return a
+
+
+def gate_backward64(g, p, da, mask=None):
+    """(dg, dp) for upstream gradient da: dp = da * sigmoid(g) * m, dg = da * p * m * s (1 - s)."""
+    s = _sigmoid64(g)
+    m = 1.0 if mask is None else np.asarray(mask, dtype=np.float64)[..., None]
+    da = np.asarray(da, dtype=np.float64) * m
+    return da * np.asarray(p, dtype=np.float64) * s * (1.0 - s), da * s

@@ -102,3 +102,36 @@ def test_bilinear_adjoint_identity(direction):
     ref = float((dx * x).sum())
     assert abs(float((da * a).sum()) - ref) < 1e-9 * max(1.0, abs(ref))
     assert abs(float((db * b).sum()) - ref) < 1e-9 * max(1.0, abs(ref))
+
+
+def test_gate_closed_forms():
+    rng = np.random.default_rng(20)
+    p = rng.standard_normal((1, 4, 4, 3))
+    # sigmoid(0) = 1/2 exactly; sigmoid(+-40) is 1 and 0 to double precision
+    assert np.array_equal(oracle.gate_forward64(np.zeros_like(p), p), p / 2)
+    np.testing.assert_allclose(oracle.gate_forward64(np.full_like(p, 40.0), p), p, rtol=1e-15, atol=0)
+    np.testing.assert_allclose(oracle.gate_forward64(np.full_like(p, -40.0), p), 0 * p, rtol=0, atol=1e-16)
+    # sigmoid(x) + sigmoid(-x) = 1
+    g = rng.standard_normal(p.shape) * 3
+    np.testing.assert_allclose(oracle.gate_forward64(g, p) + oracle.gate_forward64(-g, p), p, rtol=1e-14, atol=1e-14)
+    # masked pair entries give zeros in every channel
+    m = (rng.random((1, 4, 4)) > 0.5).astype(np.uint8)
+    a = oracle.gate_forward64(g, p, m)
+    assert np.all(a[m == 0] == 0) and np.array_equal(a[m == 1], oracle.gate_forward64(g, p)[m == 1])
+
+
+def test_gate_gradients_by_central_differences():
+    rng = np.random.default_rng(21)
+    g, p, da = (rng.standard_normal((1, 3, 3, 2)) for _ in range(3))
+    m = np.array([[[1, 0, 1], [1, 1, 0], [0, 1, 1]]], dtype=np.uint8)
+    dg, dp = oracle.gate_backward64(g, p, da, m)
+
+    def loss(gg, pp):
+        return float((oracle.gate_forward64(gg, pp, m) * da).sum())
+
+    eps = 1e-6
+    for idx in np.ndindex(g.shape):
+        e = np.zeros_like(g)
+        e[idx] = eps
+        assert abs((loss(g + e, p) - loss(g - e, p)) / (2 * eps) - dg[idx]) < 1e-7, ("dg", idx)
+        assert abs((loss(g, p + e) - loss(g, p - e)) / (2 * eps) - dp[idx]) < 1e-7, ("dp", idx)
