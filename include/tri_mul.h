@@ -100,6 +100,26 @@ tri_attn_status tri_mul_bwd(int direction, int layout, int64_t B, int64_t N, int
                             const void *a, const void *b, const void *dx, void *da, void *db,
                             void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Input gating of the update (the article's elementwise gating step; plainest reading as in
+ * AlphaFold-family models): a = sigmoid(g) * p * mask[b, i, j], in FP32, rounded once to bf16.
+ *   g, p     : bf16 [B, N, N, C], channels last (the layout projections of the pair
+ *              representation produce); C a multiple of 8
+ *   mask     : uint8 [B, N, N] (1 keep, 0 drop: the whole pair entry is zero), or NULL
+ *   a        : bf16 in `layout`: channels last, or channels first [B, C, N, N] (N a multiple of
+ *              8), so that the gated operand is written once, ready for the fast product
+ * The backward takes da in the same layout and writes dg, dp channels last:
+ *   dp = da * mask * sigmoid(g),   dg = da * mask * p * sigmoid(g) * (1 - sigmoid(g)).
+ * Errors as for tri_mul_fwd (INVALID_VALUE also for an output overlapping an input).
+ */
+tri_attn_status tri_mul_gate_fwd(int layout, int64_t B, int64_t N, int64_t C,
+                                 const void *g, const void *p, const uint8_t *mask, void *a,
+                                 hipStream_t stream);
+
+tri_attn_status tri_mul_gate_bwd(int layout, int64_t B, int64_t N, int64_t C,
+                                 const void *g, const void *p, const uint8_t *mask, const void *da,
+                                 void *dg, void *dp, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

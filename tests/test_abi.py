@@ -202,3 +202,22 @@ def test_tri_mul_validation(lib):
     assert bwd(0, 1, 64, 32, db=da + 1024) == INVALID
     assert bwd(1, 1, 64, 32, da=dx) == INVALID
     assert bwd(0, 1, 64, 32, dx=0) == INVALID
+
+
+def test_tri_mul_gate_validation(lib):
+    g, p, a, da, dg, dp = _ptrs(6)
+    fwd = lambda lay, B, N, C, **k: ta.tri_mul_gate_fwd(lay, B, N, C, k.get("g", g), k.get("p", p), k.get("m"),
+                                                          k.get("a", a), stream=0)
+    bwd = lambda lay, B, N, C, **k: ta.tri_mul_gate_bwd(lay, B, N, C, k.get("g", g), k.get("p", p), k.get("m"),
+                                                          k.get("da", da), k.get("dg", dg), k.get("dp", dp), stream=0)
+    for f in (fwd, bwd):
+        assert f(2, 1, 64, 32) == INVALID
+        assert f(0, 0, 64, 32) == INVALID
+        assert f(0, 1, 64, 12) == UNSUPPORTED     # C a multiple of 8
+        assert f(1, 1, 60, 16) == UNSUPPORTED     # channels first: N a multiple of 8
+        assert f(0, 1, 1025, 16) == UNSUPPORTED
+        assert f(0, 1, 64, 32, g=0) == INVALID
+        assert f(0, 1, 64, 32, p=p + 8) == MISALIGNED
+    assert fwd(0, 1, 64, 32, a=g + 64) == INVALID
+    assert bwd(0, 1, 64, 32, dg=dp) == INVALID
+    assert bwd(0, 1, 64, 32, dp=da + 32) == INVALID

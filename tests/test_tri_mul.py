@@ -7,7 +7,8 @@ x[i,j,c] = sum_k a[k,i,c] b[k,j,c], and the gradients da, db.
 
 Bound, from the arithmetic (exact bf16 products, FP32 sums of at most N <= 1024 terms, one
 final rounding to bf16): every element within 2^-8 |ref| + 2^-13 sum_k |a||b| of the FP64
-value (half an ulp of bf16 is 2^-9 relative; n u_fp32 <= 2^-14), and rel-RMSE <= 3e-3.
+value (the rounding to bf16 errs by at most its unit roundoff, 2^-8 relative; the FP32 sum by
+at most n u_fp32 sum|ab| <= 2^-14 sum|ab|, taken twice), and rel-RMSE <= 3e-3.
 """
 import numpy as np
 import pytest

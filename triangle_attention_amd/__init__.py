@@ -21,7 +21,8 @@ __all__ = [
     "TriAttnError", "load_library", "tri_attn_status_string", "tri_attn_fwd_workspace_bytes",
     "tri_attn_bwd_workspace_bytes", "tri_attn_fwd", "tri_attn_bwd", "tri_attn_fwd_stages", "tri_attn_bwd_stages",
     "tri_attn_fwd_ex", "tri_attn_bwd_ex", "triangle_attention", "TRI_ATTN_MAX_N", "TRI_ATTN_FWD_MAX_N", "LAYOUTS",
-    "tri_mul_fwd", "tri_mul_bwd", "tri_mul_workspace_bytes", "triangle_multiplication", "TRI_MUL_DIRECTIONS", "TRI_MUL_LAYOUTS",
+    "tri_mul_fwd", "tri_mul_bwd", "tri_mul_workspace_bytes", "tri_mul_gate_fwd", "tri_mul_gate_bwd",
+    "triangle_multiplication", "gated_operand", "TRI_MUL_DIRECTIONS", "TRI_MUL_LAYOUTS",
     "TRI_MUL_MAX_N",
 ]
 
@@ -66,6 +67,10 @@ def load_library(path: str = LIB_PATH):
     lib.tri_attn_fwd_ex.restype = ctypes.c_int
     lib.tri_attn_bwd_ex.argtypes = [ctypes.c_uint, ctypes.c_int] + lib.tri_attn_bwd.argtypes
     lib.tri_attn_bwd_ex.restype = ctypes.c_int
+    lib.tri_mul_gate_fwd.argtypes = [ctypes.c_int, i64, i64, i64, vp, vp, vp, vp, vp]
+    lib.tri_mul_gate_fwd.restype = ctypes.c_int
+    lib.tri_mul_gate_bwd.argtypes = [ctypes.c_int, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp]
+    lib.tri_mul_gate_bwd.restype = ctypes.c_int
     lib.tri_mul_workspace_bytes.argtypes = [ctypes.c_int, i64, i64, i64]
     lib.tri_mul_workspace_bytes.restype = sz
     lib.tri_mul_fwd.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, vp, vp, vp, vp, sz, vp]
@@ -154,6 +159,18 @@ def tri_attn_bwd_ex(stages, layout, B, N, H, D, q, k, v, bias, key_mask, o, lse,
                                               _ptr(key_mask), _ptr(o), _ptr(lse), _ptr(residual), _ptr(dO),
                                               _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbias), _ptr(workspace),
                                               int(workspace_bytes), _stream(stream)))
+
+
+def tri_mul_gate_fwd(layout, B, N, C, g, p, mask, a, stream=None) -> int:
+    """Marshal to the C entry point (include/tri_mul.h); returns the status code."""
+    return int(load_library().tri_mul_gate_fwd(layout, B, N, C, _ptr(g), _ptr(p), _ptr(mask), _ptr(a),
+                                               _stream(stream)))
+
+
+def tri_mul_gate_bwd(layout, B, N, C, g, p, mask, da, dg, dp, stream=None) -> int:
+    """Marshal to the C entry point (include/tri_mul.h); returns the status code."""
+    return int(load_library().tri_mul_gate_bwd(layout, B, N, C, _ptr(g), _ptr(p), _ptr(mask), _ptr(da), _ptr(dg),
+                                               _ptr(dp), _stream(stream)))
 
 
 def tri_mul_workspace_bytes(layout, B, N, C) -> int:
@@ -303,3 +320,33 @@ def triangle_multiplication(a, b, direction="outgoing", layout="channels_last"):
     layout "channels_first": [B, C, N, N] (N a multiple of 8), the faster form.
     """
     return _TriMulFn.apply(a, b, direction, layout)
+
+
+class _GateFn(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, g, p, mask, layout):
+        if g.dim() != 4 or tuple(p.shape) != tuple(g.shape) or g.shape[1] != g.shape[2]:
+            raise ValueError("g and p must both be channels-last [B, N, N, C]")
+        B, N, _, C = g.shape
+        lay = TRI_MUL_LAYOUTS[layout]
+        a = torch.empty((B, C, N, N) if lay == 1 else (B, N, N, C), dtype=g.dtype, device=g.device)
+        _check(tri_mul_gate_fwd(lay, B, N, C, g, p, mask, a), "tri_mul_gate_fwd")
+        ctx.save_for_backward(g, p, mask)
+        ctx.lay = lay
+        return a
+
+    @staticmethod
+    def backward(ctx, da):
+        g, p, mask = ctx.saved_tensors
+        B, N, _, C = g.shape
+        dg, dp = torch.empty_like(g), torch.empty_like(p)
+        _check(tri_mul_gate_bwd(ctx.lay, B, N, C, g, p, mask, da.contiguous(), dg, dp), "tri_mul_gate_bwd")
+        return dg, dp, None, None
+
+
+def gated_operand(g, p, mask=None, layout="channels_first"):
+    """a = sigmoid(g) * p * mask, differentiable in g and p: the gated operand of the triangle
+    multiplication, from channels-last projections g, p [B, N, N, C] (bf16) and an optional
+    uint8 pair mask [B, N, N]; returned in `layout` (channels first [B, C, N, N] by default,
+    ready for triangle_multiplication(..., layout="channels_first"))."""
+    return _GateFn.apply(g, p, mask, layout)

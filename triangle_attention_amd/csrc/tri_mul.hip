@@ -423,6 +423,113 @@ void transpose_kernel(const bf16* __restrict__ in, bf16* __restrict__ out, int64
   }
 }
 
+// ------------------------------------------------------------------ input gating
+// a = sigmoid(g) * p * mask[position] in FP32, rounded once to bf16; g and p channels last
+// [B][N*N][C].  With CF the result leaves channels first [B][C][N*N] through a 64 x 64 LDS tile
+// (positions x channels), like the layout change, so that gating and layout change cost one
+// pass over HBM.  The backward reads da in the same layout and writes dg, dp channels last:
+//   dp = da * m * sigmoid(g),   dg = da * m * p * sigmoid(g) (1 - sigmoid(g)).
+__device__ __forceinline__ float bf_lo(unsigned w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(unsigned w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ unsigned pack_bf16(float lo, float hi) {
+  const bf16 l = (bf16)lo, h = (bf16)hi;
+  return (unsigned)__builtin_bit_cast(unsigned short, l) | ((unsigned)__builtin_bit_cast(unsigned short, h) << 16);
+}
+__device__ __forceinline__ float sigmoid_f32(float x) {
+  return 1.0f / (1.0f + __builtin_amdgcn_exp2f(-x * 1.4426950408889634f));
+}
+
+template <bool CF>
+__global__ __launch_bounds__(256)
+void gate_fwd_kernel(const bf16* __restrict__ g, const bf16* __restrict__ p, const uint8_t* __restrict__ mask,
+                     bf16* __restrict__ a, int64_t R, int64_t K, int64_t tilesR, int64_t tilesK) {
+  __shared__ __attribute__((aligned(16))) unsigned short T[TP * TPS];
+  const int64_t per = tilesR * tilesK;
+  const int64_t b = blockIdx.x / per, rem = blockIdx.x % per;
+  const int64_t r0 = (rem / tilesK) * TP, k0 = (rem % tilesK) * TP;
+  const int64_t base = b * R * K;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int e = 0; e < 2; e++) {  // chunk (position r, channels kc*8..+7)
+    const int ch = tid + e * 256, r = ch >> 3, kc = ch & 7;
+    u32x4 out = {0u, 0u, 0u, 0u};
+    const bool ok = r0 + r < R && k0 + kc * 8 < K;
+    if (ok) {
+      const int64_t off = base + (r0 + r) * K + k0 + kc * 8;
+      const u32x4 gv = *(const u32x4*)(g + off), pv = *(const u32x4*)(p + off);
+      const float m = (mask && mask[b * R + r0 + r] == 0) ? 0.0f : 1.0f;
+#pragma unroll
+      for (int d = 0; d < 4; d++)
+        out[d] = pack_bf16(sigmoid_f32(bf_lo(gv[d])) * bf_lo(pv[d]) * m, sigmoid_f32(bf_hi(gv[d])) * bf_hi(pv[d]) * m);
+      if (!CF) *(u32x4*)(a + off) = out;
+    }
+    if (CF) *(__attribute__((address_space(3))) u32x4*)(T + r * TPS + kc * 8) = out;
+  }
+  if (!CF) return;
+  __syncthreads();
+  unsigned short* dst = (unsigned short*)a + base;
+#pragma unroll
+  for (int e = 0; e < 2; e++) {  // output chunk (channel k, positions rc*8..+7)
+    const int ch = tid + e * 256, k = ch >> 3, rc = ch & 7;
+    if (k0 + k < K && r0 + rc * 8 < R) {
+      unsigned w[4];
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+        w[i] = (unsigned)T[(rc * 8 + 2 * i) * TPS + k] | ((unsigned)T[(rc * 8 + 2 * i + 1) * TPS + k] << 16);
+      const u32x4 v = {w[0], w[1], w[2], w[3]};
+      *(u32x4*)(dst + (k0 + k) * R + r0 + rc * 8) = v;
+    }
+  }
+}
+
+template <bool CF>
+__global__ __launch_bounds__(256)
+void gate_bwd_kernel(const bf16* __restrict__ g, const bf16* __restrict__ p, const uint8_t* __restrict__ mask,
+                     const bf16* __restrict__ da, bf16* __restrict__ dg, bf16* __restrict__ dp, int64_t R, int64_t K,
+                     int64_t tilesR, int64_t tilesK) {
+  __shared__ __attribute__((aligned(16))) unsigned short T[TP * TPS];
+  const int64_t per = tilesR * tilesK;
+  const int64_t b = blockIdx.x / per, rem = blockIdx.x % per;
+  const int64_t r0 = (rem / tilesK) * TP, k0 = (rem % tilesK) * TP;
+  const int64_t base = b * R * K;
+  const int tid = threadIdx.x;
+  if (CF) {  // da channels first: chunks (channel k, 8 positions) into T[position][channel]
+#pragma unroll
+    for (int e = 0; e < 2; e++) {
+      const int ch = tid + e * 256, k = ch >> 3, rc = ch & 7;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (k0 + k < K && r0 + rc * 8 < R) v = *(const u32x4*)(da + base + (k0 + k) * R + r0 + rc * 8);
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        T[(rc * 8 + 2 * i) * TPS + k] = (unsigned short)(v[i] & 0xFFFFu);
+        T[(rc * 8 + 2 * i + 1) * TPS + k] = (unsigned short)(v[i] >> 16);
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int e = 0; e < 2; e++) {  // chunk (position r, channels kc*8..+7)
+    const int ch = tid + e * 256, r = ch >> 3, kc = ch & 7;
+    if (r0 + r < R && k0 + kc * 8 < K) {
+      const int64_t off = base + (r0 + r) * K + k0 + kc * 8;
+      const u32x4 gv = *(const u32x4*)(g + off), pv = *(const u32x4*)(p + off);
+      const u32x4 dv = CF ? *(const __attribute__((address_space(3))) u32x4*)(T + r * TPS + kc * 8)
+                          : *(const u32x4*)(da + off);
+      const float m = (mask && mask[b * R + r0 + r] == 0) ? 0.0f : 1.0f;
+      u32x4 og, op;
+#pragma unroll
+      for (int d = 0; d < 4; d++) {
+        const float s0 = sigmoid_f32(bf_lo(gv[d])), s1 = sigmoid_f32(bf_hi(gv[d]));
+        const float d0 = bf_lo(dv[d]) * m, d1 = bf_hi(dv[d]) * m;
+        op[d] = pack_bf16(d0 * s0, d1 * s1);
+        og[d] = pack_bf16(d0 * bf_lo(pv[d]) * (s0 * (1.0f - s0)), d1 * bf_hi(pv[d]) * (s1 * (1.0f - s1)));
+      }
+      *(u32x4*)(dg + off) = og;
+      *(u32x4*)(dp + off) = op;
+    }
+  }
+}
+
 void transpose(const void* in, void* out, int64_t B, int64_t R, int64_t K, hipStream_t st) {
   const int64_t tr = (R + TP - 1) / TP, tk = (K + TP - 1) / TP;
   hipLaunchKernelGGL(transpose_kernel, dim3((unsigned)(B * tr * tk)), dim3(256), 0, st, (const bf16*)in, (bf16*)out,
@@ -576,6 +683,52 @@ tri_attn_status tri_mul_bwd(int direction, int layout, int64_t B, int64_t N, int
     r2 = launch(a, dx, db, B, N, C, MulStrides{NC, C, C, NC, NC, C}, stream);
   }
   return r1 != TRI_ATTN_SUCCESS ? r1 : r2;
+}
+
+tri_attn_status tri_mul_gate_fwd(int layout, int64_t B, int64_t N, int64_t C, const void* g, const void* p,
+                                 const uint8_t* mask, void* a, hipStream_t stream) {
+  if (layout != TRI_MUL_CHANNELS_LAST && layout != TRI_MUL_CHANNELS_FIRST) return TRI_ATTN_ERROR_INVALID_VALUE;
+  if (B < 1 || N < 1 || C < 1 || !g || !p || !a) return TRI_ATTN_ERROR_INVALID_VALUE;
+  if (C % 8 != 0 || C > 1024 || N > TRI_MUL_MAX_N || B > (1 << 16) ||
+      (layout == TRI_MUL_CHANNELS_FIRST && N % 8 != 0))
+    return TRI_ATTN_ERROR_UNSUPPORTED;
+  const int64_t bytes = B * N * N * C * 2;
+  if (overlap({a, bytes}, {g, bytes}) || overlap({a, bytes}, {p, bytes}) ||
+      (mask && overlap({a, bytes}, {mask, B * N * N})))
+    return TRI_ATTN_ERROR_INVALID_VALUE;
+  if (!aligned16(g) || !aligned16(p) || !aligned16(a)) return TRI_ATTN_ERROR_MISALIGNED;
+  const int64_t R = N * N, tr = (R + TP - 1) / TP, tk = (C + TP - 1) / TP;
+  if (layout == TRI_MUL_CHANNELS_FIRST)
+    hipLaunchKernelGGL(gate_fwd_kernel<true>, dim3((unsigned)(B * tr * tk)), dim3(256), 0, stream, (const bf16*)g,
+                       (const bf16*)p, mask, (bf16*)a, R, C, tr, tk);
+  else
+    hipLaunchKernelGGL(gate_fwd_kernel<false>, dim3((unsigned)(B * tr * tk)), dim3(256), 0, stream, (const bf16*)g,
+                       (const bf16*)p, mask, (bf16*)a, R, C, tr, tk);
+  return hipGetLastError() == hipSuccess ? TRI_ATTN_SUCCESS : TRI_ATTN_ERROR_LAUNCH;
+}
+
+tri_attn_status tri_mul_gate_bwd(int layout, int64_t B, int64_t N, int64_t C, const void* g, const void* p,
+                                 const uint8_t* mask, const void* da, void* dg, void* dp, hipStream_t stream) {
+  if (layout != TRI_MUL_CHANNELS_LAST && layout != TRI_MUL_CHANNELS_FIRST) return TRI_ATTN_ERROR_INVALID_VALUE;
+  if (B < 1 || N < 1 || C < 1 || !g || !p || !da || !dg || !dp) return TRI_ATTN_ERROR_INVALID_VALUE;
+  if (C % 8 != 0 || C > 1024 || N > TRI_MUL_MAX_N || B > (1 << 16) ||
+      (layout == TRI_MUL_CHANNELS_FIRST && N % 8 != 0))
+    return TRI_ATTN_ERROR_UNSUPPORTED;
+  const int64_t bytes = B * N * N * C * 2;
+  const Range ins[] = {{g, bytes}, {p, bytes}, {da, bytes}, {mask, mask ? B * N * N : 0}};
+  for (const Range& r : ins)
+    if (r.p && (overlap({dg, bytes}, r) || overlap({dp, bytes}, r))) return TRI_ATTN_ERROR_INVALID_VALUE;
+  if (overlap({dg, bytes}, {dp, bytes})) return TRI_ATTN_ERROR_INVALID_VALUE;
+  if (!aligned16(g) || !aligned16(p) || !aligned16(da) || !aligned16(dg) || !aligned16(dp))
+    return TRI_ATTN_ERROR_MISALIGNED;
+  const int64_t R = N * N, tr = (R + TP - 1) / TP, tk = (C + TP - 1) / TP;
+  if (layout == TRI_MUL_CHANNELS_FIRST)
+    hipLaunchKernelGGL(gate_bwd_kernel<true>, dim3((unsigned)(B * tr * tk)), dim3(256), 0, stream, (const bf16*)g,
+                       (const bf16*)p, mask, (const bf16*)da, (bf16*)dg, (bf16*)dp, R, C, tr, tk);
+  else
+    hipLaunchKernelGGL(gate_bwd_kernel<false>, dim3((unsigned)(B * tr * tk)), dim3(256), 0, stream, (const bf16*)g,
+                       (const bf16*)p, mask, (const bf16*)da, (bf16*)dg, (bf16*)dp, R, C, tr, tk);
+  return hipGetLastError() == hipSuccess ? TRI_ATTN_SUCCESS : TRI_ATTN_ERROR_LAUNCH;
 }
 
 }  // extern "C"
