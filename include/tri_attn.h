@@ -50,9 +50,10 @@
 extern "C" {
 #endif
 
-/* Largest N of the backward: its work-group keeps the pair-bias gradient of all N queries of
- * its 64-key block in registers. */
-#define TRI_ATTN_MAX_N 768
+/* Largest N of the backward (and of a forward that feeds it).  Up to N = 768 a work-group keeps
+ * the pair-bias gradient of all queries of its 64-key block in registers; longer slices are
+ * split into chunks of 768 queries whose dK / dV are summed in FP32 (more workspace). */
+#define TRI_ATTN_MAX_N 2048
 /* Largest N of the forward alone (inference on longer crops): the forward streams keys and has
  * no such per-query state. */
 #define TRI_ATTN_FWD_MAX_N 4096

@@ -56,10 +56,16 @@ def test_workspace_sizes(lib):
         assert ta.tri_attn_fwd_workspace_bytes(*bad) == 0
         assert ta.tri_attn_bwd_workspace_bytes(*bad) == 0
     # the forward alone reaches TRI_ATTN_FWD_MAX_N; the backward stops at TRI_ATTN_MAX_N
-    assert ta.TRI_ATTN_MAX_N == 768 and ta.TRI_ATTN_FWD_MAX_N == 4096
-    assert ta.tri_attn_fwd_workspace_bytes(1, 769, 1, 16) > 0
+    assert ta.TRI_ATTN_MAX_N == 2048 and ta.TRI_ATTN_FWD_MAX_N == 4096
+    assert ta.tri_attn_fwd_workspace_bytes(1, 2049, 1, 16) > 0
     assert ta.tri_attn_fwd_workspace_bytes(1, 4096, 4, 32) > 0
-    assert ta.tri_attn_bwd_workspace_bytes(1, 769, 1, 16) == 0
+    assert ta.tri_attn_bwd_workspace_bytes(1, 2049, 1, 16) == 0
+    assert ta.tri_attn_bwd_workspace_bytes(1, 2048, 1, 16) > 0
+    # past six 128-query steps the backward runs in query chunks and adds FP32 dK / dV partials
+    # per chunk: two chunks at N = 769, three at N = 2048
+    for N, nqc in [(769, 2), (1536, 2), (1537, 3), (2048, 3)]:
+        b = ta.tri_attn_bwd_workspace_bytes(1, N, 2, 32)
+        assert b >= -(-N // 64) * N * 2 * N * 32 * 2 + 2 * nqc * N * 2 * N * 32 * 4, N
     # the backward partial buffers grow with N (dq partials per 64-key block)
     assert ta.tri_attn_bwd_workspace_bytes(1, 768, 4, 32) > ta.tri_attn_bwd_workspace_bytes(1, 384, 4, 32)
 
@@ -90,7 +96,7 @@ def test_fwd_validation(lib):
     assert _fwd(shape=(1, 64, 4, 64)) == UNSUPPORTED
     assert _fwd(shape=(1, 64, 4, 8)) == UNSUPPORTED
     assert _fwd(shape=(1, 4097, 4, 16)) == UNSUPPORTED
-    assert _fwd(shape=(1, 769, 4, 16), wsb=16) == WORKSPACE  # a forward-only crop past the backward's limit
+    assert _fwd(shape=(1, 2049, 4, 16), wsb=16) == WORKSPACE  # a forward-only crop past the backward's limit
     for idx in range(6):  # q, k, v, bias, o, lse are required
         p = _ptrs(8)
         p[idx] = 0
@@ -113,7 +119,9 @@ def test_fwd_validation(lib):
 
 def test_bwd_validation(lib):
     assert _bwd(shape=(1, 64, 4, 48)) == UNSUPPORTED
-    assert _bwd(shape=(1, 769, 4, 16), wsb=1 << 40) == UNSUPPORTED
+    assert _bwd(shape=(1, 2049, 4, 16), wsb=1 << 40) == UNSUPPORTED
+    # a chunked backward (N past 768) checks its larger workspace
+    assert _bwd(shape=(1, 769, 4, 16), wsb=ta.tri_attn_bwd_workspace_bytes(1, 768, 4, 16)) == WORKSPACE
     assert _bwd(shape=(2, 0, 4, 16)) == INVALID
     for idx in (0, 1, 2, 3, 4, 5, 7, 8, 9, 10, 11):  # every tensor except the residual is required
         p = _ptrs(14)

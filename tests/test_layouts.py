@@ -72,6 +72,8 @@ CASES = [
     (1, 384, 4, 32, True, True),
     (1, 640, 2, 16, True, True),   # five query steps
     (1, 768, 2, 32, False, True),  # six query steps: the largest backward instantiation
+    (1, 900, 1, 16, True, True),   # two query chunks (six steps, then two)
+    (1, 1664, 1, 32, False, True), # three query chunks (six, six, one)
 ]
 
 

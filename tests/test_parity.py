@@ -143,8 +143,59 @@ def test_workload_sampled_parity(name):
         assert float(out["dv"][:, :, :, w.N - w.mask_tail:].float().abs().max()) == 0.0
 
 
+# backward past six 128-query steps: query chunks of 768 whose dK / dV partials are summed in FP32
+# (two chunks at N = 900 and 1100, three at N = 2048, the last chunk shorter each time); sampled
+# slices element by element, sampled dbias rows, the invariants, and a bitwise repeat
+@pytest.mark.parametrize("B,N,H,D,masked", [(1, 900, 2, 32, False), (1, 1100, 1, 16, True), (1, 2048, 1, 16, True)])
+def test_chunked_backward_long_crops(B, N, H, D, masked):
+    import triangle_attention_amd as ta
+    print(f"chunked backward B={B} N={N} H={H} D={D} masked={masked}", flush=True)
+    assert N > 768 and ta.tri_attn_bwd_workspace_bytes(B, N, H, D) > 0
+    inp = make_inputs(B, N, H, D, seed=7 * N + D, bias_std=2.0)
+    rng = np.random.default_rng(N + 5)
+    if masked:
+        m = (rng.random((B, N, N)) > 0.3).astype(np.uint8)
+        m[:, :, N - 1] = 1
+        m[:, :, N - 40:N - 8] = 0  # fully masked keys inside the last key block
+        inp["key_mask"] = m
+    out = run_gpu(inp)
+    again = run_gpu(inp)
+    for n in ("o", "lse", "dq", "dk", "dv", "dbias"):
+        assert torch.equal(out[n], again[n]), n
+    x = inputs64(inp)
+    # slices from the first and the last query chunk, and the last slice
+    slices = sorted(set(rng.choice(N, size=2, replace=False).tolist() + [0, N - 1]))
+    o64, lse64 = oracle.forward64(x["q"], x["k"], x["v"], x["bias"], x["key_mask"], slices=slices)
+    dq64, dk64, dv64, _ = oracle.backward64(x["q"], x["k"], x["v"], x["bias"], x["dO"], x["key_mask"], slices=slices)
+    sl = (slice(None), slices)
+    o = f64(out["o"])[sl]
+    errs = dict(o_maxabs=maxabs(o, o64[sl]), o=rrmse(o, o64[sl]), lse=maxabs(f64(out["lse"])[sl], lse64[sl]),
+                dq=rrmse(f64(out["dq"])[sl], dq64[sl]), dk=rrmse(f64(out["dk"])[sl], dk64[sl]),
+                dv=rrmse(f64(out["dv"])[sl], dv64[sl]))
+    # dbias rows of queries in every chunk (rows 0..767 first chunk, 768.. the next ones)
+    js = [0, 767, 768, N - 1] + rng.integers(0, N, 3).tolist()
+    rows = [(0, int(rng.integers(0, H)), int(j)) for j in js]
+    db64 = oracle.dbias_rows64(x["q"], x["k"], x["v"], x["bias"], x["dO"], rows, x["key_mask"])
+    db = f64(out["dbias"])
+    errs["dbias"] = rrmse(np.stack([db[b, h, j] for b, h, j in rows]), db64)
+    print(f"N={N}", {k: f"{v:.3e}" for k, v in errs.items()}, flush=True)
+    assert errs["o_maxabs"] <= TOL_O_MAXABS and errs["o"] <= TOL_O_RRMSE and errs["lse"] <= TOL_LSE_MAXABS, errs
+    for g in ("dq", "dk", "dv", "dbias"):
+        assert errs[g] <= TOL_GRAD_RRMSE, (g, errs)
+    # per-row element checks of dk / dv keep a dropped chunk from hiding in the RMS over slices
+    for i in slices:
+        for g, ref in (("dk", dk64), ("dv", dv64)):
+            got, want = f64(out[g])[0, i], ref[0, i]
+            assert rrmse(got, want) <= TOL_GRAD_RRMSE, (g, i)
+    assert float(out["dbias"].sum(-1).abs().max()) <= 1e-3 * float(out["dbias"].abs().max()) * N ** 0.5
+    if masked:
+        assert float(out["dbias"][..., N - 40:N - 8].abs().max()) == 0.0
+        assert float(out["dk"][:, :, :, N - 40:N - 8].float().abs().max()) == 0.0
+        assert float(out["dv"][:, :, :, N - 40:N - 8].float().abs().max()) == 0.0
+
+
 # forward alone on crops past the backward's limit (inference): sampled slices, element by element
-@pytest.mark.parametrize("B,N,H,D,masked", [(1, 1100, 1, 16, True), (1, 1536, 2, 32, False)])
+@pytest.mark.parametrize("B,N,H,D,masked", [(1, 2100, 1, 16, True), (1, 2304, 1, 32, False)])
 def test_forward_only_long_crops(B, N, H, D, masked):
     import triangle_attention_amd as ta
     from tri_synth import bf16_bits_to_f64

@@ -26,7 +26,7 @@ __all__ = [
     "TRI_MUL_MAX_N",
 ]
 
-TRI_ATTN_MAX_N = 768        # backward (and a forward that feeds it)
+TRI_ATTN_MAX_N = 2048       # backward (and a forward that feeds it)
 TRI_ATTN_FWD_MAX_N = 4096   # forward alone
 TRI_MUL_MAX_N = 1024
 TRI_MUL_DIRECTIONS = {"outgoing": 0, "incoming": 1}

@@ -557,7 +557,7 @@ void bwd_pre_kernel(const bf16* __restrict__ dO, const bf16* __restrict__ o, con
 // Rows of Q, dO, K and V in LDS hold their 16-byte chunks in XOR-swizzled order (chunk c
 // of row r sits in slot c ^ swz(r)), which spreads the row-wise operand reads of a wave
 // over all LDS banks.
-constexpr int kBwdMaxSteps = 6;  // 6 steps x 128 queries = TRI_ATTN_MAX_N
+constexpr int kBwdMaxSteps = 6;  // 128-query steps of one work-group (768 queries)
 
 // s_waitcnt vmcnt(n) for a wave-uniform n in 0..15 (the instruction takes an immediate)
 __device__ __forceinline__ void wait_vmcnt(int n) {
@@ -581,12 +581,24 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
   }
 }
 
-template <int D, bool MASK, int NS, bool STRIDED>
+// Query chunks of the backward for N past six 128-query steps: a work-group keeps the pair-bias
+// gradient of its chunk's queries in registers (at most six steps), so longer slices are split
+// into chunks of six steps (the last one shorter), each its own set of work-groups.  dQ rows and
+// dbias rows of different chunks are disjoint; dK and dV sum over all queries, so chunked
+// work-groups write FP32 partials per chunk, summed in chunk order by reduce_dkv_kernel.
+struct Chunking {
+  int nst;       // 128-query steps per slice in total
+  int c_begin;   // first chunk of this launch (all of whose chunks have NS steps)
+  int ncl;       // chunks in this launch
+  float* dkvp;   // FP32 partials [chunk][dk, dv][B*N*H slice-head rows][N keys][D]
+};
+
+template <int D, bool MASK, int NS, bool STRIDED, bool CHUNKED>
 __global__ __launch_bounds__(512, 1)
 void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
                 const bf16* __restrict__ dO, const bf16* __restrict__ biasB, const uint8_t* __restrict__ mask,
                 const float* __restrict__ LDp, unsigned* __restrict__ dqp, float* __restrict__ dbp, bf16* __restrict__ dk, bf16* __restrict__ dv,
-                int B, int N, int H, int G, int ngroups, float alpha, TokLayout Lg) {
+                int B, int N, int H, int G, int ngroups, float alpha, TokLayout Lg, Chunking Ck) {
   const TokLayout L = tok_layout<STRIDED, D>(Lg, N, H);
   constexpr int NC = D / 16;
   constexpr int CPR = D / 8;    // 16-byte chunks per row
@@ -606,9 +618,14 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
 
   const int KB = (N + 63) / 64;
-  const int64_t ntiles = (int64_t)B * H * ngroups * KB;
-  const int64_t tile = xcd_tile(ntiles);
-  if (tile >= ntiles) return;
+  const int64_t per_chunk = (int64_t)B * H * ngroups * KB;
+  const int64_t ntiles = CHUNKED ? per_chunk * Ck.ncl : per_chunk;
+  const int64_t tile0 = xcd_tile(ntiles);
+  if (tile0 >= ntiles) return;
+  const int64_t tile = CHUNKED ? tile0 % per_chunk : tile0;
+  const int chunk = CHUNKED ? Ck.c_begin + (int)(tile0 / per_chunk) : 0;
+  const int s_base = chunk * kBwdMaxSteps;  // first 128-query step of this work-group's chunk
+  const int NSt = CHUNKED ? Ck.nst : NS;    // 128-query steps per slice in total
   // Tile order: the key blocks of one (head, slice group) adjacent, so that they run together
   // on one XCD and share its L2 for the slices' Q and dO rows.  In a strided layout the heads
   // of one token row also share cache lines, so there the heads come fastest.
@@ -638,18 +655,18 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   // NS = ceil(N / 128) 128-query steps per slice, fixed at compile time so that the step
   // loop, its buffer parity (for even NS) and every step offset are constants
   constexpr int nsteps = NS;
-  constexpr int Jp = NS * 128;
+  const int Jpt = NSt * 128;  // padded queries per slice (all chunks)
   const float c1 = alpha * kLog2e;
   const int sT = L.sT;
   const int span = L.span_bytes(N, D);                                   // bytes of a slice-head's rows
-  constexpr int nqt = Jp / 16;                                           // 16-query tiles per slice
+  const int nqt = Jpt / 16;                                              // 16-query tiles per slice
   const int64_t dq_kb_stride = (int64_t)B * N * H * nqt * (16 * D * 2);  // bytes of one key block's partials
   const int nitems = (i_end - i_begin) * nsteps;
 
   // Per-lane byte offset of the streamed Q and dO loads, fixed for the whole work-group; slice
   // and step enter through the buffer base and the scalar offset.  Q, dO, K and V land swizzled.
   const unsigned qd_vo = (unsigned)(((tid / CPR) * sT + ((tid % CPR) ^ swz<D>(tid / CPR)) * 8) * 2);
-  const bf16* bias_blk = biasB + ((int64_t)(b * H + h) * KB + kb) * (int64_t)nsteps * 8192;
+  const bf16* bias_blk = biasB + (((int64_t)(b * H + h) * KB + kb) * NSt + s_base) * (int64_t)8192;
 
   // Per-lane LDS byte offsets of the operand reads; the buffer and the step enter as uniform
   // additions or immediate offsets.
@@ -691,17 +708,17 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
     const int64_t tb = L.slice(b, ii, h);
     r.q = raw_rsrc(q + tb, span);
     r.dO = raw_rsrc(dO + tb, span);
-    r.ld = raw_rsrc(LDp + sl * 2 * Jp, Jp * 8);
+    r.ld = raw_rsrc(LDp + sl * 2 * Jpt, Jpt * 8);
     return r;
   };
   // issue the loads of work item (slice with row descriptors rr, step ss) into LDS buffer `buf`
   auto prefetch = [&](const RowRes& rr, int ss, int buf) {
     static_assert(2 * CPR <= 8, "Q/dO rows of a step in one load per wave");
     if (w < 2 * CPR) {
-      dma16_asm(rr.q, qd_vo, ss * 128 * sT * 2, lds0 + oQD + buf * kQDB + w * 1024);
-      dma16_asm(rr.dO, qd_vo, ss * 128 * sT * 2, lds0 + oQD + buf * kQDB + 128 * D * 2 + w * 1024);
+      dma16_asm(rr.q, qd_vo, (s_base + ss) * 128 * sT * 2, lds0 + oQD + buf * kQDB + w * 1024);
+      dma16_asm(rr.dO, qd_vo, (s_base + ss) * 128 * sT * 2, lds0 + oQD + buf * kQDB + 128 * D * 2 + w * 1024);
     }
-    if (w == 0) dma16_asm(rr.ld, (unsigned)l * 16u, ss * 1024, lds0 + oLD + buf * kLDB);
+    if (w == 0) dma16_asm(rr.ld, (unsigned)l * 16u, (s_base + ss) * 1024, lds0 + oLD + buf * kLDB);
     // this step's pair-bias tiles: 16 KiB, 2 KiB per wave
     dma16_asm(rbias, (unsigned)l * 16u, ss * 16384 + w * 2048, lds0 + oBias + buf * kBiasB + w * 2048);
     dma16_asm(rbias, (unsigned)l * 16u, ss * 16384 + w * 2048 + 1024, lds0 + oBias + buf * kBiasB + w * 2048 + 1024);
@@ -758,7 +775,7 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
 #pragma unroll
       for (int e = 0; e < 4; e++) pk[u][e] = (bf16)c[e];
     }
-    char* blk = (char*)dqp + kb * dq_kb_stride + ((prev_sl * nqt + prev_s * 8 + w) * (int64_t)(16 * D * 2));
+    char* blk = (char*)dqp + kb * dq_kb_stride + ((prev_sl * nqt + (s_base + prev_s) * 8 + w) * (int64_t)(16 * D * 2));
     // streaming stores: the partials are read back once, by the final reduction
     if (NC == 2) {
       const bf16x8 v8 = __builtin_shufflevector(pk[0], pk[NC - 1], 0, 1, 2, 3, 4, 5, 6, 7);
@@ -944,7 +961,28 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
       }
     }
     lds_barrier();
-    if (p == 0 && any_key) {
+    if (CHUNKED && p == 0 && any_key) {  // FP32 partials of this chunk, unscaled
+      const int slot2 = (kh * 2 + 1) * (2 * NR * 64) + l;
+      const int64_t rows = (int64_t)B * N * H * N;
+      float* pk = Ck.dkvp + ((int64_t)(2 * chunk) * rows + sl_row * N + kb * 64) * D;
+      float* pv = pk + rows * D;
+#pragma unroll
+      for (int R = 0; R < NR / 4; R++) {
+        f32x4 k4, v4;
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          const int r = R * 4 + e;
+          k4[e] = dkT[r] + red[slot2 + r * 64];
+          v4[e] = dvT[r] + red[slot2 + (NR + r) * 64];
+        }
+        if (kok) {
+          const int lh = lane_here();
+          const unsigned lo = (unsigned)(((kh * 32 + (lh & 31)) * D + R * 8 + (lh >> 5) * 4) * 4);
+          *(f32x4*)((char*)pk + lo) = k4;
+          *(f32x4*)((char*)pv + lo) = v4;
+        }
+      }
+    } else if (p == 0 && any_key) {
       const int slot2 = (kh * 2 + 1) * (2 * NR * 64) + l;
 #pragma unroll
       for (int R = 0; R < NR / 4; R++) {
@@ -975,7 +1013,7 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   for (int s = 0; s < NS; s++) {
 #pragma unroll
     for (int r = 0; r < 16; r++) {
-      const int jj = s * 128 + p * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
+      const int jj = (s_base + s) * 128 + p * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
       if (jj < N && kok) dst[(int64_t)jj * N + kg] = face[s][r];
     }
   }
@@ -989,13 +1027,12 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
 // lane) slot.  All loads of a thread are issued before the sum (indexes past the last partial
 // re-read it and are not added), so the kernel streams at memory speed instead of paying one
 // latency per term.
-template <int D, bool STRIDED>
+template <int D, bool STRIDED, int kMaxKB>
 __global__ __launch_bounds__(256)
 void reduce_dq_kernel(const unsigned* __restrict__ dqp, bf16* __restrict__ dq, int KB, int N, int H, int nqt,
                       int64_t nslots, float alpha, TokLayout Lg) {
   const TokLayout L = tok_layout<STRIDED, D>(Lg, N, H);
   constexpr int NC = D / 16;
-  constexpr int kMaxKB = TRI_ATTN_MAX_N / 64;
   constexpr int BLK = 16 * D * 2;  // bytes per block
   typedef typename std::conditional<NC == 2, bf16x8, bf16x4>::type V;
   // one wave per 16 x D block: the block, its slice and its rows are wave-uniform
@@ -1031,6 +1068,38 @@ void reduce_dq_kernel(const unsigned* __restrict__ dqp, bf16* __restrict__ dq, i
   }
 }
 
+// Chunked backward: dk = bf16(alpha * sum_c partial[c]), dv = bf16(sum_c partial[c]), chunks in
+// ascending order, in FP32.  One thread per 4 channels of one key row of one slice-head.
+template <int D, bool STRIDED>
+__global__ __launch_bounds__(256)
+void reduce_dkv_kernel(const float* __restrict__ dkvp, bf16* __restrict__ dk, bf16* __restrict__ dv, int N, int H,
+                       int nqc, int64_t rows, float alpha, TokLayout Lg) {
+  const TokLayout L = tok_layout<STRIDED, D>(Lg, N, H);
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= rows * (D / 4)) return;
+  const int64_t row = t / (D / 4);  // (slice-head row) * N + key
+  const int c = (int)(t % (D / 4)) * 4;
+  f32x4 sk = {}, sv = {};
+  for (int ch = 0; ch < nqc; ch++) {
+    const f32x4 a = __builtin_nontemporal_load((const f32x4*)(dkvp + ((int64_t)(2 * ch) * rows + row) * D + c));
+    const f32x4 b = __builtin_nontemporal_load((const f32x4*)(dkvp + ((int64_t)(2 * ch + 1) * rows + row) * D + c));
+    sk += a;
+    sv += b;
+  }
+  const int64_t sl = row / N;
+  const int key = (int)(row % N);
+  const int64_t bi = sl / H;
+  const int64_t off = L.slice((int)(bi / N), (int)(bi % N), (int)(sl % H)) + (int64_t)key * L.sT + c;
+  bf16x4 ok, ov;
+#pragma unroll
+  for (int e = 0; e < 4; e++) {
+    ok[e] = (bf16)(sk[e] * alpha);
+    ov[e] = (bf16)sv[e];
+  }
+  *(bf16x4*)(dk + off) = ok;
+  *(bf16x4*)(dv + off) = ov;
+}
+
 // VEC: four adjacent elements per thread (n divisible by 4, so every partial stays 16-byte aligned)
 template <bool VEC>
 __global__ __launch_bounds__(256)
@@ -1064,7 +1133,8 @@ struct Plan {
   int64_t rows;             // B*N*H*N
   int64_t bias_f32_bytes;   // prepared forward bias (FP32 tiles)
   int64_t bias_b16_bytes;   // prepared backward bias (bf16 column blocks)
-  int64_t off_LD, off_dqp, off_dbp, bwd_bytes;
+  int64_t nst, nqc;          // 128-query steps per slice; query chunks of the backward
+  int64_t off_LD, off_dqp, off_dbp, off_dkv, bwd_bytes;
 };
 
 constexpr int64_t kAlign = 256;
@@ -1083,9 +1153,11 @@ Plan make_plan(int64_t B, int64_t N, int64_t H, int64_t D) {
   p.Kp = round_up(N, 64);
   p.Jp = round_up(N, 128);
   p.KB = (N + 63) / 64;
-  // enough (b, h, key block, slice group) work-groups for ~3 per CU, with as few groups
-  // (pair-bias partials) as that allows
-  const int64_t per_group = B * H * p.KB;
+  p.nst = p.Jp / 128;
+  p.nqc = (p.nst + kBwdMaxSteps - 1) / kBwdMaxSteps;
+  // enough (b, h, key block, query chunk, slice group) work-groups for ~3 per CU, with as few
+  // groups (pair-bias partials) as that allows
+  const int64_t per_group = B * H * p.KB * p.nqc;
   int64_t groups = (768 + per_group - 1) / per_group;
   if (groups < 1) groups = 1;
   if (groups > N) groups = N;
@@ -1098,7 +1170,9 @@ Plan make_plan(int64_t B, int64_t N, int64_t H, int64_t D) {
   p.off_LD = p.bias_b16_bytes;
   p.off_dqp = p.off_LD + round_up(B * N * H * p.Jp * 2 * 4, kAlign);
   p.off_dbp = p.off_dqp + round_up(p.KB * B * N * H * p.Jp * D * 2, kAlign);
-  p.bwd_bytes = p.off_dbp + round_up(p.ngroups * B * H * N * N * 4, kAlign);
+  p.off_dkv = p.off_dbp + round_up(p.ngroups * B * H * N * N * 4, kAlign);
+  // FP32 dK / dV partials per query chunk, only when there is more than one chunk
+  p.bwd_bytes = p.off_dkv + (p.nqc > 1 ? round_up(2 * p.nqc * p.elems * 4, kAlign) : 0);
   return p;
 }
 
@@ -1182,32 +1256,50 @@ tri_attn_status launch_bwd(unsigned stages, const Plan& P, const TokLayout& L, c
                        (const bf16*)dO, (const bf16*)o, (const bf16*)res, lse, LDg, (int)P.N, (int)P.H,
                        (int)P.Jp, L);
   }
+  float* dkvp = (float*)(base + P.off_dkv);
   if (stages & TRI_ATTN_STAGE_MAIN) {
-    const int64_t ntiles = P.B * P.H * P.ngroups * P.KB;
-    auto launch = [&](auto ns_) {
+    const int64_t per_chunk = P.B * P.H * P.ngroups * P.KB;
+    auto launch = [&](auto ns_, auto chunked_, int c_begin, int ncl) {
       constexpr int NS = decltype(ns_)::value;
+      constexpr bool CH = decltype(chunked_)::value;
+      const Chunking ck{(int)P.nst, c_begin, ncl, dkvp};
+      const dim3 grid(grid_xcd(per_chunk * ncl));
       if (mask)
-        hipLaunchKernelGGL((bwd_kernel<D, true, NS, STRIDED>), dim3(grid_xcd(ntiles)), dim3(512), 0, st, (const bf16*)q,
+        hipLaunchKernelGGL((bwd_kernel<D, true, NS, STRIDED, CH>), grid, dim3(512), 0, st, (const bf16*)q,
                            (const bf16*)k, (const bf16*)v, (const bf16*)dO, biasB, mask, LDg, dqp, dbp, (bf16*)dk,
-                           (bf16*)dv, (int)P.B, (int)P.N, (int)P.H, (int)P.G, (int)P.ngroups, alpha, L);
+                           (bf16*)dv, (int)P.B, (int)P.N, (int)P.H, (int)P.G, (int)P.ngroups, alpha, L, ck);
       else
-        hipLaunchKernelGGL((bwd_kernel<D, false, NS, STRIDED>), dim3(grid_xcd(ntiles)), dim3(512), 0, st, (const bf16*)q,
+        hipLaunchKernelGGL((bwd_kernel<D, false, NS, STRIDED, CH>), grid, dim3(512), 0, st, (const bf16*)q,
                            (const bf16*)k, (const bf16*)v, (const bf16*)dO, biasB, mask, LDg, dqp, dbp, (bf16*)dk,
-                           (bf16*)dv, (int)P.B, (int)P.N, (int)P.H, (int)P.G, (int)P.ngroups, alpha, L);
+                           (bf16*)dv, (int)P.B, (int)P.N, (int)P.H, (int)P.G, (int)P.ngroups, alpha, L, ck);
     };
-    switch (P.Jp / 128) {  // 128-query steps per slice (shape_ok bounds N by TRI_ATTN_MAX_N)
-      case 1: launch(std::integral_constant<int, 1>{}); break;
-      case 2: launch(std::integral_constant<int, 2>{}); break;
-      case 3: launch(std::integral_constant<int, 3>{}); break;
-      case 4: launch(std::integral_constant<int, 4>{}); break;
-      case 5: launch(std::integral_constant<int, 5>{}); break;
-      default: launch(std::integral_constant<int, 6>{}); break;
+    auto by_steps = [&](int ns, auto chunked_, int c_begin, int ncl) {
+      switch (ns) {  // 128-query steps of the chunk (1..6)
+        case 1: launch(std::integral_constant<int, 1>{}, chunked_, c_begin, ncl); break;
+        case 2: launch(std::integral_constant<int, 2>{}, chunked_, c_begin, ncl); break;
+        case 3: launch(std::integral_constant<int, 3>{}, chunked_, c_begin, ncl); break;
+        case 4: launch(std::integral_constant<int, 4>{}, chunked_, c_begin, ncl); break;
+        case 5: launch(std::integral_constant<int, 5>{}, chunked_, c_begin, ncl); break;
+        default: launch(std::integral_constant<int, 6>{}, chunked_, c_begin, ncl); break;
+      }
+    };
+    if (P.nqc == 1) {
+      by_steps((int)P.nst, std::false_type{}, 0, 1);
+    } else {  // full chunks of six steps, then the last chunk with the remaining steps
+      const int last = (int)(P.nst - kBwdMaxSteps * (P.nqc - 1));
+      by_steps(kBwdMaxSteps, std::true_type{}, 0, (int)P.nqc - 1);
+      by_steps(last, std::true_type{}, (int)P.nqc - 1, 1);
     }
   }
   if (stages & TRI_ATTN_STAGE_FINAL) {
     const int64_t nslots = P.B * P.N * P.H * (P.Jp / 16) * 64;
-    hipLaunchKernelGGL((reduce_dq_kernel<D, STRIDED>), dim3((unsigned)((nslots + 255) / 256)), dim3(256), 0, st, dqp,
-                       (bf16*)dq, (int)P.KB, (int)P.N, (int)P.H, (int)(P.Jp / 16), nslots, alpha, L);
+    const dim3 gq((unsigned)((nslots + 255) / 256));
+    if (P.KB <= 12)  // up to N = 768: no more partials than that are loaded per slot
+      hipLaunchKernelGGL((reduce_dq_kernel<D, STRIDED, 12>), gq, dim3(256), 0, st, dqp, (bf16*)dq, (int)P.KB,
+                         (int)P.N, (int)P.H, (int)(P.Jp / 16), nslots, alpha, L);
+    else
+      hipLaunchKernelGGL((reduce_dq_kernel<D, STRIDED, TRI_ATTN_MAX_N / 64>), gq, dim3(256), 0, st, dqp, (bf16*)dq,
+                         (int)P.KB, (int)P.N, (int)P.H, (int)(P.Jp / 16), nslots, alpha, L);
     const int64_t nbias = P.B * P.H * P.N * P.N;
     if (nbias % 4 == 0)
       hipLaunchKernelGGL(reduce_dbias_kernel<true>, dim3((unsigned)((nbias / 4 + 255) / 256)), dim3(256), 0, st, dbp,
@@ -1215,6 +1307,11 @@ tri_attn_status launch_bwd(unsigned stages, const Plan& P, const TokLayout& L, c
     else
       hipLaunchKernelGGL(reduce_dbias_kernel<false>, dim3((unsigned)((nbias + 255) / 256)), dim3(256), 0, st, dbp,
                          dbias, (int)P.ngroups, nbias);
+    if (P.nqc > 1) {
+      const int64_t nt = P.rows * (D / 4);
+      hipLaunchKernelGGL((reduce_dkv_kernel<D, STRIDED>), dim3((unsigned)((nt + 255) / 256)), dim3(256), 0, st, dkvp,
+                         (bf16*)dk, (bf16*)dv, (int)P.N, (int)P.H, (int)P.nqc, P.rows, alpha, L);
+    }
   }
   return hipGetLastError() == hipSuccess ? TRI_ATTN_SUCCESS : TRI_ATTN_ERROR_LAUNCH;
 }
