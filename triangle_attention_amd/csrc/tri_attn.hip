@@ -314,9 +314,11 @@ __device__ __forceinline__ int tr_off(int lane, int r0, int c0) {
 // The accumulator of each score tile starts from the prepared bias/alpha tile.
 //
 // Software pipeline over 64-key tiles: while tile t is computed, tile t+1's K and V (shared
-// by the work-group) and each wave's two bias tiles stream into the other half of
-// double-buffered LDS (buffer loads to LDS); keys past N read as zeros and carry a -inf
-// bias.  K and V rows are XOR-swizzled like the backward's.
+// by the work-group) stream into the other half of double-buffered LDS (buffer loads to
+// LDS); keys past N read as zeros.  Each wave reads its two bias tiles of tile t straight
+// from global memory into the score accumulators (every slice of a head reads the same
+// tiles, so they come from L2); padded keys carry a -inf bias.  K and V rows are
+// XOR-swizzled like the backward's.
 template <int D, bool MASK, bool STRIDED>
 __global__ __launch_bounds__(256, 5)
 void fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
