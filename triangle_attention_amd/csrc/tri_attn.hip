@@ -585,13 +585,15 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
 
 // Query chunks of the backward for N past six 128-query steps: a work-group keeps the pair-bias
 // gradient of its chunk's queries in registers (at most six steps), so longer slices are split
-// into chunks of six steps (the last one shorter), each its own set of work-groups.  dQ rows and
-// dbias rows of different chunks are disjoint; dK and dV sum over all queries, so chunked
-// work-groups write FP32 partials per chunk, summed in chunk order by reduce_dkv_kernel.
+// into ceil(steps / 6) chunks as equal as possible (cs or cs - 1 steps), each its own set of
+// work-groups, in one launch per chunk length.  dQ rows and dbias rows of different chunks are
+// disjoint; dK and dV sum over all queries, so chunked work-groups write FP32 partials per
+// chunk, summed in chunk order by reduce_dkv_kernel.
 struct Chunking {
   int nst;       // 128-query steps per slice in total
   int c_begin;   // first chunk of this launch (all of whose chunks have NS steps)
   int ncl;       // chunks in this launch
+  int step0;     // first 128-query step of this launch's first chunk
   float* dkvp;   // FP32 partials [chunk][dk, dv][B*N*H slice-head rows][N keys][D]
 };
 
@@ -626,7 +628,8 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   if (tile0 >= ntiles) return;
   const int64_t tile = CHUNKED ? tile0 % per_chunk : tile0;
   const int chunk = CHUNKED ? Ck.c_begin + (int)(tile0 / per_chunk) : 0;
-  const int s_base = chunk * kBwdMaxSteps;  // first 128-query step of this work-group's chunk
+  // first 128-query step of this work-group's chunk
+  const int s_base = CHUNKED ? Ck.step0 + (int)(tile0 / per_chunk) * NS : 0;
   const int NSt = CHUNKED ? Ck.nst : NS;    // 128-query steps per slice in total
   // Tile order: the key blocks of one (head, slice group) adjacent, so that they run together
   // on one XCD and share its L2 for the slices' Q and dO rows.  In a strided layout the heads
@@ -1136,6 +1139,7 @@ struct Plan {
   int64_t bias_f32_bytes;   // prepared forward bias (FP32 tiles)
   int64_t bias_b16_bytes;   // prepared backward bias (bf16 column blocks)
   int64_t nst, nqc;          // 128-query steps per slice; query chunks of the backward
+  int64_t cs, n1;            // steps of the longest chunks, and how many chunks have cs steps
   int64_t off_LD, off_dqp, off_dbp, off_dkv, bwd_bytes;
 };
 
@@ -1157,13 +1161,39 @@ Plan make_plan(int64_t B, int64_t N, int64_t H, int64_t D) {
   p.KB = (N + 63) / 64;
   p.nst = p.Jp / 128;
   p.nqc = (p.nst + kBwdMaxSteps - 1) / kBwdMaxSteps;
-  // enough (b, h, key block, query chunk, slice group) work-groups for ~3 per CU, with as few
-  // groups (pair-bias partials) as that allows
-  const int64_t per_group = B * H * p.KB * p.nqc;
-  int64_t groups = (768 + per_group - 1) / per_group;
-  if (groups < 1) groups = 1;
-  if (groups > N) groups = N;
-  p.G = (N + groups - 1) / groups;
+  p.cs = (p.nst + p.nqc - 1) / p.nqc;
+  p.n1 = p.nst - (p.cs - 1) * p.nqc;
+  if (p.nqc == 1) {
+    // enough (b, h, key block, slice group) work-groups for ~3 per CU, with as few groups
+    // (pair-bias partials) as that allows
+    const int64_t per_group = B * H * p.KB;
+    int64_t groups = (768 + per_group - 1) / per_group;
+    if (groups < 1) groups = 1;
+    if (groups > N) groups = N;
+    p.G = (N + groups - 1) / groups;
+  } else {
+    // Chunked: each work-group runs a whole slice group, one per CU, so a launch takes
+    // ceil(work-groups / CUs) rounds of (slices per group) x (chunk steps).  Pick the group
+    // count that minimises that time (about 1.6 us per slice and 128-query step) plus the
+    // round trip of one FP32 pair-bias partial per group (B*H*N*N*4 bytes written and read
+    // at about 5.5 TB/s).
+    constexpr int64_t kCUs = 256;
+    double best = 0.0;
+    int64_t bestG = N;
+    for (int64_t g = 1; g <= std::min<int64_t>(N, 256); g++) {
+      const int64_t G = (N + g - 1) / g, ng = (N + G - 1) / G;
+      if (ng != g) continue;  // same partition as a smaller g
+      const int64_t tiles = B * H * p.KB * ng;
+      int64_t units = ((p.n1 * tiles + kCUs - 1) / kCUs) * p.cs * G;
+      if (p.n1 < p.nqc) units += (((p.nqc - p.n1) * tiles + kCUs - 1) / kCUs) * (p.cs - 1) * G;
+      const double t = (double)units * 1.6e-6 + (double)ng * (double)(B * H * N * N) * 8.0 / 5.5e12;
+      if (g == 1 || t < best) {
+        best = t;
+        bestG = G;
+      }
+    }
+    p.G = bestG;
+  }
   p.ngroups = (N + p.G - 1) / p.G;
   p.elems = B * N * H * N * D;
   p.rows = B * N * H * N;
@@ -1261,10 +1291,10 @@ tri_attn_status launch_bwd(unsigned stages, const Plan& P, const TokLayout& L, c
   float* dkvp = (float*)(base + P.off_dkv);
   if (stages & TRI_ATTN_STAGE_MAIN) {
     const int64_t per_chunk = P.B * P.H * P.ngroups * P.KB;
-    auto launch = [&](auto ns_, auto chunked_, int c_begin, int ncl) {
+    auto launch = [&](auto ns_, auto chunked_, int c_begin, int ncl, int step0) {
       constexpr int NS = decltype(ns_)::value;
       constexpr bool CH = decltype(chunked_)::value;
-      const Chunking ck{(int)P.nst, c_begin, ncl, dkvp};
+      const Chunking ck{(int)P.nst, c_begin, ncl, step0, dkvp};
       const dim3 grid(grid_xcd(per_chunk * ncl));
       if (mask)
         hipLaunchKernelGGL((bwd_kernel<D, true, NS, STRIDED, CH>), grid, dim3(512), 0, st, (const bf16*)q,
@@ -1275,22 +1305,22 @@ tri_attn_status launch_bwd(unsigned stages, const Plan& P, const TokLayout& L, c
                            (const bf16*)k, (const bf16*)v, (const bf16*)dO, biasB, mask, LDg, dqp, dbp, (bf16*)dk,
                            (bf16*)dv, (int)P.B, (int)P.N, (int)P.H, (int)P.G, (int)P.ngroups, alpha, L, ck);
     };
-    auto by_steps = [&](int ns, auto chunked_, int c_begin, int ncl) {
+    auto by_steps = [&](int ns, auto chunked_, int c_begin, int ncl, int step0) {
       switch (ns) {  // 128-query steps of the chunk (1..6)
-        case 1: launch(std::integral_constant<int, 1>{}, chunked_, c_begin, ncl); break;
-        case 2: launch(std::integral_constant<int, 2>{}, chunked_, c_begin, ncl); break;
-        case 3: launch(std::integral_constant<int, 3>{}, chunked_, c_begin, ncl); break;
-        case 4: launch(std::integral_constant<int, 4>{}, chunked_, c_begin, ncl); break;
-        case 5: launch(std::integral_constant<int, 5>{}, chunked_, c_begin, ncl); break;
-        default: launch(std::integral_constant<int, 6>{}, chunked_, c_begin, ncl); break;
+        case 1: launch(std::integral_constant<int, 1>{}, chunked_, c_begin, ncl, step0); break;
+        case 2: launch(std::integral_constant<int, 2>{}, chunked_, c_begin, ncl, step0); break;
+        case 3: launch(std::integral_constant<int, 3>{}, chunked_, c_begin, ncl, step0); break;
+        case 4: launch(std::integral_constant<int, 4>{}, chunked_, c_begin, ncl, step0); break;
+        case 5: launch(std::integral_constant<int, 5>{}, chunked_, c_begin, ncl, step0); break;
+        default: launch(std::integral_constant<int, 6>{}, chunked_, c_begin, ncl, step0); break;
       }
     };
     if (P.nqc == 1) {
-      by_steps((int)P.nst, std::false_type{}, 0, 1);
-    } else {  // full chunks of six steps, then the last chunk with the remaining steps
-      const int last = (int)(P.nst - kBwdMaxSteps * (P.nqc - 1));
-      by_steps(kBwdMaxSteps, std::true_type{}, 0, (int)P.nqc - 1);
-      by_steps(last, std::true_type{}, (int)P.nqc - 1, 1);
+      by_steps((int)P.nst, std::false_type{}, 0, 1, 0);
+    } else {  // chunks as equal as possible: n1 chunks of cs steps, then chunks of cs - 1
+      const int nqc = (int)P.nqc, cs = (int)P.cs, n1 = (int)P.n1;
+      by_steps(cs, std::true_type{}, 0, n1, 0);
+      if (n1 < nqc) by_steps(cs - 1, std::true_type{}, n1, nqc - n1, n1 * cs);
     }
   }
   if (stages & TRI_ATTN_STAGE_FINAL) {
