@@ -1163,20 +1163,12 @@ Plan make_plan(int64_t B, int64_t N, int64_t H, int64_t D) {
   p.nqc = (p.nst + kBwdMaxSteps - 1) / kBwdMaxSteps;
   p.cs = (p.nst + p.nqc - 1) / p.nqc;
   p.n1 = p.nst - (p.cs - 1) * p.nqc;
-  if (p.nqc == 1) {
-    // enough (b, h, key block, slice group) work-groups for ~3 per CU, with as few groups
-    // (pair-bias partials) as that allows
-    const int64_t per_group = B * H * p.KB;
-    int64_t groups = (768 + per_group - 1) / per_group;
-    if (groups < 1) groups = 1;
-    if (groups > N) groups = N;
-    p.G = (N + groups - 1) / groups;
-  } else {
-    // Chunked: each work-group runs a whole slice group, one per CU, so a launch takes
-    // ceil(work-groups / CUs) rounds of (slices per group) x (chunk steps).  Pick the group
-    // count that minimises that time (about 1.6 us per slice and 128-query step) plus the
-    // round trip of one FP32 pair-bias partial per group (B*H*N*N*4 bytes written and read
-    // at about 5.5 TB/s).
+  {
+    // Slice groups of the backward: each work-group runs a whole slice group, one per CU, so a
+    // launch takes ceil(work-groups / CUs) rounds of (slices per group) x (chunk steps).  Pick
+    // the group count that minimises that time (about 1.6 us per slice and 128-query step)
+    // plus the round trip of one FP32 pair-bias partial per group (B*H*N*N*4 bytes written
+    // and read at about 5.5 TB/s).
     constexpr int64_t kCUs = 256;
     double best = 0.0;
     int64_t bestG = N;
