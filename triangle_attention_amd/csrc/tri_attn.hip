@@ -192,25 +192,13 @@ __global__ void bias_prep_bwd_kernel(const bf16* __restrict__ bias, _Float16* __
 
 // ------------------------------------------------------------------ streaming helpers
 
-__device__ __forceinline__ void dma16(const void* g, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
-}
-
-// Raw buffer resource over [base, base + bytes): loads past the end return zeros, which is how
-// rows beyond N are read below.  The range check applies to the per-lane and the scalar
+// Raw buffer resources (raw_rsrc below) cover [base, base + bytes): loads past the end return
+// zeros, which is how rows beyond N are read.  The range check applies to the per-lane and the scalar
 // offset together (a load at voffset + soffset >= bytes returns zeros; measured on gfx950 with
 // every address inside the allocation), so row offsets may go into either.  (Only loads go through buffer resources: the compiler's
 // wait-state rule for the store-data hazard of wide buffer stores does not cover the form
 // with a register scalar offset on gfx950, where such stores were seen to write
 // overwritten data.  Global stores get the wait states.)
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
-}
-// 16 bytes per lane from a buffer straight into LDS: lane l's bytes land at lds_wave_base + 16 l
-__device__ __forceinline__ void dma16b(__amdgpu_buffer_rsrc_t r, unsigned voff, int soff, void* lds_wave_base) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave_base, 16, voff, soff,
-                                           0, 0);
-}
 
 // Direct-to-LDS loads written as inline assembly.  The compiler's own form of these loads
 // makes it wait for every outstanding one before any later LDS read it cannot prove
@@ -242,6 +230,12 @@ __device__ __forceinline__ void dma16_asm(i32x4 rsrc, unsigned voff, int soff, u
 }
 __device__ __forceinline__ void dma16_asm(i32x4 rsrc, unsigned voff, int soff, const void* lds_wave_base) {
   dma16_asm(rsrc, voff, soff, lds_addr(lds_wave_base));
+}
+// as dma16_asm, issued only once `after` has been computed (an operand the statement ignores)
+__device__ __forceinline__ void dma16_asm_after(i32x4 rsrc, unsigned voff, int soff, unsigned lds_wave_base, float after) {
+  asm volatile("s_mov_b32 m0, %3\n\ts_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soff)),
+                  "s"(__builtin_amdgcn_readfirstlane(lds_wave_base)), "v"(after) : "memory", "m0");
 }
 // one byte per lane, zero-extended into lane l's dword at LDS byte address lds_wave_base + 4 l
 __device__ __forceinline__ void dma1_asm(i32x4 rsrc, unsigned voff, int soff, unsigned lds_wave_base) {
@@ -313,12 +307,13 @@ __device__ __forceinline__ int tr_off(int lane, int r0, int c0) {
 // 16 keys per 32-key tile, so the running max/sum of a query needs one cross-lane step.
 // The accumulator of each score tile starts from the prepared bias/alpha tile.
 //
-// Software pipeline over 64-key tiles: while tile t is computed, tile t+1's K and V (shared
-// by the work-group) stream into the other half of double-buffered LDS (buffer loads to
-// LDS); keys past N read as zeros.  Each wave reads its two bias tiles of tile t straight
-// from global memory into the score accumulators (every slice of a head reads the same
-// tiles, so they come from L2); padded keys carry a -inf bias.  K and V rows are
-// XOR-swizzled like the backward's.
+// Software pipeline over 64-key tiles: while tile t's softmax and PV product run, tile t+1's
+// K and V (shared by the work-group) stream into the other half of double-buffered LDS
+// (direct-to-LDS loads, issued once tile t's scores are complete); keys past N read as zeros.
+// Each wave reads its two bias tiles of tile t straight from global memory into the score
+// accumulators (every slice of a head reads the same tiles, so they come from L2), issued
+// before the barrier that publishes tile t so that their latency overlaps that wait; padded
+// keys carry a -inf bias.  K and V rows are XOR-swizzled like the backward's.
 template <int D, bool MASK, bool STRIDED>
 __global__ __launch_bounds__(256, 5)
 void fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
@@ -358,12 +353,13 @@ void fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   const uint8_t* mrow = MASK ? mask + ((int64_t)b * N + i) * N : nullptr;
 
   // streamed loads: K and V rows (lane -> swizzled 16-byte chunk), this wave's bias tiles
-  const __amdgpu_buffer_rsrc_t rk = buf_rsrc(k + sbase, L.span_bytes(N, D)), rv = buf_rsrc(v + sbase, L.span_bytes(N, D));
+  // (inline-assembly loads, which the compiler's own waits do not cover: see dma16_asm)
+  const i32x4 rk = raw_rsrc(k + sbase, L.span_bytes(N, D)), rv = raw_rsrc(v + sbase, L.span_bytes(N, D));
   const unsigned kv_vo = (unsigned)(((tid / CPR) * sT + ((tid % CPR) ^ swz<D>(tid / CPR)) * 8) * 2);
-  auto prefetch = [&](int kt, int buf) {
+  auto prefetch = [&](int kt, int buf, float after) {
     if (w < KT * CPR / 64) {
-      dma16b(rk, kv_vo, kt * KT * sT * 2, &Ks_[buf][w * 512]);
-      dma16b(rv, kv_vo, kt * KT * sT * 2, &Vs_[buf][w * 512]);
+      dma16_asm_after(rk, kv_vo, kt * KT * sT * 2, lds_addr(&Ks_[buf][w * 512]), after);
+      dma16_asm_after(rv, kv_vo, kt * KT * sT * 2, lds_addr(&Vs_[buf][w * 512]), after);
     }
   };
 
@@ -377,20 +373,10 @@ void fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
 
   const int nkt = (N + KT - 1) / KT;
   if (MASK && tid < KT) Ms_[0][tid] = tid < N ? mrow[tid] : (uint8_t)1;
-  prefetch(0, 0);
+  prefetch(0, 0, 0.0f);
   for (int kt = 0; kt < nkt; kt++) {
     const int cur = kt & 1;
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's part of tile kt is in LDS
-    __syncthreads();                     // all of tile kt is in LDS; buffer cur^1 is free
-    uint8_t mnext = 1;
-    if (kt + 1 < nkt) {
-      // the mask byte is loaded before the tile so that waiting for it leaves the tile in flight
-      if (MASK && tid < KT && (kt + 1) * KT + tid < N) mnext = mrow[(kt + 1) * KT + tid];
-      prefetch(kt + 1, cur ^ 1);
-    }
-    const lbf16* Ks = (const lbf16*)Ks_[cur];
-    const lbf16* Vs = (const lbf16*)Vs_[cur];
-
+    // this wave's bias tiles of tile kt: eight 16-byte loads into the score accumulators
     f32x16 s[2];
 #pragma unroll
     for (int tt = 0; tt < 2; tt++) {
@@ -400,6 +386,18 @@ void fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
         s[tt][R * 4 + 0] = bv[0]; s[tt][R * 4 + 1] = bv[1];
         s[tt][R * 4 + 2] = bv[2]; s[tt][R * 4 + 3] = bv[3];
       }
+    }
+    // every load but those eight, among them this wave's part of tile kt, has landed (loads
+    // complete in issue order; the memory clobber keeps the bias loads above the wait)
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    __syncthreads();  // all of tile kt is in LDS; buffer cur^1 is free
+    uint8_t mnext = 1;
+    if (MASK && kt + 1 < nkt && tid < KT && (kt + 1) * KT + tid < N) mnext = mrow[(kt + 1) * KT + tid];
+    const lbf16* Ks = (const lbf16*)Ks_[cur];
+    const lbf16* Vs = (const lbf16*)Vs_[cur];
+
+#pragma unroll
+    for (int tt = 0; tt < 2; tt++) {
       const int rk_ = tt * 32 + ln;
 #pragma unroll
       for (int cc = 0; cc < NC; cc++) {
@@ -422,6 +420,9 @@ void fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
 #pragma unroll
     for (int r = 0; r < 16; r++) mx = fmaxf(mx, s[1][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
+    // the next tile's K and V, issued once this tile's scores exist: the compiler's waits for
+    // the bias loads then never include them, and they stream during the softmax and PV
+    if (kt + 1 < nkt) prefetch(kt + 1, cur ^ 1, mx);
     // The reference maximum of a query moves only when a score exceeds it by more than
     // 2^8 in probability (exp2 units): probabilities stay <= 256, exact in FP32 and with
     // bf16's relative precision, and most tiles skip the rescale of the accumulators.  The
