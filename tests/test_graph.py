@@ -82,6 +82,16 @@ def test_graph_replay_masked_ragged():
     _check_graph_replays(inp)
 
 
+def test_graph_replay_chunked_backward():
+    # N = 900: two query chunks in two launches plus the dK/dV chunk sum, all inside the graph
+    inp = make_inputs(1, 900, 1, 16, seed=79, bias_std=2.0)
+    rng = np.random.default_rng(80)
+    msk = (rng.random((1, 900, 900)) > 0.3).astype(np.uint8)
+    msk[:, :, 899] = 1
+    inp["key_mask"] = msk
+    _check_graph_replays(inp)
+
+
 def test_graph_replay_tri_mul():
     """The triangle multiplication core (both directions, forward and backward, channels first and
     channels last through the workspace) captured in one graph: replays reproduce eager results."""

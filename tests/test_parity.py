@@ -222,3 +222,22 @@ def test_forward_only_long_crops(B, N, H, D, masked):
             e = dict(o_maxabs=maxabs(o_[0, i, h], o64), o=rrmse(o_[0, i, h], o64), lse=maxabs(lse_[0, i, h], l64))
             print(f"  slice {i} head {h}", {k_: f"{v_:.2e}" for k_, v_ in e.items()}, flush=True)
             assert e["o_maxabs"] <= TOL_O_MAXABS and e["o"] <= TOL_O_RRMSE and e["lse"] <= TOL_LSE_MAXABS, e
+
+
+def test_autograd_chunked_backward():
+    """The autograd function past N = 768 returns the C entry points' results bit for bit."""
+    import triangle_attention_amd as ta
+    from ._util import mask_dev, to_dev
+    B, N, H, D = 1, 800, 1, 32
+    print(f"autograd chunked B={B} N={N} H={H} D={D}", flush=True)
+    inp = make_inputs(B, N, H, D, seed=81, bias_std=2.0)
+    ref = run_gpu(inp)
+    q, k, v = (to_dev(inp[n]).requires_grad_(True) for n in ("q", "k", "v"))
+    bias = to_dev(inp["bias"]).requires_grad_(True)
+    o = ta.triangle_attention(q, k, v, bias, mask_dev(inp["key_mask"]))
+    o.backward(to_dev(inp["dO"]))
+    torch.cuda.synchronize()
+    assert torch.equal(o.detach(), ref["o"])
+    for n, t in (("dq", q), ("dk", k), ("dv", v)):
+        assert torch.equal(t.grad, ref[n]), n
+    assert torch.equal(bias.grad, ref["dbias"].to(torch.bfloat16))
