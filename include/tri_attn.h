@@ -52,7 +52,8 @@ extern "C" {
 
 /* Largest N of the backward (and of a forward that feeds it).  Up to N = 768 a work-group keeps
  * the pair-bias gradient of all queries of its 64-key block in registers; longer slices are
- * split into chunks of 768 queries whose dK / dV are summed in FP32 (more workspace). */
+ * split into ceil(N / 768) query chunks of near-equal size, whose dK / dV are summed in FP32
+ * in chunk order (the workspace grows by 2 * chunks * B*N*H*N*D * 4 bytes). */
 #define TRI_ATTN_MAX_N 2048
 /* Largest N of the forward alone (inference on longer crops): the forward streams keys and has
  * no such per-query state. */
