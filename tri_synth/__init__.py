@@ -47,8 +47,9 @@ class Workload:
         return 2.5 * self.flops_fwd
 
 
-# The five synthetic workloads: tiny latency case, crop 384, masked crop 640,
-# crop 768 at both head dims (the d=16 one with a wide bias to stress softmax).
+# The synthetic workloads: tiny latency case, crop 384, masked crop 640, crop 768 at both head
+# dims (the d=16 one with a wide bias to stress softmax), and a crop of 1024, past the 768
+# queries one backward work-group covers (its backward runs in two query chunks).
 WORKLOADS = {
     w.name: w
     for w in [
@@ -57,6 +58,7 @@ WORKLOADS = {
         Workload("n640_h4_d16_mask64", 1, 640, 4, 16, mask_tail=64, seed=3),
         Workload("n768_h4_d32", 1, 768, 4, 32, seed=4),
         Workload("n768_h4_d16_bias4", 1, 768, 4, 16, bias_std=4.0, seed=5),
+        Workload("n1024_h4_d32", 1, 1024, 4, 32, seed=6),
     ]
 }
 
