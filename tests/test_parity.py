@@ -194,8 +194,9 @@ def test_chunked_backward_long_crops(B, N, H, D, masked):
         assert float(out["dv"][:, :, :, N - 40:N - 8].float().abs().max()) == 0.0
 
 
-# forward alone on crops past the backward's limit (inference): sampled slices, element by element
-@pytest.mark.parametrize("B,N,H,D,masked", [(1, 2100, 1, 16, True), (1, 2304, 1, 32, False)])
+# forward alone on crops past the backward's limit (inference), up to its maximum N = 4096:
+# sampled slices, element by element
+@pytest.mark.parametrize("B,N,H,D,masked", [(1, 2100, 1, 16, True), (1, 2304, 1, 32, False), (1, 4096, 1, 16, False)])
 def test_forward_only_long_crops(B, N, H, D, masked):
     import triangle_attention_amd as ta
     from tri_synth import bf16_bits_to_f64
