@@ -1319,12 +1319,18 @@ tri_attn_status launch_bwd(unsigned stages, const Plan& P, const TokLayout& L, c
   if (stages & TRI_ATTN_STAGE_FINAL) {
     const int64_t nslots = P.B * P.N * P.H * (P.Jp / 16) * 64;
     const dim3 gq((unsigned)((nslots + 255) / 256));
-    if (P.KB <= 12)  // up to N = 768: no more partials than that are loaded per slot
-      hipLaunchKernelGGL((reduce_dq_kernel<D, STRIDED, 12>), gq, dim3(256), 0, st, dqp, (bf16*)dq, (int)P.KB,
+    // the instance that loads no more partials per slot than there are key blocks, rounded up
+    // to 12 (N <= 768), 16 (N <= 1024), 24 (N <= 1536) or 32
+    auto reduce_dq = [&](auto kmax_) {
+      constexpr int KM = decltype(kmax_)::value;
+      hipLaunchKernelGGL((reduce_dq_kernel<D, STRIDED, KM>), gq, dim3(256), 0, st, dqp, (bf16*)dq, (int)P.KB,
                          (int)P.N, (int)P.H, (int)(P.Jp / 16), nslots, alpha, L);
-    else
-      hipLaunchKernelGGL((reduce_dq_kernel<D, STRIDED, TRI_ATTN_MAX_N / 64>), gq, dim3(256), 0, st, dqp, (bf16*)dq,
-                         (int)P.KB, (int)P.N, (int)P.H, (int)(P.Jp / 16), nslots, alpha, L);
+    };
+    static_assert(TRI_ATTN_MAX_N / 64 == 32, "largest reduce_dq_kernel instance");
+    if (P.KB <= 12) reduce_dq(std::integral_constant<int, 12>{});
+    else if (P.KB <= 16) reduce_dq(std::integral_constant<int, 16>{});
+    else if (P.KB <= 24) reduce_dq(std::integral_constant<int, 24>{});
+    else reduce_dq(std::integral_constant<int, 32>{});
     const int64_t nbias = P.B * P.H * P.N * P.N;
     if (nbias % 4 == 0)
       hipLaunchKernelGGL(reduce_dbias_kernel<true>, dim3((unsigned)((nbias / 4 + 255) / 256)), dim3(256), 0, st, dbp,
