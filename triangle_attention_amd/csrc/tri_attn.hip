@@ -860,11 +860,15 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
         for (int e = 0; e < 4; e++) dp[R * 4 + e] = x[e];
       }
       __builtin_amdgcn_sched_barrier(0);
+      // raised wave priority while a wave issues its products, so that the arbiter lets it
+      // finish them before the other wave of its SIMD takes the issue slots for VALU work
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int cc = 0; cc < NC; cc++) {
         sacc = mfma32(aq[cc], kf[cc], sacc);
         dp = mfma32(ao[cc], vf[cc], dp);
       }
+      __builtin_amdgcn_s_setprio(0);
       // P = exp2(c1 S + log2e bias - lse2) and dS = P (dP - D); dS is summed into the face.
       // The bias term log2e * bias - lse2 comes from one v_fma_mix_f32 per element (fp16
       // bias pairs, -lse2 rows), independent of the products above.
@@ -917,8 +921,10 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
                                tr16p((const lbf16*)(qd + 128 * D * 2 + trB + m2 * 16 * D * 2)));
         const bf16x8 aq = cat8(tr16p((const lbf16*)(qd + trA + m2 * 16 * D * 2)),
                                tr16p((const lbf16*)(qd + trB + m2 * 16 * D * 2)));
+        __builtin_amdgcn_s_setprio(1);
         dvT = mfma32(ao, pb[m2], dvT);
         dkT = mfma32(aq, sb[m2], dkT);
+        __builtin_amdgcn_s_setprio(0);
       }
       if (t >= 1) dq_product(cur ^ 1);
       prev_sl = sl_row;
