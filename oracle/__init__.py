@@ -19,7 +19,9 @@ Sources:
 - The per-slice formula (the pages print none): for every batch b, slice i and
   head h, o[j] = sum_k softmax_k(alpha * q[j].k[k] + bias[j,k] + mask[k]) v[k],
   with alpha = 1/sqrt(d), the bias indexed [b,h,j,k] and shared by every slice,
-  and the key mask adding -1e9 to masked keys.
+  and the key mask leaving masked keys out of the softmax (the workloads' additive
+  -1e9; a row with no key of finite score outputs 0, has lse = +inf and no
+  gradient).
 
 The triangle multiplication core (``tri_mul_oracle``) follows the kongchang.com
 article on fast_trimul, section "什么是三角乘法更新"; its reading is stated in that

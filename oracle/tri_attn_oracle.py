@@ -11,19 +11,28 @@ Conventions (all arrays float64 unless stated):
   dbias       : [B, H, N, N]
 
 The score of slice (b, i, h) is
-    s[j, k] = alpha * sum_c q[j, c] k[k, c] + bias[b, h, j, k] + m[k],
-    m[k] = -1e9 if key k of slice i is masked else 0,  alpha = d ** -0.5,
+    s[j, k] = alpha * sum_c q[j, c] k[k, c] + bias[b, h, j, k] + m[k],  alpha = d ** -0.5,
 the forward is o = softmax_k(s) v, and the backward is the vector-Jacobian
 product of L = sum(dO * o) with respect to q, k, v and the shared bias.
 Following the TurboPairFormer abstract (arXiv 2610.05854), the bias gradient
 of one slice is the score gradient dS of that slice, and because the bias is
 shared, dbias is the sum of dS over all slices i.
+
+Key mask.  The workloads describe the mask as an additive -1e9 on the score of
+a masked key.  That term stands for leaving the key out: whenever a row keeps
+a key with a finite score, exp(-1e9 + O(1)) is exactly 0 in float64 and the
+result is the same as with m[k] = -inf.  The oracle therefore writes m[k] =
+-inf, which also settles the case the -1e9 form leaves open: a row with no key
+of finite score (every key of its slice masked, or every key carrying a -inf
+bias) attends to nothing, so its output is 0, its lse is +inf (the value whose
+exp(s - lse) gives zero probability) and it contributes no gradient.  Bias
+values are finite or -inf.
 """
 from __future__ import annotations
 
 import numpy as np
 
-MASK_NEG = -1e9  # additive score term for a masked key
+MASK_NEG = -1e9  # additive score term for a masked key, as the workloads state it (see above)
 
 
 def _alpha(d: int) -> float:
@@ -37,17 +46,31 @@ def slice_forward64(qs, ks, vs, bias_h, mask_row=None):
     Returns (o [N, d], lse [N], p [N, N]).
     """
     alpha = _alpha(qs.shape[1])
-    s = alpha * (qs @ ks.T) + bias_h
-    if mask_row is not None:
-        s = s + np.where(np.asarray(mask_row) == 0, MASK_NEG, 0.0)[None, :]
-    # softmax over keys, after subtracting each row's maximum
-    row_max = s.max(axis=1, keepdims=True)
-    e = np.exp(s - row_max)
-    row_sum = e.sum(axis=1, keepdims=True)
-    p = e / row_sum
-    lse = row_max[:, 0] + np.log(row_sum[:, 0])
+    s = _scores(alpha, qs, ks, bias_h, mask_row)
+    p, lse = _softmax_rows(s)
     o = p @ vs
     return o, lse, p
+
+
+def _scores(alpha, qs, ks, bias_h, mask_row):
+    """s[j, k] = alpha q[j].k[k] + bias[j, k], with masked keys left out (-inf)."""
+    s = alpha * (qs @ ks.T) + bias_h
+    if mask_row is not None:
+        s = np.where(np.asarray(mask_row)[None, :] == 0, -np.inf, s)
+    return s
+
+
+def _softmax_rows(s):
+    """Softmax over keys of each row of s, after subtracting the row's maximum, and the row's
+    logsumexp.  A row with no finite score attends to nothing: p = 0 and lse = +inf."""
+    row_max = s.max(axis=-1, keepdims=True)
+    empty = ~np.isfinite(row_max)
+    shift = np.where(empty, 0.0, row_max)
+    e = np.exp(s - shift)
+    row_sum = e.sum(axis=-1, keepdims=True)
+    p = np.where(empty, 0.0, e / np.where(empty, 1.0, row_sum))
+    lse = np.where(empty, np.inf, shift + np.log(np.where(empty, 1.0, row_sum)))
+    return p, lse[..., 0]
 
 
 def slice_backward64(qs, ks, vs, bias_h, dOs, mask_row=None):
@@ -129,11 +152,9 @@ def dbias_rows64(q, k, v, bias, dO, rows, key_mask=None):
     out = np.zeros((len(rows), N))
     for r, (b, h, j) in enumerate(rows):
         for i in range(N):
-            s = alpha * (k[b, i, h] @ q[b, i, h, j]) + bias[b, h, j]
-            if key_mask is not None:
-                s = s + np.where(key_mask[b, i] == 0, MASK_NEG, 0.0)
-            e = np.exp(s - s.max())
-            p = e / e.sum()
+            mrow = None if key_mask is None else key_mask[b, i]
+            s = _scores(alpha, q[b, i, h, j][None, :], k[b, i, h], bias[b, h, j][None, :], mrow)[0]
+            p, _ = _softmax_rows(s)
             o = p @ v[b, i, h]
             D = dO[b, i, h, j] @ o
             dp = v[b, i, h] @ dO[b, i, h, j]

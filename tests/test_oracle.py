@@ -143,6 +143,78 @@ def test_tail_mask_zero_columns_in_dbias():
     assert np.abs(dk[..., 4:, :]).max() == 0.0 and np.abs(dv[..., 4:, :]).max() == 0.0
 
 
+def _sdpa_slices(q, k, v, bias, dO, m, slices, b):
+    """Per-slice torch float64 attention with autograd over the listed slices of batch entry b:
+    returns o, dq, dk, dv of those slices and the sum of their bias gradients."""
+    B, N, H, _, d = q.shape
+    outs, db = {}, np.zeros((H, N, N))
+    for i in slices:
+        t = lambda x: torch.tensor(x, dtype=torch.float64, requires_grad=True)  # noqa: E731
+        tq, tk, tv, tb = t(q[b, i]), t(k[b, i]), t(v[b, i]), t(bias[b])
+        madd = torch.where(torch.tensor(m[b, i] == 0)[None, None, :], -1e9, 0.0).double()
+        o = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=tb + madd, scale=1.0 / math.sqrt(d))
+        o.backward(torch.tensor(dO[b, i]))
+        outs[i] = (o.detach().numpy(), tq.grad.numpy(), tk.grad.numpy(), tv.grad.numpy())
+        db += tb.grad.numpy()
+    return outs, db
+
+
+def test_fully_masked_slices_attend_to_nothing():
+    # Slices whose every key is masked (padded residues of a cropped batch): output 0, lse = +inf,
+    # no gradient, and dbias is the sum over the remaining slices only.  The remaining slices are
+    # checked against torch's library attention with autograd, slice by slice.
+    q, k, v, bias, dO, m = _case(B=2, N=6, H=2, d=4, seed=61, mask=True)
+    empty = {0: [1, 4], 1: [5]}
+    for b, sl in empty.items():
+        m[b, sl] = 0
+    o, lse = oracle.forward64(q, k, v, bias, m)
+    dq, dk, dv, db = oracle.backward64(q, k, v, bias, dO, m)
+    for b, sl in empty.items():
+        assert np.abs(o[b, sl]).max() == 0.0
+        assert np.isposinf(lse[b, sl]).all()
+        for g in (dq, dk, dv):
+            assert np.abs(g[b, sl]).max() == 0.0
+        rest = [i for i in range(6) if i not in sl]
+        assert np.isfinite(lse[b, rest]).all()
+        ref, db_ref = _sdpa_slices(q, k, v, bias, dO, m, rest, b)
+        for i in rest:
+            for got, want in zip((o[b, i], dq[b, i], dk[b, i], dv[b, i]), ref[i]):
+                np.testing.assert_allclose(got, want, rtol=1e-10, atol=1e-11)
+        np.testing.assert_allclose(db[b], db_ref, rtol=1e-10, atol=1e-11)
+    # the same rows through the row-restricted dbias
+    rows = [(0, 1, 2), (1, 0, 5)]
+    got = oracle.dbias_rows64(q, k, v, bias, dO, rows, m)
+    for r, (b, h, j) in enumerate(rows):
+        np.testing.assert_allclose(got[r], db[b, h, j], atol=1e-13)
+
+
+def test_row_with_only_minus_inf_bias_attends_to_nothing():
+    # A query row whose keys all carry a -inf bias has no finite score: o = 0, lse = +inf, and the
+    # row adds nothing to any gradient.  So every gradient equals that of the same problem with the
+    # row's bias made finite and its output gradient set to zero (which also adds nothing).
+    q, k, v, bias, dO, m = _case(B=1, N=5, H=2, d=4, seed=71)
+    j, h = 3, 1
+    bias_inf = bias.copy()
+    bias_inf[0, h, j, :] = -np.inf
+    o, lse = oracle.forward64(q, k, v, bias_inf)
+    assert np.abs(o[0, :, h, j]).max() == 0.0 and np.isposinf(lse[0, :, h, j]).all()
+    assert np.isfinite(lse[0, :, 0]).all()
+    g_inf = oracle.backward64(q, k, v, bias_inf, dO)
+    dO0 = dO.copy()
+    dO0[0, :, h, j] = 0.0
+    g_ref = oracle.backward64(q, k, v, bias, dO0)
+    for a, b_ in zip(g_inf, g_ref):
+        np.testing.assert_allclose(a, b_, rtol=1e-12, atol=1e-13)
+    # a -inf bias on some keys only: those keys get exactly zero probability (key deletion)
+    bias_part = bias.copy()
+    bias_part[0, h, :, [0, 2]] = -np.inf
+    o_p, _ = oracle.forward64(q, k, v, bias_part)
+    keep = [1, 3, 4]
+    for i in range(5):
+        o_r, _, _ = oracle.slice_forward64(q[0, i, h], k[0, i, h][keep], v[0, i, h][keep], bias[0, h][:, keep])
+        np.testing.assert_allclose(o_p[0, i, h], o_r, atol=1e-13)
+
+
 # ---------------------------------------------------------------- invariants
 
 @pytest.mark.parametrize("mask", [False, True])
@@ -209,9 +281,14 @@ def _torch_reference(q, k, v, bias, dO, m):
 
 
 @pytest.mark.parametrize("mask", [False, True])
-@pytest.mark.parametrize("N,H,d", [(6, 2, 4), (9, 3, 8), (17, 2, 16)])
-def test_matches_torch_sdpa_autograd(N, H, d, mask):
-    q, k, v, bias, dO, m = _case(N=N, H=H, d=d, seed=N * 10 + d, mask=mask, bias_scale=2.0)
+@pytest.mark.parametrize("B,N,H,d", [(1, 6, 2, 4), (1, 9, 3, 8), (1, 17, 2, 16), (2, 6, 2, 4), (2, 9, 3, 8)])
+def test_matches_torch_sdpa_autograd(B, N, H, d, mask):
+    # B = 2 draws a different bias and key mask for each batch entry, so a batch-index slip in the
+    # oracle (bias[0] or key_mask[0] used for b = 1) fails here
+    q, k, v, bias, dO, m = _case(B=B, N=N, H=H, d=d, seed=N * 10 + d + 1000 * (B - 1), mask=mask, bias_scale=2.0)
+    if B > 1:
+        assert np.abs(bias[1] - bias[0]).max() > 0.5
+        assert m is None or (m[1] != m[0]).any()
     ro, rdq, rdk, rdv, rdb = _torch_reference(q, k, v, bias, dO, m)
     o, _ = oracle.forward64(q, k, v, bias, m)
     dq, dk, dv, db = oracle.backward64(q, k, v, bias, dO, m)
@@ -222,10 +299,11 @@ def test_matches_torch_sdpa_autograd(N, H, d, mask):
     np.testing.assert_allclose(db, rdb, rtol=1e-10, atol=1e-11)
 
 
-def test_dbias_is_slice_sum_of_per_slice_bias_gradients():
+@pytest.mark.parametrize("B", [1, 2])
+def test_dbias_is_slice_sum_of_per_slice_bias_gradients(B):
     # Give every slice its own bias leaf [B, N(slice), H, N, N]; their gradients summed over slices
-    # must equal the oracle's shared-bias gradient.
-    q, k, v, bias, dO, m = _case(N=6, H=2, d=4, seed=31, mask=True)
+    # must equal the oracle's shared-bias gradient (per batch entry, with per-batch bias and mask).
+    q, k, v, bias, dO, m = _case(B=B, N=6, H=2, d=4, seed=31, mask=True)
     B, N, H, _, d = q.shape
     per = torch.tensor(np.broadcast_to(bias[:, None], (B, N, H, N, N)).copy(), requires_grad=True)
     madd = torch.where(torch.tensor(m == 0)[:, :, None, None, :], -1e9, 0.0).double()
@@ -257,9 +335,10 @@ def _loss(q, k, v, bias, dO, m):
     return float((o * dO).sum())
 
 
-@pytest.mark.parametrize("N,d,mask", [(2, 2, False), (3, 4, True), (5, 2, True), (5, 4, False)])
-def test_central_finite_differences(N, d, mask):
-    q, k, v, bias, dO, m = _case(B=1, N=N, H=2, d=d, seed=100 + N * d, mask=mask)
+@pytest.mark.parametrize("B,N,d,mask", [(1, 2, 2, False), (1, 3, 4, True), (1, 5, 2, True), (1, 5, 4, False),
+                                         (2, 3, 2, True), (2, 4, 2, False)])
+def test_central_finite_differences(B, N, d, mask):
+    q, k, v, bias, dO, m = _case(B=B, N=N, H=2, d=d, seed=100 + N * d + B, mask=mask)
     dq, dk, dv, db = oracle.backward64(q, k, v, bias, dO, m)
     eps = 1e-6
     rng = np.random.default_rng(0)
