@@ -9,9 +9,18 @@
  *   s[j,k] = alpha * sum_c q[b,i,h,j,c] k[b,i,h,k,c] + bias[b,h,j,k] + m[b,i,k]
  *   o[b,i,h,j,:] = sum_k softmax_k(s[j,:]) v[b,i,h,k,:]
  *
- * where the pair bias is shared by all N slices and m = -1e9 for a masked key, else 0.
- * The backward returns dq, dk, dv and dbias[b,h,j,k] = sum_i dS[b,i,h,j,k], the
- * reduction across slices that the shared bias adds (same Abstract).
+ * where the pair bias is shared by all N slices and m = -inf for a masked key, else 0 (a
+ * masked key is left out of the softmax; an additive -1e9 gives the same result for every
+ * row that keeps a key).  The backward returns dq, dk, dv and dbias[b,h,j,k] =
+ * sum_i dS[b,i,h,j,k], the reduction across slices that the shared bias adds (same Abstract).
+ *
+ * Rows with no key of finite score -- every key of the slice masked (a padded residue of a
+ * cropped batch), or every key of the query carrying a -inf bias -- attend to nothing: their
+ * output and residual are 0, their lse is +inf, and they contribute nothing to any gradient.
+ *
+ * Bias values are finite or -inf (a -inf bias removes that key for that query).  Finite bias
+ * values are clamped to [-65504, 65504] in both passes (the backward streams the bias as
+ * fp16); below that magnitude the bias is used exactly.  A bias of +inf is not supported.
  *
  * Memory layouts (row-major, contiguous, caller-owned DEVICE memory):
  *   q, k, v, o, residual, dO, dq, dk, dv : bf16 [B, N, H, N, D]   index [b, i, h, j, c]
@@ -35,8 +44,7 @@
  *   - Every floating-point reduction runs in a fixed order that depends only on the
  *     shape, with no floating-point atomics: repeated calls with the same inputs and
  *     shape on the same device return bitwise-identical outputs.
- *   - Every row must keep at least one key; a fully masked row gives finite but
- *     otherwise unspecified results.
+ *   - Inputs (q, k, v, dO) are finite.
  */
 #ifndef TRI_ATTN_H
 #define TRI_ATTN_H

@@ -22,7 +22,7 @@ def _bits(t: torch.Tensor) -> torch.Tensor:
     return t.view(torch.int32) if t.dtype == torch.float32 else t.view(torch.int16)
 
 
-def _check_graph_replays(inp):
+def _check_graph_replays(inp, against_oracle=False):
     import triangle_attention_amd as ta
     q, k, v, bias, dO = (to_dev(inp[n]) for n in ("q", "k", "v", "bias", "dO"))
     m = mask_dev(inp["key_mask"])
@@ -66,11 +66,30 @@ def _check_graph_replays(inp):
         torch.cuda.synchronize()
         for n in OUTS:
             assert torch.equal(_bits(out[n]), _bits(ref[n])), (rep, n)
+        if against_oracle:  # each replay's outputs against the FP64 oracle, element by element
+            _oracle_check(inp, out, f"graph replay {rep}")
+
+
+def _oracle_check(inp, out, label):
+    import oracle
+    from ._util import (TOL_GRAD_RRMSE, TOL_LSE_MAXABS, TOL_O_MAXABS, TOL_O_RRMSE, f64, inputs64, maxabs,
+                        rrmse)
+    x = inputs64(inp)
+    o64, lse64 = oracle.forward64(x["q"], x["k"], x["v"], x["bias"], x["key_mask"])
+    g64 = oracle.backward64(x["q"], x["k"], x["v"], x["bias"], x["dO"], x["key_mask"])
+    o = f64(out["o"])
+    errs = dict(o_maxabs=maxabs(o, o64), o=rrmse(o, o64), lse=maxabs(f64(out["lse"]), lse64))
+    for n, ref in zip(("dq", "dk", "dv", "dbias"), g64):
+        errs[n] = rrmse(f64(out[n]), ref)
+    print(label, {k: f"{v:.3e}" for k, v in errs.items()}, flush=True)
+    assert errs["o_maxabs"] <= TOL_O_MAXABS and errs["o"] <= TOL_O_RRMSE and errs["lse"] <= TOL_LSE_MAXABS, errs
+    for n in ("dq", "dk", "dv", "dbias"):
+        assert errs[n] <= TOL_GRAD_RRMSE, (n, errs)
 
 
 def test_graph_replay_small():
-    # the launch-bound workload the graph path is for
-    _check_graph_replays(workload_inputs(WORKLOADS["n64_h4_d16"]))
+    # the launch-bound workload the graph path is for; replays also checked against the oracle
+    _check_graph_replays(workload_inputs(WORKLOADS["n64_h4_d16"]), against_oracle=True)
 
 
 def test_graph_replay_masked_ragged():
@@ -79,7 +98,7 @@ def test_graph_replay_masked_ragged():
     msk = (rng.random((1, 200, 200)) > 0.3).astype(np.uint8)
     msk[:, :, 5] = 1
     inp["key_mask"] = msk
-    _check_graph_replays(inp)
+    _check_graph_replays(inp, against_oracle=True)
 
 
 def test_graph_replay_chunked_backward():

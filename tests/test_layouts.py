@@ -72,8 +72,9 @@ CASES = [
     (1, 384, 4, 32, True, True),
     (1, 640, 2, 16, True, True),   # five query steps
     (1, 768, 2, 32, False, True),  # six query steps: the largest backward instantiation
-    (1, 900, 1, 16, True, True),   # two query chunks (six steps, then two)
-    (1, 1664, 1, 32, False, True), # three query chunks (six, six, one)
+    (1, 900, 1, 16, True, True),   # two query chunks of four steps each
+    (1, 800, 1, 32, True, True),   # two query chunks of four and three steps
+    (1, 1664, 1, 32, False, True), # three query chunks of five, four and four steps
 ]
 
 

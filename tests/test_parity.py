@@ -143,8 +143,8 @@ def test_workload_sampled_parity(name):
         assert float(out["dv"][:, :, :, w.N - w.mask_tail:].float().abs().max()) == 0.0
 
 
-# backward past six 128-query steps: query chunks of 768 whose dK / dV partials are summed in FP32
-# (two chunks at N = 900 and 1100, three at N = 2048, the last chunk shorter each time); sampled
+# backward past six 128-query steps: query chunks as equal as possible, whose dK / dV partials are
+# summed in FP32 (N = 900: 4 + 4 steps; N = 1100: 5 + 4; N = 2048: 6 + 5 + 5); sampled
 # slices element by element, sampled dbias rows, the invariants, and a bitwise repeat
 @pytest.mark.parametrize("B,N,H,D,masked", [(1, 900, 2, 32, False), (1, 1100, 1, 16, True), (1, 2048, 1, 16, True)])
 def test_chunked_backward_long_crops(B, N, H, D, masked):

@@ -198,8 +198,8 @@ def _check(status: int, where: str):
 def _shape(q, layout="slice_head"):
     if layout not in LAYOUTS:
         raise ValueError(f"layout must be one of {sorted(LAYOUTS)}")
-    if q.dim() != 5:
-        raise ValueError("q must have 5 dimensions")
+    if not isinstance(q, torch.Tensor) or q.dim() != 5:
+        raise ValueError("q must be a 5-dimensional tensor")
     if layout == "slice_head":
         B, N, H, N2, D = q.shape
     else:
@@ -209,17 +209,65 @@ def _shape(q, layout="slice_head"):
     return B, N, H, D
 
 
+def _require(t, name, shape, dtypes):
+    """Raise ValueError unless t is a contiguous tensor of one of `dtypes` with exactly `shape`.
+    The C entry points read raw memory in the documented layout, so a view with other strides or
+    another dtype would be misread, not rejected."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor, got {type(t).__name__}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} must have dtype {' or '.join(str(d) for d in dtypes)}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (strides {t.stride()}); call .contiguous() first")
+
+
+def _one_gpu(named):
+    """Raise ValueError unless every tensor of `named` ((name, tensor) pairs, None skipped) is on
+    the GPU of the first one."""
+    named = [(n, t) for n, t in named if t is not None]
+    dev = named[0][1].device
+    for n, t in named:
+        if not t.is_cuda:
+            raise ValueError(f"{n} must be on a GPU, got device {t.device}")
+        if t.device != dev:
+            raise ValueError(f"{n} is on {t.device}, {named[0][0]} on {dev}: all tensors must be on one GPU")
+
+
+_BF16 = (torch.bfloat16,)
+_MASK = (torch.uint8, torch.bool)
+
+
+def _check_inputs(q, k, v, bias, key_mask, layout, more=()):
+    B, N, H, D = _shape(q, layout)
+    if D not in (16, 32):
+        raise ValueError(f"head dimension must be 16 or 32, got {D}")
+    tok = tuple(q.shape)
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _require(t, n, tok, _BF16)
+    _require(bias, "bias", (B, H, N, N), _BF16)
+    if key_mask is not None:
+        _require(key_mask, "key_mask", (B, N, N), _MASK)
+    for n, t, shape, dtypes in more:
+        if t is not None:
+            _require(t, n, shape, dtypes)
+    _one_gpu([("q", q), ("k", k), ("v", v), ("bias", bias), ("key_mask", key_mask)] + [(m[0], m[1]) for m in more])
+    return B, N, H, D
+
+
 def _workspace(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
 
 
 def forward(q, k, v, bias, key_mask=None, residual_compensation=True, layout="slice_head"):
-    """Returns (o, lse, residual-or-None).  Tensors must be contiguous bf16 (mask uint8) on one GPU;
-    q, k, v (and o, residual) are laid out as `layout` names (see triangle_attention)."""
-    B, N, H, D = _shape(q, layout)
-    o = torch.empty_like(q)
+    """Returns (o, lse, residual-or-None).  q, k, v: contiguous bf16 laid out as `layout` names
+    (see triangle_attention); bias: contiguous bf16 [B, H, N, N]; key_mask: contiguous uint8 (or
+    bool) [B, N, N] or None; all on one GPU.  Anything else raises ValueError before any call."""
+    B, N, H, D = _check_inputs(q, k, v, bias, key_mask, layout)
+    o = torch.empty(q.shape, dtype=q.dtype, device=q.device)
     lse = torch.empty((B, N, H, N), dtype=torch.float32, device=q.device)
-    res = torch.empty_like(q) if residual_compensation else None
+    res = torch.empty(q.shape, dtype=q.dtype, device=q.device) if residual_compensation else None
     nws = tri_attn_fwd_workspace_bytes(B, N, H, D)
     ws = _workspace(nws, q.device)
     _check(tri_attn_fwd_ex(STAGE_ALL, LAYOUTS[layout], B, N, H, D, q, k, v, bias, key_mask, o, lse, res, ws,
@@ -228,12 +276,17 @@ def forward(q, k, v, bias, key_mask=None, residual_compensation=True, layout="sl
 
 
 def backward(q, k, v, bias, key_mask, o, lse, residual, dO, layout="slice_head"):
-    """Returns (dq, dk, dv, dbias) with dbias in float32."""
+    """Returns (dq, dk, dv, dbias) with dbias in float32.  The inputs follow forward(); o,
+    residual (or None) and dO have q's shape and dtype, lse is float32 [B, N, H, N]."""
     B, N, H, D = _shape(q, layout)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    dbias = torch.empty((B, H, N, N), dtype=torch.float32, device=q.device)
+    dev, tok = q.device, tuple(q.shape)
+    _check_inputs(q, k, v, bias, key_mask, layout,
+                  more=(("o", o, tok, _BF16), ("lse", lse, (B, N, H, N), (torch.float32,)),
+                        ("residual", residual, tok, _BF16), ("dO", dO, tok, _BF16)))
+    dq, dk, dv = (torch.empty(tok, dtype=q.dtype, device=dev) for _ in range(3))
+    dbias = torch.empty((B, H, N, N), dtype=torch.float32, device=dev)
     nws = tri_attn_bwd_workspace_bytes(B, N, H, D)
-    ws = _workspace(nws, q.device)
+    ws = _workspace(nws, dev)
     _check(tri_attn_bwd_ex(STAGE_ALL, LAYOUTS[layout], B, N, H, D, q, k, v, bias, key_mask, o, lse, residual, dO,
                            dq, dk, dv, dbias, ws, ws.numel()), "tri_attn_bwd_ex")
     return dq, dk, dv, dbias
@@ -273,14 +326,17 @@ def _mul_shape(a, b, direction, layout):
         raise ValueError(f"direction must be one of {sorted(TRI_MUL_DIRECTIONS)}")
     if layout not in TRI_MUL_LAYOUTS:
         raise ValueError(f"layout must be one of {sorted(TRI_MUL_LAYOUTS)}")
-    if a.dim() != 4 or tuple(b.shape) != tuple(a.shape):
-        raise ValueError("a and b must have the same 4-dimensional shape")
+    if not isinstance(a, torch.Tensor) or a.dim() != 4:
+        raise ValueError("a must be a 4-dimensional tensor")
     if layout == "channels_last":
         B, N, N2, C = a.shape
     else:
         B, C, N, N2 = a.shape
     if N2 != N:
         raise ValueError("the two pair indices must have equal extents")
+    _require(a, "a", tuple(a.shape), _BF16)
+    _require(b, "b", tuple(a.shape), _BF16)
+    _one_gpu([("a", a), ("b", b)])
     return B, N, C
 
 
@@ -293,7 +349,7 @@ class _TriMulFn(torch.autograd.Function):
     @staticmethod
     def forward(ctx, a, b, direction, layout):
         B, N, C = _mul_shape(a, b, direction, layout)
-        x = torch.empty_like(a)
+        x = torch.empty(a.shape, dtype=a.dtype, device=a.device)
         ws = _mul_workspace(layout, B, N, C, a.device)
         _check(tri_mul_fwd(TRI_MUL_DIRECTIONS[direction], TRI_MUL_LAYOUTS[layout], B, N, C, a, b, x, ws,
                            0 if ws is None else ws.numel()), "tri_mul_fwd")
@@ -305,10 +361,13 @@ class _TriMulFn(torch.autograd.Function):
     def backward(ctx, dx):
         a, b = ctx.saved_tensors
         B, N, C = ctx.shape
-        da, db = torch.empty_like(a), torch.empty_like(b)
+        dx = dx.contiguous()
+        _require(dx, "dx", tuple(a.shape), _BF16)
+        _one_gpu([("a", a), ("dx", dx)])
+        da, db = (torch.empty(a.shape, dtype=a.dtype, device=a.device) for _ in range(2))
         ws = _mul_workspace(ctx.layout, B, N, C, a.device)
         _check(tri_mul_bwd(TRI_MUL_DIRECTIONS[ctx.direction], TRI_MUL_LAYOUTS[ctx.layout], B, N, C, a, b,
-                           dx.contiguous(), da, db, ws, 0 if ws is None else ws.numel()), "tri_mul_bwd")
+                           dx, da, db, ws, 0 if ws is None else ws.numel()), "tri_mul_bwd")
         return da, db, None, None
 
 
@@ -325,9 +384,14 @@ def triangle_multiplication(a, b, direction="outgoing", layout="channels_last"):
 class _GateFn(torch.autograd.Function):
     @staticmethod
     def forward(ctx, g, p, mask, layout):
-        if g.dim() != 4 or tuple(p.shape) != tuple(g.shape) or g.shape[1] != g.shape[2]:
-            raise ValueError("g and p must both be channels-last [B, N, N, C]")
+        if not isinstance(g, torch.Tensor) or g.dim() != 4 or g.shape[1] != g.shape[2]:
+            raise ValueError("g must be channels-last [B, N, N, C]")
         B, N, _, C = g.shape
+        _require(g, "g", tuple(g.shape), _BF16)
+        _require(p, "p", tuple(g.shape), _BF16)
+        if mask is not None:
+            _require(mask, "mask", (B, N, N), _MASK)
+        _one_gpu([("g", g), ("p", p), ("mask", mask)])
         lay = TRI_MUL_LAYOUTS[layout]
         a = torch.empty((B, C, N, N) if lay == 1 else (B, N, N, C), dtype=g.dtype, device=g.device)
         _check(tri_mul_gate_fwd(lay, B, N, C, g, p, mask, a), "tri_mul_gate_fwd")
@@ -339,8 +403,11 @@ class _GateFn(torch.autograd.Function):
     def backward(ctx, da):
         g, p, mask = ctx.saved_tensors
         B, N, _, C = g.shape
-        dg, dp = torch.empty_like(g), torch.empty_like(p)
-        _check(tri_mul_gate_bwd(ctx.lay, B, N, C, g, p, mask, da.contiguous(), dg, dp), "tri_mul_gate_bwd")
+        da = da.contiguous()
+        _require(da, "da", (B, C, N, N) if ctx.lay == 1 else (B, N, N, C), _BF16)
+        _one_gpu([("g", g), ("da", da)])
+        dg, dp = (torch.empty(g.shape, dtype=g.dtype, device=g.device) for _ in range(2))
+        _check(tri_mul_gate_bwd(ctx.lay, B, N, C, g, p, mask, da, dg, dp), "tri_mul_gate_bwd")
         return dg, dp, None, None
 
 

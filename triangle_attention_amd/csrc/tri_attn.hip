@@ -43,7 +43,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kMaskNeg = -1e9f;  // additive score term of a masked key
+// Largest finite fp16 magnitude: finite bias values are clamped to [-kBiasMax, kBiasMax] in both
+// passes (the backward streams the bias as fp16), so forward and backward see the same scores.
+constexpr float kBiasMax = 65504.0f;
 constexpr int kXcd = 8;            // XCDs per MI355X; dispatch is round-robin over them
 
 // Element offsets of the token tensors (q, k, v, o, residual, dO, dq, dk, dv): entry
@@ -140,8 +142,9 @@ __host__ __device__ __forceinline__ int64_t ctile_off(int m, int n) {
 
 // ------------------------------------------------------------------ bias preparation
 // biasF: forward operand, 32x32 tiles indexed (b,h, query block, key block), element
-// (row m = key k%32, column n = query j%32) in accumulator order; value bias[b,h,j,k]/alpha,
-// -inf for k >= N, 0 for padded queries j >= N.
+// (row m = key k%32, column n = query j%32) in accumulator order; value bias[b,h,j,k]/alpha
+// (finite values clamped to +-kBiasMax first, infinities kept), -inf for k >= N, 0 for padded
+// queries j >= N.
 __global__ void bias_prep_fwd_kernel(const bf16* __restrict__ bias, float* __restrict__ out, int N, int Jp, int Kp,
                                      float inv_alpha, int64_t total) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -158,7 +161,11 @@ __global__ void bias_prep_fwd_kernel(const bf16* __restrict__ bias, float* __res
   float val;
   if (k >= N) val = -INFINITY;
   else if (j >= N) val = 0.0f;
-  else val = (float)bias[(bh * N + j) * N + k] * inv_alpha;
+  else {
+    val = (float)bias[(bh * N + j) * N + k];
+    if (!__builtin_isinf(val)) val = fminf(fmaxf(val, -kBiasMax), kBiasMax);
+    val *= inv_alpha;
+  }
   out[idx] = val;
 }
 
@@ -185,7 +192,7 @@ __global__ void bias_prep_bwd_kernel(const bf16* __restrict__ bias, _Float16* __
   float x = -INFINITY;
   if (j < N && k < N) {
     x = (float)bias[(bh * N + j) * N + k];
-    if (!__builtin_isinf(x)) x = fminf(fmaxf(x, -65504.0f), 65504.0f);
+    if (!__builtin_isinf(x)) x = fminf(fmaxf(x, -kBiasMax), kBiasMax);
   }
   out[idx] = (_Float16)x;
 }
@@ -349,7 +356,6 @@ void fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   const int Kp = (int)round_up(N, 64), Jp = (int)round_up(N, 128);
   const float* btile = biasF + ((int64_t)(b * H + h) * (Jp / 32) + (qt * 4 + w)) * (int64_t)(Kp / 32) * 1024;
   const float c1 = alpha * kLog2e;
-  const float mneg = kMaskNeg / alpha;
   const uint8_t* mrow = MASK ? mask + ((int64_t)b * N + i) * N : nullptr;
 
   // streamed loads: K and V rows (lane -> swizzled 16-byte chunk), this wave's bias tiles
@@ -409,7 +415,7 @@ void fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
         for (int R = 0; R < 4; R++) {
 #pragma unroll
           for (int e = 0; e < 4; e++)
-            if (!Ms_[cur][tt * 32 + R * 8 + g * 4 + e]) s[tt][R * 4 + e] += mneg;
+            if (!Ms_[cur][tt * 32 + R * 8 + g * 4 + e]) s[tt][R * 4 + e] = -INFINITY;
         }
       }
     }
@@ -435,7 +441,8 @@ void fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
 #pragma unroll
       for (int r = 0; r < 16; r++) acc_o[r] *= scale;
     }
-    const float nm = m_run * c1;
+    // (while every score so far is -inf, the reference is 0: exp2(-inf - 0) = 0, not NaN)
+    const float nm = m_run == -INFINITY ? 0.0f : m_run * c1;
     float p[2][16];
     float lsum = 0.0f;
 #pragma unroll
@@ -467,9 +474,12 @@ void fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
     if (MASK && tid < KT) Ms_[cur ^ 1][tid] = mnext;  // read after the next barrier
   }
 
-  // epilogue: normalise, round, residual, logsumexp
+  // epilogue: normalise, round, residual, logsumexp.  A query with no key of finite score (every
+  // key masked, or every key's bias -inf) attends to nothing: o = 0, residual 0, lse = +inf, which
+  // gives every one of its probabilities in the backward exp(s - lse) = 0.
   const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float inv = 1.0f / l_tot;
+  const bool empty = !(l_tot > 0.0f);
+  const float inv = empty ? 0.0f : 1.0f / l_tot;
   if (jok) {
     bf16* orow = o + sbase + (int64_t)j * sT;
     bf16* rrow = res ? res + sbase + (int64_t)j * sT : nullptr;
@@ -487,7 +497,7 @@ void fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
       *(bf16x4*)(orow + c) = ob;
       if (rrow) *(bf16x4*)(rrow + c) = rb;
     }
-    if (g == 0) lse[(((int64_t)b * N + i) * H + h) * N + j] = m_run * alpha + logf(l_tot);
+    if (g == 0) lse[(((int64_t)b * N + i) * H + h) * N + j] = empty ? INFINITY : m_run * alpha + logf(l_tot);
   }
 }
 
@@ -834,7 +844,7 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
       }
       if (MASK && s == 0) {
         const unsigned mb = *(const __attribute__((address_space(3))) unsigned*)(Ks + 2 * 64 * D * 2 + kl * 4);
-        mterm = (kok && (mb & 0xFFu) == 0) ? kMaskNeg * kLog2e : 0.0f;
+        mterm = (kok && (mb & 0xFFu) == 0) ? -INFINITY : 0.0f;
       }
 
       const char* qd = lds + oQD + cur * kQDB;   // this item's Q rows, then its dO rows
