@@ -76,7 +76,9 @@ typedef enum {
                                        span exceeds 32-bit offsets */
   TRI_ATTN_ERROR_MISALIGNED = 3,    /* a tensor pointer that is not 16-byte aligned */
   TRI_ATTN_ERROR_WORKSPACE = 4,     /* workspace NULL or smaller than *_workspace_bytes() */
-  TRI_ATTN_ERROR_LAUNCH = 5         /* the HIP runtime rejected a kernel launch */
+  TRI_ATTN_ERROR_LAUNCH = 5,        /* the HIP runtime rejected a kernel launch */
+  TRI_ATTN_ERROR_SCRATCH_LIMIT = 6  /* tri_attn_fwd_noalloc: the shape needs more than
+                                       TRI_ATTN_NOALLOC_SCRATCH_BYTES of scratch */
 } tri_attn_status;
 
 /* Human-readable name of a status code (static storage; never NULL). */
@@ -199,6 +201,35 @@ tri_attn_status tri_attn_bwd_ex(unsigned stages, int layout, int64_t B, int64_t 
                                 const void *dO,
                                 void *dq, void *dk, void *dv, float *dbias,
                                 void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Allocation-free forward, for callers that cannot allocate device memory while they run: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * The same computation and results as tri_attn_fwd on the same arguments (same kernels, bit for
+ * bit), without a workspace argument: the scratch it needs (B*H*ceil(N/64)*64*ceil(N/128)*128*4
+ * bytes of prepared bias tiles, rounded up to 256) lives in a device array inside the library,
+ * TRI_ATTN_NOALLOC_SCRATCH_BYTES = 64 MiB per GPU, which each GPU the library runs on holds
+ * until the process ends.  The call makes no hipMalloc, hipFree or other allocating call.
+ *   - Shapes needing more scratch than that return TRI_ATTN_ERROR_SCRATCH_LIMIT before anything
+ *     is launched (at N = 768, up to B*H = 28 slices' heads fit; tri_attn_noalloc_scratch_bytes()
+ *     and tri_attn_fwd_workspace_bytes() give the two sizes).
+ *   - Every call on one GPU uses that GPU's one array, on the caller's stream: calls that
+ *     overlap on one GPU (other streams, other host threads) race and must be serialised by
+ *     the caller.  Nothing needs clearing between calls: each call writes all the scratch it
+ *     reads before reading it.
+ *   - The scratch belongs to the current device (hipGetDevice); `stream` must be a stream of
+ *     that device.  Its address is looked up once per device, on the first call there.
+ *   - Otherwise as tri_attn_fwd: slice-major layout [B, N, H, N, D], same validation and errors.
+ */
+#define TRI_ATTN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+size_t tri_attn_noalloc_scratch_bytes(void);
+
+tri_attn_status tri_attn_fwd_noalloc(int64_t B, int64_t N, int64_t H, int64_t D,
+                                     const void *q, const void *k, const void *v, const void *bias,
+                                     const uint8_t *key_mask,
+                                     void *o, float *lse, void *residual, hipStream_t stream);
 
 #ifdef __cplusplus
 }

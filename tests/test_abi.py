@@ -12,7 +12,7 @@ import pytest
 import triangle_attention_amd as ta
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-SUCCESS, INVALID, UNSUPPORTED, MISALIGNED, WORKSPACE, LAUNCH = range(6)
+SUCCESS, INVALID, UNSUPPORTED, MISALIGNED, WORKSPACE, LAUNCH, SCRATCH_LIMIT = range(7)
 
 
 @pytest.fixture(scope="module")
@@ -40,7 +40,8 @@ def test_exports_every_declared_symbol(lib):
 
 def test_status_strings(lib):
     for code, name in [(SUCCESS, "SUCCESS"), (INVALID, "INVALID_VALUE"), (UNSUPPORTED, "UNSUPPORTED"),
-                       (MISALIGNED, "MISALIGNED"), (WORKSPACE, "WORKSPACE"), (LAUNCH, "LAUNCH")]:
+                       (MISALIGNED, "MISALIGNED"), (WORKSPACE, "WORKSPACE"), (LAUNCH, "LAUNCH"),
+                       (SCRATCH_LIMIT, "SCRATCH_LIMIT")]:
         assert ta.tri_attn_status_string(code).endswith(name)
     assert "UNKNOWN" in ta.tri_attn_status_string(1234)
 
@@ -229,3 +230,19 @@ def test_tri_mul_gate_validation(lib):
     assert fwd(0, 1, 64, 32, a=g + 64) == INVALID
     assert bwd(0, 1, 64, 32, dg=dp) == INVALID
     assert bwd(0, 1, 64, 32, dp=da + 32) == INVALID
+
+
+def test_noalloc_forward_validation(lib):
+    """The allocation-free forward rejects, before any HIP call, what tri_attn_fwd rejects, and
+    shapes whose prepared bias exceeds the library's scratch array."""
+    assert ta.tri_attn_noalloc_scratch_bytes() == 64 << 20
+    P = 1 << 20  # fake, 16-byte aligned; never dereferenced
+    args = lambda B, N, H, D, q=P: (B, N, H, D, q, P, P, P, None, P, P, P, 0)  # noqa: E731
+    assert ta.tri_attn_fwd_noalloc(*args(0, 8, 1, 16)) == INVALID
+    assert ta.tri_attn_fwd_noalloc(*args(1, 8, 1, 64)) == UNSUPPORTED
+    assert ta.tri_attn_fwd_noalloc(*args(1, 8, 1, 16, q=0)) == INVALID
+    # N = 768: 2359296 bytes of prepared bias per (batch, head); 28 fit in 64 MiB, 29 do not
+    assert ta.tri_attn_fwd_workspace_bytes(1, 768, 28, 32) <= 64 << 20 < ta.tri_attn_fwd_workspace_bytes(1, 768, 29, 32)
+    assert ta.tri_attn_fwd_noalloc(*args(1, 768, 29, 32)) == SCRATCH_LIMIT
+    assert ta.tri_attn_fwd_workspace_bytes(2, 1024, 8, 16) == 64 << 20  # exactly full: accepted
+    assert ta.tri_attn_fwd_noalloc(*args(2, 1024, 9, 16)) == SCRATCH_LIMIT

@@ -20,7 +20,8 @@ from ._build import LIB_PATH, build  # noqa: F401
 __all__ = [
     "TriAttnError", "load_library", "tri_attn_status_string", "tri_attn_fwd_workspace_bytes",
     "tri_attn_bwd_workspace_bytes", "tri_attn_fwd", "tri_attn_bwd", "tri_attn_fwd_stages", "tri_attn_bwd_stages",
-    "tri_attn_fwd_ex", "tri_attn_bwd_ex", "triangle_attention", "TRI_ATTN_MAX_N", "TRI_ATTN_FWD_MAX_N", "LAYOUTS",
+    "tri_attn_fwd_ex", "tri_attn_bwd_ex", "tri_attn_fwd_noalloc", "tri_attn_noalloc_scratch_bytes",
+    "triangle_attention", "TRI_ATTN_MAX_N", "TRI_ATTN_FWD_MAX_N", "LAYOUTS",
     "tri_mul_fwd", "tri_mul_bwd", "tri_mul_workspace_bytes", "tri_mul_gate_fwd", "tri_mul_gate_bwd",
     "triangle_multiplication", "gated_operand", "TRI_MUL_DIRECTIONS", "TRI_MUL_LAYOUTS",
     "TRI_MUL_MAX_N",
@@ -67,6 +68,10 @@ def load_library(path: str = LIB_PATH):
     lib.tri_attn_fwd_ex.restype = ctypes.c_int
     lib.tri_attn_bwd_ex.argtypes = [ctypes.c_uint, ctypes.c_int] + lib.tri_attn_bwd.argtypes
     lib.tri_attn_bwd_ex.restype = ctypes.c_int
+    lib.tri_attn_noalloc_scratch_bytes.argtypes = []
+    lib.tri_attn_noalloc_scratch_bytes.restype = sz
+    lib.tri_attn_fwd_noalloc.argtypes = [i64, i64, i64, i64] + [vp] * 8 + [vp]
+    lib.tri_attn_fwd_noalloc.restype = ctypes.c_int
     lib.tri_mul_gate_fwd.argtypes = [ctypes.c_int, i64, i64, i64, vp, vp, vp, vp, vp]
     lib.tri_mul_gate_fwd.restype = ctypes.c_int
     lib.tri_mul_gate_bwd.argtypes = [ctypes.c_int, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp]
@@ -122,6 +127,17 @@ def tri_attn_bwd(B, N, H, D, q, k, v, bias, key_mask, o, lse, residual, dO, dq, 
                                            _ptr(o), _ptr(lse), _ptr(residual), _ptr(dO), _ptr(dq), _ptr(dk),
                                            _ptr(dv), _ptr(dbias), _ptr(workspace), int(workspace_bytes),
                                            _stream(stream)))
+
+
+def tri_attn_noalloc_scratch_bytes() -> int:
+    return int(load_library().tri_attn_noalloc_scratch_bytes())
+
+
+def tri_attn_fwd_noalloc(B, N, H, D, q, k, v, bias, key_mask, o, lse, residual, stream=None) -> int:
+    """Marshal to the allocation-free forward (scratch inside the library); returns the status code."""
+    return int(load_library().tri_attn_fwd_noalloc(B, N, H, D, _ptr(q), _ptr(k), _ptr(v), _ptr(bias),
+                                                   _ptr(key_mask), _ptr(o), _ptr(lse), _ptr(residual),
+                                                   _stream(stream)))
 
 
 STAGE_PREP, STAGE_MAIN, STAGE_FINAL, STAGE_ALL = 1, 2, 4, 7

@@ -29,6 +29,7 @@
 #include <string.h>
 #include <math.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "tri_attn.h"
@@ -1363,12 +1364,38 @@ tri_attn_status launch_bwd(unsigned stages, const Plan& P, const TokLayout& L, c
   return hipGetLastError() == hipSuccess ? TRI_ATTN_SUCCESS : TRI_ATTN_ERROR_LAUNCH;
 }
 
+// ------------------------------------------------------------------ allocation-free forward
+// Device-resident scratch of tri_attn_fwd_noalloc: the prepared forward bias tiles of one call.
+// The runtime gives every GPU the library runs on its own copy, at its own address, held until
+// the process ends.  In host code `scratch` names a host-side stand-in, never a device address:
+// the address a kernel may use comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[TRI_ATTN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch (looked up on the first call per device).
+tri_attn_status current_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return TRI_ATTN_ERROR_LAUNCH;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return TRI_ATTN_ERROR_LAUNCH;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return TRI_ATTN_SUCCESS;
+}
+
 }  // namespace
 
 extern "C" {
 
 const char* tri_attn_status_string(int status) {
   switch (status) {
+    case TRI_ATTN_ERROR_SCRATCH_LIMIT: return "TRI_ATTN_ERROR_SCRATCH_LIMIT";
     case TRI_ATTN_SUCCESS: return "TRI_ATTN_SUCCESS";
     case TRI_ATTN_ERROR_INVALID_VALUE: return "TRI_ATTN_ERROR_INVALID_VALUE";
     case TRI_ATTN_ERROR_UNSUPPORTED: return "TRI_ATTN_ERROR_UNSUPPORTED";
@@ -1433,6 +1460,25 @@ tri_attn_status tri_attn_fwd(int64_t B, int64_t N, int64_t H, int64_t D, const v
                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return tri_attn_fwd_stages(TRI_ATTN_STAGE_ALL, B, N, H, D, q, k, v, bias, key_mask, o, lse, residual, workspace,
                              workspace_bytes, stream);
+}
+
+size_t tri_attn_noalloc_scratch_bytes(void) { return (size_t)TRI_ATTN_NOALLOC_SCRATCH_BYTES; }
+
+tri_attn_status tri_attn_fwd_noalloc(int64_t B, int64_t N, int64_t H, int64_t D, const void* q, const void* k,
+                                     const void* v, const void* bias, const uint8_t* key_mask, void* o, float* lse,
+                                     void* residual, hipStream_t stream) {
+  // host-only checks first, in the order of tri_attn_fwd_ex, then the scratch limit; no HIP call
+  // is made unless all of them pass
+  if (B < 1 || N < 1 || H < 1) return TRI_ATTN_ERROR_INVALID_VALUE;
+  if (!shape_ok(B, N, H, D, TRI_ATTN_FWD_MAX_N)) return TRI_ATTN_ERROR_UNSUPPORTED;
+  if (!q || !k || !v || !bias || !o || !lse) return TRI_ATTN_ERROR_INVALID_VALUE;
+  const Plan P = make_plan(B, N, H, D);
+  if (P.bias_f32_bytes > (int64_t)TRI_ATTN_NOALLOC_SCRATCH_BYTES) return TRI_ATTN_ERROR_SCRATCH_LIMIT;
+  void* ws = nullptr;
+  const tri_attn_status st = current_scratch(&ws);
+  if (st != TRI_ATTN_SUCCESS) return st;
+  return tri_attn_fwd_ex(TRI_ATTN_STAGE_ALL, TRI_ATTN_LAYOUT_SLICE_HEAD, B, N, H, D, q, k, v, bias, key_mask, o, lse,
+                         residual, ws, (size_t)TRI_ATTN_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 tri_attn_status tri_attn_bwd_ex(unsigned stages, int layout, int64_t B, int64_t N, int64_t H, int64_t D,
