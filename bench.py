@@ -48,6 +48,9 @@ def _parse():
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--no-residual", action="store_true", help="uncompensated backward correction")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle CPU-baseline budget (0 = skip)")
+    ap.add_argument("--cpu-protocol", nargs="*", default=None, metavar="WORKLOAD",
+                    help="only time the FP64 oracle on whole workloads (all five by default), forward and "
+                         "backward apart, and print one JSON line per workload")
     ap.add_argument("--graph", action="store_true",
                     help="also time the whole fwd+bwd step captured in one HIP graph (small-N launch latency)")
     ap.add_argument("--op", choices=("attention", "trimul"), default="attention")
@@ -76,32 +79,88 @@ def _traffic(bytes_alg: float, path: str = TRAFFIC_FILE, src: str = KERNEL_SRC, 
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, inp, budget_s: float):
-    """The FP64 oracle as it stands, fwd+bwd slice by slice (all heads), until the budget is spent."""
-    import oracle
-    from tri_synth import bf16_bits_to_f64
+def cpu_info() -> dict:
+    """The host the oracle runs on: CPU model, usable cores, BLAS library and its thread count."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas, threads = None, None
     try:
         from threadpoolctl import threadpool_info
-        threads = max([d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"] or [1])
+        for d in threadpool_info():
+            if d.get("user_api") == "blas":
+                blas = f"{d.get('internal_api')} {d.get('version')}"
+                threads = max(threads or 0, int(d.get("num_threads", 1)))
     except Exception:
-        threads = len(os.sched_getaffinity(0))
+        pass
+    host = len(os.sched_getaffinity(0))
+    return {"cpu_model": model, "host_cores": host, "blas": blas, "blas_threads": threads or host}
+
+
+def cpu_baseline(w, inp, budget_s: float):
+    """The FP64 oracle as it stands, slice by slice (all heads), forward then backward, until the
+    budget is spent; forward and backward timed apart.  The backward of a slice recomputes its
+    forward, as the oracle is written."""
+    import oracle
+    from tri_synth import bf16_bits_to_f64
+    info = cpu_info()
     x = {n: bf16_bits_to_f64(inp[n]) for n in ("q", "k", "v", "bias", "dO")}
     m = inp["key_mask"]
-    t0 = time.perf_counter()
+    t_f = t_b = 0.0
     done = 0
+    t0 = time.perf_counter()
     for i in range(w.N):
         for h in range(w.H):
             mrow = None if m is None else m[0, i]
+            a = time.perf_counter()
             oracle.slice_forward64(x["q"][0, i, h], x["k"][0, i, h], x["v"][0, i, h], x["bias"][0, h], mrow)
+            b = time.perf_counter()
             oracle.slice_backward64(x["q"][0, i, h], x["k"][0, i, h], x["v"][0, i, h], x["bias"][0, h],
                                     x["dO"][0, i, h], mrow)
+            t_f += b - a
+            t_b += time.perf_counter() - b
         done += 1
         if time.perf_counter() - t0 >= budget_s:
             break
-    dt = time.perf_counter() - t0
-    flops = 14.0 * w.N * w.N * w.H * w.D * done  # fwd (4) + bwd (10) per score element
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} of {w.N} slices x {w.H} heads of {w.name}, fwd+bwd in FP64 ({dt:.1f} s)"}
+    per = w.N * w.N * w.H * w.D * done  # score elements x d of the sample
+    f_fwd, f_bwd = 4.0 * per, 10.0 * per
+    return {"value": (f_fwd + f_bwd) / (t_f + t_b) / 1e12, "unit": "TFLOP/s", "cores": int(info["blas_threads"]),
+            "kind": "oracle",
+            "sample": f"{done} of {w.N} slices x {w.H} heads of {w.name}, forward then backward in FP64 "
+                      f"({t_f + t_b:.1f} s)",
+            "fwd_tflops": f_fwd / t_f / 1e12, "bwd_tflops": f_bwd / t_b / 1e12, **info}
+
+
+def cpu_protocol(names):
+    """The oracle on whole workloads, forward and backward timed apart: median of three runs for
+    the small workloads, one run for crop 768.  One JSON line per workload."""
+    import statistics
+    import oracle
+    from tri_synth import WORKLOADS, bf16_bits_to_f64, workload_inputs
+    info = cpu_info()
+    for name in names:
+        w = WORKLOADS[name]
+        inp = workload_inputs(w)
+        x = {n: bf16_bits_to_f64(inp[n]) for n in ("q", "k", "v", "bias", "dO")}
+        m = inp["key_mask"]
+        runs = 1 if w.N >= 768 else 3
+        tf, tb = [], []
+        for _ in range(runs):
+            a = time.perf_counter()
+            oracle.forward64(x["q"], x["k"], x["v"], x["bias"], m)
+            b = time.perf_counter()
+            oracle.backward64(x["q"], x["k"], x["v"], x["bias"], x["dO"], m)
+            tf.append(b - a)
+            tb.append(time.perf_counter() - b)
+        f, b_ = statistics.median(tf), statistics.median(tb)
+        print(json.dumps({"workload": name, "runs": runs, "t_fwd_s": round(f, 3), "t_bwd_s": round(b_, 3),
+                          "fwd_gflops": round(w.flops_fwd / f / 1e9, 2), "bwd_gflops": round(w.flops_bwd / b_ / 1e9, 2),
+                          "fwd_bwd_s": round(f + b_, 3), **info}), flush=True)
 
 
 def trimul_cpu_baseline(a64, b64, dx64, budget_s: float):
@@ -251,6 +310,10 @@ def main():
         print(f"bench.py measures one GPU only: the library has no multi-GPU path (asked for --gpus {args.gpus}, "
               f"WORLD_SIZE {world}).", file=sys.stderr)
         sys.exit(2)
+    if args.cpu_protocol is not None:
+        cpu_protocol(args.cpu_protocol or ["n64_h4_d16", "n384_h4_d32", "n640_h4_d16_mask64", "n768_h4_d32",
+                                           "n768_h4_d16_bias4"])
+        return
     if args.op == "trimul":
         main_trimul(args)
         return

@@ -1,10 +1,10 @@
 """Small workloads for hardware-counter runs under rocprofv3.
 
-  python3 -m triangle_attention_amd.profile_drv attn [workload] [reps]
+  python3 profile_drv.py attn [workload] [reps]
       forward + backward of a synthetic workload through the C ABI, `reps` times
-  python3 -m triangle_attention_amd.profile_drv mul [workload] [layout] [reps]
+  python3 profile_drv.py mul [workload] [layout] [reps]
       triangle multiplication core, both directions, forward + backward, `reps` times
-  python3 -m triangle_attention_amd.profile_drv copy [mib] [reps]
+  python3 profile_drv.py copy [mib] [reps]
       a plain device-to-device copy of `mib` MiB (torch's copy kernel), used to
       calibrate FETCH_SIZE / WRITE_SIZE against a known byte count
 """
@@ -13,7 +13,7 @@ from __future__ import annotations
 import os
 import sys
 
-ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
