@@ -113,9 +113,12 @@ size_t tri_attn_bwd_workspace_bytes(int64_t B, int64_t N, int64_t H, int64_t D);
  * FP32 from o + residual when residual is non-NULL (compensated), or from the bf16 o
  * alone when residual is NULL.  dv does not depend on this choice.
  *
- * The key-tile-parallel scheme recomputes each probability tile once for all four
- * gradients and reduces dq (over key blocks) and dbias (over slice groups) through
- * ordered partial buffers held in the workspace (TurboPairFormer Abstract).
+ * A key-tile-parallel kernel recomputes each probability tile once for dk, dv and dbias and
+ * sums dbias over slices on chip, then over slice groups through ordered partial buffers held
+ * in the workspace (TurboPairFormer Abstract: probability recomputation, ordered partial
+ * reductions, no stored score gradient).  dq sums over every key: a query-tile kernel
+ * recomputes the probability and score-gradient tiles once more and sums dq in FP32 in key
+ * order, rounding once.  Every sum runs in a fixed order, so results are bitwise reproducible.
  */
 tri_attn_status tri_attn_bwd(int64_t B, int64_t N, int64_t H, int64_t D,
                              const void *q, const void *k, const void *v, const void *bias,
@@ -133,7 +136,8 @@ tri_attn_status tri_attn_bwd(int64_t B, int64_t N, int64_t H, int64_t D,
  * stage to the next.  Validation is the same as for the unstaged call.
  *   forward : PREP = bias conversion into the workspace; MAIN = attention kernel; FINAL = none
  *   backward: PREP = bias conversion and the correction D; MAIN = the key-tile-parallel kernel
- *             (all five products); FINAL = ordered sums of the dq and dbias partials
+ *             (dk, dv, dbias partials); FINAL = the query-tile dq kernel and the ordered sums
+ *             of the dbias partials
  */
 #define TRI_ATTN_STAGE_PREP 1u
 #define TRI_ATTN_STAGE_MAIN 2u

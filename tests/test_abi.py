@@ -51,8 +51,9 @@ def test_workspace_sizes(lib):
         f = ta.tri_attn_fwd_workspace_bytes(B, N, H, D)
         b = ta.tri_attn_bwd_workspace_bytes(B, N, H, D)
         assert f > 0 and b > 0 and f % 256 == 0 and b % 256 == 0
-        # the backward holds one bf16 dq partial (2 bytes per element) per 64-key block
-        assert b >= -(-N // 64) * B * N * H * N * D * 2
+        # the backward holds the pair bias twice (fp16 column blocks, FP32 tiles), the -lse2 and
+        # -D rows (8 bytes per query) and one FP32 pair-bias partial per slice group
+        assert b >= B * H * N * N * (2 + 4 + 4) + B * N * H * N * 8
     for bad in [(0, 8, 1, 16), (1, 0, 1, 16), (1, 8, 0, 16), (1, 8, 1, 64), (1, 4097, 1, 16)]:
         assert ta.tri_attn_fwd_workspace_bytes(*bad) == 0
         assert ta.tri_attn_bwd_workspace_bytes(*bad) == 0
@@ -66,8 +67,7 @@ def test_workspace_sizes(lib):
     # per chunk: two chunks at N = 769, three at N = 2048
     for N, nqc in [(769, 2), (1536, 2), (1537, 3), (2048, 3)]:
         b = ta.tri_attn_bwd_workspace_bytes(1, N, 2, 32)
-        assert b >= -(-N // 64) * N * 2 * N * 32 * 2 + 2 * nqc * N * 2 * N * 32 * 4, N
-    # the backward partial buffers grow with N (dq partials per 64-key block)
+        assert b >= 2 * N * N * (2 + 4 + 4) + 2 * nqc * N * 2 * N * 32 * 4, N
     assert ta.tri_attn_bwd_workspace_bytes(1, 768, 4, 32) > ta.tri_attn_bwd_workspace_bytes(1, 384, 4, 32)
 
 

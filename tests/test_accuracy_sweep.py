@@ -13,10 +13,10 @@ exact gradient to bf16, rrmse(bf16_RNE(x64), x64).  What the residual can change
 excess of that floor, sqrt(rrmse^2 - floor^2); the sweep reports it with and without the
 residual (dbias is FP32, its floor is negligible).
 
-A rounding model of the kernel locates the rest: the exact (FP64) dS and P rounded to bf16 before
-the products, exact sums, dq summed from bf16 partials over 64-key blocks, and every output rounded
-to bf16.  Its error against FP64 matches the GPU's for dq, dk and dv, so their error is the bf16
-rounding of the products' operands and of the partials, which the residual does not touch; dbias
+A rounding model of the kernels locates the rest: the exact (FP64) dS and P rounded to bf16 before
+the products, exact sums (dq, dk and dv each one sum over all keys or queries), and every output
+rounded to bf16.  Its error against FP64 matches the GPU's for dq, dk and dv, so their error is the
+bf16 rounding of the products' operands, which the residual does not touch; dbias
 sums FP32 dS over slices with none of these roundings, so the error of the correction D is what
 remains in it, and that is what the residual lowers.  The table is printed (`pytest -s`) and its
 figures are quoted where the design notes discuss accuracy.
@@ -79,8 +79,7 @@ def _model(x, slices):
             _, _, p = oracle.slice_forward64(q, k, v, x["bias"][0, h])
             _, _, _, ds = oracle.slice_backward64(q, k, v, x["bias"][0, h], dO)
             dsb, pb = _round_bf16(ds), _round_bf16(p)
-            parts = [_round_bf16(dsb[:, c:c + 64] @ k[c:c + 64]) for c in range(0, N, 64)]
-            out["dq"][0, n, h] = _round_bf16(alpha * np.sum(parts, axis=0))
+            out["dq"][0, n, h] = _round_bf16(alpha * (dsb @ k))
             out["dk"][0, n, h] = _round_bf16(alpha * (dsb.T @ q))
             out["dv"][0, n, h] = _round_bf16(pb.T @ dO)
     return out

@@ -41,8 +41,8 @@ def test_five_calls_bitwise_wide_bias_768():
 
 @pytest.mark.parametrize("name", ["n768_h4_d32", "n640_h4_d16_mask64"])
 def test_five_calls_bitwise_full_size(name):
-    # the other full-size workloads (both head dimensions, with and without the key mask):
-    # every store of the dq partials is exercised at the benchmark's launch configuration
+    # the other full-size workloads (both head dimensions, with and without the key mask), each
+    # kernel at the benchmark's launch configuration
     _five_calls_identical(workload_inputs(WORKLOADS[name]))
 
 

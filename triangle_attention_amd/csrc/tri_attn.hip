@@ -95,6 +95,25 @@ typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) u32x4v lu32x4;
 typedef unsigned u32x2v __attribute__((ext_vector_type(2)));
 
+// 32x32 product over k = 8 from two-dword operands (lane l: row or column l % 32, k = 4 (l / 32)
+// + 0..3); as fast as the k = 16 form, with half the operand registers
+typedef short s16x4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x16 mfma32k8(u32x2v a, u32x2v b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(__builtin_bit_cast(s16x4v, a), __builtin_bit_cast(s16x4v, b), c, 0, 0, 0);
+}
+
+// x as three bf16 parts (hi, mid, lo: each the round-to-nearest-even of what the parts before it
+// leave) and a zero, packed into two dwords; the parts sum to x exactly for a finite x below the
+// bf16 range limit (24 significand bits in three 8-bit parts)
+__device__ __forceinline__ u32x2v split3_bf16(float x) {
+  const bf16 hi = (bf16)x;
+  const float r1 = x - (float)hi;
+  const bf16 mid = (bf16)r1;
+  const bf16 lo = (bf16)(r1 - (float)mid);
+  return u32x2v{(unsigned)__builtin_bit_cast(unsigned short, hi) | ((unsigned)__builtin_bit_cast(unsigned short, mid) << 16),
+                (unsigned)__builtin_bit_cast(unsigned short, lo)};
+}
+
 // Lane part of a transposed read: lane t of a 16-lane group addresses row t/4 and
 // column 4*(t%4) of the 4x16 block it helps to load.
 __device__ __forceinline__ int tr_lane(int ld) {
@@ -554,17 +573,15 @@ void bwd_pre_kernel(const bf16* __restrict__ dO, const bf16* __restrict__ o, con
 // summed over slices on chip and written once per group.  The steps of a slice are
 // unrolled at compile time so that every face slot is addressed statically.
 //
-// One barrier per item.  The dQ product of an item needs dS from both key halves, so it
-// runs one item late: after the barrier that starts item t, every wave has written its
-// dS^T of item t-1, and the wave computes dQ of item t-1 after the products of item t
-// (placed last, its LDS reads do not pile up right behind the barrier).
-// dS^T, K and V are therefore kept in two (dS^T) and three (K/V, a buffer per slice)
-// copies in LDS.
+// dQ is not formed here: it sums over every key block, and dq_kernel computes it on its own
+// (see there), so nothing leaves this work-group but dK, dV and the pair-bias gradient.
 //
-// Software pipeline: while item t is computed, item t+1's Q, dO, lse2, -D and pair-bias
+// One barrier per item.  Software pipeline: while item t is computed, item t+1's Q, dO, lse2,
+// -D and pair-bias
 // tiles stream from global memory straight into the other half of double-buffered LDS
 // (direct-to-LDS loads, no registers involved), and the next slice's K, V and key-mask
-// bytes stream into their own buffer from the first item of a slice on.  Rows past N read
+// bytes stream into the other of two K/V buffers from the first item of a slice on (the
+// first barrier of a slice is the point after which no wave reads the previous slice's).  Rows past N read
 // as zeros through the buffer range check, and the -inf padding of the prepared bias turns
 // every padded query or key into an exact zero probability.
 //
@@ -613,23 +630,21 @@ template <int D, bool MASK, int NS, bool STRIDED, bool CHUNKED>
 __global__ __launch_bounds__(512, 1)
 void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
                 const bf16* __restrict__ dO, const bf16* __restrict__ biasB, const uint8_t* __restrict__ mask,
-                const float* __restrict__ LDp, unsigned* __restrict__ dqp, float* __restrict__ dbp, bf16* __restrict__ dk, bf16* __restrict__ dv,
+                const float* __restrict__ LDp, float* __restrict__ dbp, bf16* __restrict__ dk, bf16* __restrict__ dv,
                 int B, int N, int H, int G, int ngroups, float alpha, TokLayout Lg, Chunking Ck) {
   const TokLayout L = tok_layout<STRIDED, D>(Lg, N, H);
   constexpr int NC = D / 16;
   constexpr int CPR = D / 8;    // 16-byte chunks per row
-  constexpr int LDT = 128 + 8;  // dS^T row stride (elements), padded
   constexpr int NR = D / 2;     // accumulator registers of dK^T / dV^T holding channels c < D
-  // LDS map (bytes): pair-bias tiles x2 | Q,dO x2 | K,V,mask x3 | lse2,-D x2 | dS^T x2 | dK/dV reduction
+  // LDS map (bytes): pair-bias tiles x2 | Q,dO x2 | K,V,mask x2 | lse2,-D x2 | dK/dV reduction
   // (the odd query lanes' partials)
   constexpr int kBiasB = 8 * 2048;                  // 8 waves x one 32x32 bf16 tile
   constexpr int kQDB = 2 * 128 * D * 2;             // Q rows then dO rows
   constexpr int kKVB = 2 * 64 * D * 2 + 64 * 4;     // K rows, V rows, 64 mask bytes (one per dword)
   constexpr int kLDB = 2 * 128 * 4;                 // lse2 rows then -D rows
-  constexpr int kSTB = 64 * LDT * 2;
   constexpr int kREDB = 4 * 2 * NR * 64 * 4;        // dK^T, dV^T partials of four waves
-  constexpr int oBias = 0, oQD = oBias + 2 * kBiasB, oKV = oQD + 2 * kQDB, oLD = oKV + 3 * kKVB;
-  constexpr int oST = oLD + 2 * kLDB, oRED = oST + 2 * kSTB, kLdsBytes = oRED + kREDB;
+  constexpr int oBias = 0, oQD = oBias + 2 * kBiasB, oKV = oQD + 2 * kQDB, oLD = oKV + 2 * kKVB;
+  constexpr int oRED = oLD + 2 * kLDB, kLdsBytes = oRED + kREDB;
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
   __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
 
@@ -676,9 +691,6 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   const float c1 = alpha * kLog2e;
   const int sT = L.sT;
   const int span = L.span_bytes(N, D);                                   // bytes of a slice-head's rows
-  const int nqt = Jpt / 16;                                              // 16-query tiles per slice
-  const int64_t dq_kb_stride = (int64_t)B * N * H * nqt * (16 * D * 2);  // bytes of one key block's partials
-  const int nitems = (i_end - i_begin) * nsteps;
 
   // Per-lane byte offset of the streamed Q and dO loads, fixed for the whole work-group; slice
   // and step enter through the buffer base and the scalar offset.  Q, dO, K and V land swizzled.
@@ -690,7 +702,6 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   //  * row reads (A/B operands of the 32x32x16 products): row rr = (p or kh)*32 + ln, chunk
   //    cc*2+g in swizzled position; the swizzle of such a row depends on ln only
   //  * transposed reads of dO/Q (dV^T, dK^T A operands) over query rows p*32 + m2*16 + 4g (+8)
-  //  * transposed reads of K (dQ^T A operand) over key rows 8*(l/16) (+4) of each 32-key half
   const int swl = swz<D>(ln);
   unsigned offR[NC];
 #pragma unroll
@@ -700,16 +711,8 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   const int c0 = D == 32 ? 16 * chalf : 0;
   const unsigned trA = (unsigned)((tr_off<D>(l, 4 * g, c0) + p * 32 * D) * 2);
   const unsigned trB = (unsigned)((tr_off<D>(l, 4 * g + 8, c0) + p * 32 * D) * 2);
-  unsigned trK[NC][2];
-#pragma unroll
-  for (int u = 0; u < NC; u++) {
-    trK[u][0] = (unsigned)(tr_off<D>(l, 8 * G16, u * 16) * 2);
-    trK[u][1] = (unsigned)(tr_off<D>(l, 8 * G16 + 4, u * 16) * 2);
-  }
   const unsigned offBias = (unsigned)((kh * 4 + p) * 2048 + l * 16);
   const unsigned offRow = (unsigned)((p * 32 + g * 4) * 4);  // lse2 / -D rows of this lane
-  const unsigned offST = (unsigned)((kl * LDT + p * 32 + g * 4) * 2);  // dS^T write
-  const unsigned offSTr = (unsigned)((8 * G16 * LDT + (w >> 1) * 32 + (w & 1) * 16 + tr_lane(LDT)) * 2);
 
   // issue the loads of work item (ii, ss) into LDS buffer `buf`; rows past N read as zeros
   // LDS byte address of the work-group's LDS block; the streamed loads take LDS addresses
@@ -763,49 +766,8 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   RowRes rr_cur = row_res(i_begin);  // descriptors of slice i
   prefetch(rr_cur, 0, 0);
 
-  // dQ^T tiles (16 channels x 16 queries) of the previous item over the 64 keys of this
-  // block, stored as this block's bf16 partial: one 16 x D block per (slice, 16-query tile),
-  // lane-major, so that every store writes whole cache lines
-  int64_t prev_sl = 0;
-  int prev_s = 0, prev_kv = 0;
-  auto dq_product = [&](int stb) {
-    const char* kbase = lds + oKV + prev_kv * kKVB;
-    const char* sbase_t = lds + oST + stb * kSTB + offSTr;
-    bf16x4 pk[NC];
-    // all operands first (one latency), then the products
-    bf16x8 a[NC][2], bb[2];
-#pragma unroll
-    for (int kk = 0; kk < 2; kk++) {
-      bb[kk] = cat8(tr16p((const lbf16*)(sbase_t + kk * 32 * LDT * 2)),
-                    tr16p((const lbf16*)(sbase_t + (kk * 32 + 4) * LDT * 2)));
-#pragma unroll
-      for (int u = 0; u < NC; u++)
-        a[u][kk] = cat8(tr16p((const lbf16*)(kbase + trK[u][0] + kk * 32 * D * 2)),
-                        tr16p((const lbf16*)(kbase + trK[u][1] + kk * 32 * D * 2)));
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int u = 0; u < NC; u++) {
-      f32x4 c = {};
-#pragma unroll
-      for (int kk = 0; kk < 2; kk++) c = mfma16(a[u][kk], bb[kk], c);
-#pragma unroll
-      for (int e = 0; e < 4; e++) pk[u][e] = (bf16)c[e];
-    }
-    char* blk = (char*)dqp + kb * dq_kb_stride + ((prev_sl * nqt + (s_base + prev_s) * 8 + w) * (int64_t)(16 * D * 2));
-    // streaming stores: the partials are read back once, by the final reduction
-    if (NC == 2) {
-      const bf16x8 v8 = __builtin_shufflevector(pk[0], pk[NC - 1], 0, 1, 2, 3, 4, 5, 6, 7);
-      __builtin_nontemporal_store(__builtin_bit_cast(u32x4v, v8), (u32x4v*)(blk + (unsigned)(l * 16)));
-    } else {
-      __builtin_nontemporal_store(__builtin_bit_cast(u32x2v, pk[0]), (u32x2v*)(blk + (unsigned)(l * 8)));
-    }
-  };
-
-  // VMEM operations a wave issues after an item's prefetch and before that item's wait:
-  // the previous item's dq stores and, after the last item of a slice, the dK/dV stores
-  constexpr int kDqStores = 1;
-  // dk and dv stores of a slice's end: p = 0 waves whose 32 keys are not all past N (the
+  // VMEM operations a wave issues after an item's prefetch and before that item's wait: after
+  // the last item of a slice, the dK/dV stores; dk and dv stores of a slice's end: p = 0 waves whose 32 keys are not all past N (the
   // stores sit behind that wave-uniform test, so each one the count includes is issued with
   // at least one active lane)
   const bool any_key = kb * 64 + kh * 32 < N;
@@ -817,7 +779,7 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   for (int i = i_begin; i < i_end; i++) {
     const int64_t sl_row = ((int64_t)b * N + i) * H + h;  // slice-head row index
     const int64_t sbase = L.slice(b, i, h);
-    const int kvc = (i - i_begin) % 3;                     // K/V buffer of this slice
+    const int kvc = (i - i_begin) & 1;                     // K/V buffer of this slice
     const char* Ks = lds + oKV + kvc * kKVB;
     const char* Vs = Ks + 64 * D * 2;
     float mterm = 0.0f;
@@ -830,11 +792,11 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
       // register per buffer and region live across the loop)
       const int cur = cur_rt;
       // wait for item t's loads (issued one item earlier); what follows them in the queue
-      // is the previous item's dq stores and, at a slice start, the dK/dV stores
+      // is, at a slice start, the dK/dV stores
       if (t == 0) wait_vmcnt(0);
-      else wait_vmcnt((t >= 2 ? kDqStores : 0) + (s == 0 ? kvStores : 0));
-      lds_barrier();  // item t is in LDS everywhere, dS^T of item t-1 is complete, the other buffers are free
-      if (s == 0 && i + 1 < i_end) prefetch_kv(i + 1, (i + 1 - i_begin) % 3);
+      else wait_vmcnt(s == 0 ? kvStores : 0);
+      lds_barrier();  // item t is in LDS everywhere, the other buffers are free
+      if (s == 0 && i + 1 < i_end) prefetch_kv(i + 1, (i + 1 - i_begin) & 1);
       {  // the next item: step s+1 of this slice, else step 0 of the next slice
         const bool same = s + 1 < nsteps;
         RowRes rn;
@@ -918,14 +880,6 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
         pb[m2] = pack8(&P[m2 * 8]);
         sb[m2] = pack8(&dS[m2 * 8]);
       }
-      // dS^T (keys x queries) to LDS for the dQ product of the next item: accumulator rows
-      // 8R+4g+0..3 of this lane's key are four consecutive queries
-      char* stw = lds + oST + cur * kSTB + offST;
-#pragma unroll
-      for (int m2 = 0; m2 < 2; m2++) {
-        *(lbf16x4*)(stw + m2 * 32) = __builtin_shufflevector(sb[m2], sb[m2], 0, 1, 2, 3);
-        *(lbf16x4*)(stw + m2 * 32 + 16) = __builtin_shufflevector(sb[m2], sb[m2], 4, 5, 6, 7);
-      }
 #pragma unroll
       for (int m2 = 0; m2 < 2; m2++) {
         const bf16x8 ao = cat8(tr16p((const lbf16*)(qd + 128 * D * 2 + trA + m2 * 16 * D * 2)),
@@ -937,10 +891,6 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
         dkT = mfma32(aq, sb[m2], dkT);
         __builtin_amdgcn_s_setprio(0);
       }
-      if (t >= 1) dq_product(cur ^ 1);
-      prev_sl = sl_row;
-      prev_s = s;
-      prev_kv = kvc;
       cur_rt ^= 1;
       t++;
     };
@@ -1026,10 +976,6 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
       }
     }
   }
-  // the last item's dQ product
-  lds_barrier();
-  dq_product(cur_rt ^ 1);
-
   // write this group's pair-bias gradient partial: dbp[grp][b][h][j][k]
   float* dst = dbp + (((int64_t)grp * B + b) * H + h) * (int64_t)N * N;
 #pragma unroll
@@ -1042,52 +988,158 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   }
 }
 
-// ------------------------------------------------------------------ backward: ordered sums
-// dq = bf16(alpha * sum_kb partial[kb]) with kb ascending, summed in FP32.  The partials are
-// bf16 blocks of 16 queries x D channels per (key block, slice-head row, 16-query tile); inside
-// a block lane t (0..63) of the writing wave owns query t%16 and channels u*16 + 4*(t/16) + 0..3
-// (u < D/16), stored contiguously at (D/4)*2*t bytes.  One thread here handles one (block,
-// lane) slot.  All loads of a thread are issued before the sum (indexes past the last partial
-// re-read it and are not added), so the kernel streams at memory speed instead of paying one
-// latency per term.
-template <int D, bool STRIDED, int kMaxKB>
-__global__ __launch_bounds__(256)
-void reduce_dq_kernel(const unsigned* __restrict__ dqp, bf16* __restrict__ dq, int KB, int N, int H, int nqt,
-                      int64_t nslots, float alpha, TokLayout Lg) {
+// ------------------------------------------------------------------ backward: dQ
+// dq[j] = alpha * sum_k dS[j,k] K[k] for the queries of one slice (b,i,h), with P and dS
+// recomputed from the forward's statistics: P = exp2(c1 S + log2e bias - lse2), dS = P (dP - D).
+// The work-group and its key loop have the forward's shape: 4 waves = 128 queries, wave w owns
+// 32 of them, and 64-key tiles of K and V stream through double-buffered LDS.  S^T = K Q^T
+// (starting from the prepared bias/alpha tile) and dP^T = V dO^T run on 32x32x16 MFMA, each lane
+// holding one query column and 16 keys per 32-key tile, so a query's -lse2 and -D are one
+// register of its lane.  Values constant along one side of a score tile enter the accumulator
+// through one k = 8 product instead of an operation per element: -D of each query column
+// (the bf16 parts of split3_bf16 against ones) starts the dP^T accumulator, and a masked key's
+// row of S^T gets -2^100 (its probabilities underflow to exactly zero).
+// dQ^T (channels x queries) += K^T dS^T is the forward's O^T += V^T P^T
+// with K in place of V and dS in place of P: the score accumulator's layout is already that of
+// the product's B operand, so dS needs no trip through LDS, and the sum over all keys stays in
+// an FP32 accumulator, in key order, rounded once.
+template <int D, bool MASK, bool STRIDED>
+__global__ __launch_bounds__(256, 4)
+void dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+               const bf16* __restrict__ dO, const float* __restrict__ biasF, const uint8_t* __restrict__ mask,
+               const float* __restrict__ LDp, bf16* __restrict__ dq, int B, int N, int H, float alpha, TokLayout Lg) {
   const TokLayout L = tok_layout<STRIDED, D>(Lg, N, H);
-  constexpr int NC = D / 16;
-  constexpr int BLK = 16 * D * 2;  // bytes per block
-  typedef typename std::conditional<NC == 2, bf16x8, bf16x4>::type V;
-  // one wave per 16 x D block: the block, its slice and its rows are wave-uniform
-  const unsigned blk = __builtin_amdgcn_readfirstlane(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6));
-  if ((int64_t)blk * 64 >= nslots) return;
-  const int lane = (int)(threadIdx.x & 63);
-  const unsigned sl = blk / (unsigned)nqt;  // (b*N + i)*H + h
-  const int row = (int)(blk % (unsigned)nqt) * 16 + (lane & 15);
-  if (row >= N) return;
-  const int64_t kb_stride = nslots / 64 * BLK;
-  const char* base = (const char*)dqp + (int64_t)blk * BLK + lane * (int)sizeof(V);
-  V x[kMaxKB];
-#pragma unroll
-  for (int kb = 0; kb < kMaxKB; kb++) x[kb] = __builtin_nontemporal_load((const V*)(base + min(kb, KB - 1) * kb_stride));
-  float acc[4 * NC];
-#pragma unroll
-  for (int e = 0; e < 4 * NC; e++) acc[e] = (float)x[0][e];
-#pragma unroll
-  for (int kb = 1; kb < kMaxKB; kb++)
-    if (kb < KB) {
-#pragma unroll
-      for (int e = 0; e < 4 * NC; e++) acc[e] += (float)x[kb][e];
+  constexpr int KT = 64;        // keys per iteration
+  constexpr int NC = D / 16;    // 16-wide channel chunks
+  constexpr int CPR = D / 8;    // 16-byte chunks per row
+  __shared__ __attribute__((aligned(16))) bf16 Ks_[2][KT * D];
+  __shared__ __attribute__((aligned(16))) bf16 Vs_[2][KT * D];
+  __shared__ __attribute__((aligned(16))) uint8_t Ms_[2][KT];
+
+  const int QT = (N + 127) / 128;
+  const int64_t ntiles = (int64_t)B * H * N * QT;
+  const int64_t tile = xcd_tile(ntiles);
+  if (tile >= ntiles) return;
+  // the forward's tile order: the work-groups on one XCD share one head's bias tiles in its L2
+  const int qt = (int)(tile % QT);
+  int64_t rest = tile / QT;
+  const int i = (int)(rest % N); rest /= N;
+  const int h = (int)(rest % H);
+  const int b = (int)(rest / H);
+
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, g = l >> 5, ln = l & 31;
+  const int64_t sbase = L.slice(b, i, h);
+  const int sT = L.sT;
+  const int j = qt * 128 + w * 32 + ln;  // this lane's query
+  const bool jok = j < N;
+  const int Kp = (int)round_up(N, 64), Jp = (int)round_up(N, 128);
+  const float* btile = biasF + ((int64_t)(b * H + h) * (Jp / 32) + (qt * 4 + w)) * (int64_t)(Kp / 32) * 1024;
+  const float c1 = alpha * kLog2e;
+  const uint8_t* mrow = MASK ? mask + ((int64_t)b * N + i) * N : nullptr;
+
+  const i32x4 rk = raw_rsrc(k + sbase, L.span_bytes(N, D)), rv = raw_rsrc(v + sbase, L.span_bytes(N, D));
+  const unsigned kv_vo = (unsigned)(((tid / CPR) * sT + ((tid % CPR) ^ swz<D>(tid / CPR)) * 8) * 2);
+  auto prefetch = [&](int kt, int buf, float after) {
+    if (w < KT * CPR / 64) {
+      dma16_asm_after(rk, kv_vo, kt * KT * sT * 2, lds_addr(&Ks_[buf][w * 512]), after);
+      dma16_asm_after(rv, kv_vo, kt * KT * sT * 2, lds_addr(&Vs_[buf][w * 512]), after);
     }
-  const unsigned bi = sl / (unsigned)H;
-  bf16* out = dq + L.slice((int)(bi / (unsigned)N), (int)(bi % (unsigned)N), (int)(sl % (unsigned)H)) +
-              (int64_t)row * L.sT + 4 * (lane >> 4);
+  };
+
+  // this lane's query row of Q and dO (B operands of the two score products), -lse2 and -D
+  bf16x8 qf[NC], df[NC];
 #pragma unroll
-  for (int u = 0; u < NC; u++) {
-    bf16x4 r;
+  for (int cc = 0; cc < NC; cc++) {
+    qf[cc] = jok ? *(const bf16x8*)(q + sbase + (int64_t)j * sT + cc * 16 + g * 8) : zero8();
+    df[cc] = jok ? *(const bf16x8*)(dO + sbase + (int64_t)j * sT + cc * 16 + g * 8) : zero8();
+  }
+  const float* ldrow = LDp + (((int64_t)b * N + i) * H + h) * 2 * Jp + (j >> 7) * 256 + (j & 127);
+  const float nl2 = ldrow[0];
+  // B operand of the -D start product (parts at k = 0..2 of this lane's query column; the upper
+  // lane half holds k = 4..7, zero) and its A operand (ones at k = 0..2 in every key row)
+  const u32x2v dB = g == 0 ? split3_bf16(ldrow[128]) : u32x2v{0u, 0u};
+
+  f32x16 acc = {};
+  const int nkt = (N + KT - 1) / KT;
+  if (MASK && tid < KT) Ms_[0][tid] = tid < N ? mrow[tid] : (uint8_t)1;
+  prefetch(0, 0, 0.0f);
+  for (int kt = 0; kt < nkt; kt++) {
+    const int cur = kt & 1;
+    // the next tile's key-mask bytes, loaded ahead of the bias loads (and so covered by the wait
+    // below) and stored right after the barrier, to be read after the next one
+    uint8_t mnext = 1;
+    if (MASK && kt + 1 < nkt && tid < KT && (kt + 1) * KT + tid < N) mnext = mrow[(kt + 1) * KT + tid];
+    // this wave's bias tiles of tile kt: eight 16-byte loads into the score accumulators
+    f32x16 s[2];
 #pragma unroll
-    for (int e = 0; e < 4; e++) r[e] = (bf16)(acc[u * 4 + e] * alpha);
-    *(bf16x4*)(out + u * 16) = r;
+    for (int tt = 0; tt < 2; tt++) {
+#pragma unroll
+      for (int R = 0; R < 4; R++) {
+        const f32x4 bv = *(const f32x4*)(btile + (int64_t)(kt * 2 + tt) * 1024 + ((R * 2 + g) * 32 + ln) * 4);
+        s[tt][R * 4 + 0] = bv[0]; s[tt][R * 4 + 1] = bv[1];
+        s[tt][R * 4 + 2] = bv[2]; s[tt][R * 4 + 3] = bv[3];
+      }
+    }
+    // every load but those eight, among them this wave's part of tile kt, has landed
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    __syncthreads();  // all of tile kt is in LDS; buffer cur^1 is free
+    if (MASK && tid < KT) Ms_[cur ^ 1][tid] = mnext;
+    // the next tile's K and V, issued once the bias loads have landed (an operand of the
+    // statement is one of their values), so that the compiler's waits for them never include it
+    if (kt + 1 < nkt) prefetch(kt + 1, cur ^ 1, s[1][15]);
+    const lbf16* Ks = (const lbf16*)Ks_[cur];
+    const lbf16* Vs = (const lbf16*)Vs_[cur];
+    const int G16 = l >> 4, chalf = G16 & 1;
+
+#pragma unroll
+    for (int tt = 0; tt < 2; tt++) {
+      const int rk_ = tt * 32 + ln;
+      // (made here on every tile: a constant kept from the loop's start would hold its
+      // registers through the whole loop)
+      u32x2v one3;
+      asm volatile("v_mov_b32 %0, 0x3f803f80\n\tv_mov_b32 %1, 0x3f80" : "=v"(one3.x), "=v"(one3.y));
+      if (g != 0) one3 = u32x2v{0u, 0u};
+      f32x16 dp = mfma32k8(one3, dB, f32x16{});
+      if (MASK) {  // A: -2^100 at k = 0 of a masked key's row (this lane's row is key rk_); B: one at k = 0
+        const u32x2v mA = {(g == 0 && !Ms_[cur][rk_]) ? 0xF180u : 0u, 0u};
+        s[tt] = mfma32k8(mA, u32x2v{one3.x & 0xFFFFu, 0u}, s[tt]);
+      }
+#pragma unroll
+      for (int cc = 0; cc < NC; cc++) {
+        const bf16x8 ka = *(const lbf16x8*)(Ks + rk_ * D + ((cc * 2 + g) ^ swz<D>(rk_)) * 8);
+        const bf16x8 va = *(const lbf16x8*)(Vs + rk_ * D + ((cc * 2 + g) ^ swz<D>(rk_)) * 8);
+        s[tt] = mfma32(ka, qf[cc], s[tt]);
+        dp = mfma32(va, df[cc], dp);
+      }
+      float ds[16];
+#pragma unroll
+      for (int r = 0; r < 16; r++) ds[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[tt][r], c1, nl2)) * dp[r];
+      // dQ^T += K^T dS^T; lane group (l/16) selects channel half and key run
+#pragma unroll
+      for (int m2 = 0; m2 < 2; m2++) {
+        const bf16x8 sb = pack8(&ds[m2 * 8]);
+        const int r0 = tt * 32 + m2 * 16 + g * 4;
+        bf16x8 a;
+        if (D == 32 || chalf == 0) {
+          const int c0 = D == 32 ? chalf * 16 : 0;
+          a = cat8(tr16p(Ks + tr_off<D>(l, r0, c0)), tr16p(Ks + tr_off<D>(l, r0 + 8, c0)));
+        } else {
+          a = zero8();
+        }
+        acc = mfma32(a, sb, acc);
+      }
+    }
+  }
+
+  if (jok) {
+    bf16* drow = dq + sbase + (int64_t)j * sT;
+#pragma unroll
+    for (int R = 0; R < D / 8; R++) {
+      bf16x4 ob;
+#pragma unroll
+      for (int e = 0; e < 4; e++) ob[e] = (bf16)(acc[R * 4 + e] * alpha);
+      *(bf16x4*)(drow + R * 8 + g * 4) = ob;
+    }
   }
 }
 
@@ -1158,7 +1210,7 @@ struct Plan {
   int64_t bias_b16_bytes;   // prepared backward bias (bf16 column blocks)
   int64_t nst, nqc;          // 128-query steps per slice; query chunks of the backward
   int64_t cs, n1;            // steps of the longest chunks, and how many chunks have cs steps
-  int64_t off_LD, off_dqp, off_dbp, off_dkv, bwd_bytes;
+  int64_t off_LD, off_bF, off_dbp, off_dkv, bwd_bytes;
 };
 
 constexpr int64_t kAlign = 256;
@@ -1209,9 +1261,11 @@ Plan make_plan(int64_t B, int64_t N, int64_t H, int64_t D) {
   p.rows = B * N * H * N;
   p.bias_f32_bytes = round_up(B * H * p.Kp * p.Jp * 4, kAlign);
   p.bias_b16_bytes = round_up(B * H * p.Kp * p.Jp * 2, kAlign);
+  // backward workspace: fp16 bias column blocks | -lse2, -D rows | FP32 bias/alpha tiles (the dQ
+  // kernel's, as the forward's) | pair-bias gradient partials | chunked dK / dV partials
   p.off_LD = p.bias_b16_bytes;
-  p.off_dqp = p.off_LD + round_up(B * N * H * p.Jp * 2 * 4, kAlign);
-  p.off_dbp = p.off_dqp + round_up(p.KB * B * N * H * p.Jp * D * 2, kAlign);
+  p.off_bF = p.off_LD + round_up(B * N * H * p.Jp * 2 * 4, kAlign);
+  p.off_dbp = p.off_bF + p.bias_f32_bytes;
   p.off_dkv = p.off_dbp + round_up(p.ngroups * B * H * N * N * 4, kAlign);
   // FP32 dK / dV partials per query chunk, only when there is more than one chunk
   p.bwd_bytes = p.off_dkv + (p.nqc > 1 ? round_up(2 * p.nqc * p.elems * 4, kAlign) : 0);
@@ -1287,12 +1341,14 @@ tri_attn_status launch_bwd(unsigned stages, const Plan& P, const TokLayout& L, c
   char* base = (char*)ws;
   bf16* biasB = (bf16*)base;
   float* LDg = (float*)(base + P.off_LD);
-  unsigned* dqp = (unsigned*)(base + P.off_dqp);
+  float* biasF = (float*)(base + P.off_bF);
   float* dbp = (float*)(base + P.off_dbp);
   const int64_t nb = P.B * P.H * P.Kp * P.Jp;
   if (stages & TRI_ATTN_STAGE_PREP) {
     hipLaunchKernelGGL(bias_prep_bwd_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, st,
                        (const bf16*)bias, (_Float16*)biasB, (int)P.N, (int)P.KB, (int)(P.Jp / 128), nb);
+    hipLaunchKernelGGL(bias_prep_fwd_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, st,
+                       (const bf16*)bias, biasF, (int)P.N, (int)P.Jp, (int)P.Kp, 1.0f / alpha, nb);
     const int64_t nrows = P.B * P.N * P.H;
     hipLaunchKernelGGL((bwd_pre_kernel<D, STRIDED>), dim3((unsigned)(nrows * P.Jp * (D / 8) / 256)), dim3(256), 0, st,
                        (const bf16*)dO, (const bf16*)o, (const bf16*)res, lse, LDg, (int)P.N, (int)P.H,
@@ -1308,11 +1364,11 @@ tri_attn_status launch_bwd(unsigned stages, const Plan& P, const TokLayout& L, c
       const dim3 grid(grid_xcd(per_chunk * ncl));
       if (mask)
         hipLaunchKernelGGL((bwd_kernel<D, true, NS, STRIDED, CH>), grid, dim3(512), 0, st, (const bf16*)q,
-                           (const bf16*)k, (const bf16*)v, (const bf16*)dO, biasB, mask, LDg, dqp, dbp, (bf16*)dk,
+                           (const bf16*)k, (const bf16*)v, (const bf16*)dO, biasB, mask, LDg, dbp, (bf16*)dk,
                            (bf16*)dv, (int)P.B, (int)P.N, (int)P.H, (int)P.G, (int)P.ngroups, alpha, L, ck);
       else
         hipLaunchKernelGGL((bwd_kernel<D, false, NS, STRIDED, CH>), grid, dim3(512), 0, st, (const bf16*)q,
-                           (const bf16*)k, (const bf16*)v, (const bf16*)dO, biasB, mask, LDg, dqp, dbp, (bf16*)dk,
+                           (const bf16*)k, (const bf16*)v, (const bf16*)dO, biasB, mask, LDg, dbp, (bf16*)dk,
                            (bf16*)dv, (int)P.B, (int)P.N, (int)P.H, (int)P.G, (int)P.ngroups, alpha, L, ck);
     };
     auto by_steps = [&](int ns, auto chunked_, int c_begin, int ncl, int step0) {
@@ -1334,20 +1390,15 @@ tri_attn_status launch_bwd(unsigned stages, const Plan& P, const TokLayout& L, c
     }
   }
   if (stages & TRI_ATTN_STAGE_FINAL) {
-    const int64_t nslots = P.B * P.N * P.H * (P.Jp / 16) * 64;
-    const dim3 gq((unsigned)((nslots + 255) / 256));
-    // the instance that loads no more partials per slot than there are key blocks, rounded up
-    // to 12 (N <= 768), 16 (N <= 1024), 24 (N <= 1536) or 32
-    auto reduce_dq = [&](auto kmax_) {
-      constexpr int KM = decltype(kmax_)::value;
-      hipLaunchKernelGGL((reduce_dq_kernel<D, STRIDED, KM>), gq, dim3(256), 0, st, dqp, (bf16*)dq, (int)P.KB,
-                         (int)P.N, (int)P.H, (int)(P.Jp / 16), nslots, alpha, L);
-    };
-    static_assert(TRI_ATTN_MAX_N / 64 == 32, "largest reduce_dq_kernel instance");
-    if (P.KB <= 12) reduce_dq(std::integral_constant<int, 12>{});
-    else if (P.KB <= 16) reduce_dq(std::integral_constant<int, 16>{});
-    else if (P.KB <= 24) reduce_dq(std::integral_constant<int, 24>{});
-    else reduce_dq(std::integral_constant<int, 32>{});
+    const int64_t qtiles = P.B * P.H * P.N * ((P.N + 127) / 128);
+    if (mask)
+      hipLaunchKernelGGL((dq_kernel<D, true, STRIDED>), dim3(grid_xcd(qtiles)), dim3(256), 0, st, (const bf16*)q,
+                         (const bf16*)k, (const bf16*)v, (const bf16*)dO, biasF, mask, LDg, (bf16*)dq, (int)P.B,
+                         (int)P.N, (int)P.H, alpha, L);
+    else
+      hipLaunchKernelGGL((dq_kernel<D, false, STRIDED>), dim3(grid_xcd(qtiles)), dim3(256), 0, st, (const bf16*)q,
+                         (const bf16*)k, (const bf16*)v, (const bf16*)dO, biasF, mask, LDg, (bf16*)dq, (int)P.B,
+                         (int)P.N, (int)P.H, alpha, L);
     const int64_t nbias = P.B * P.H * P.N * P.N;
     if (nbias % 4 == 0)
       hipLaunchKernelGGL(reduce_dbias_kernel<true>, dim3((unsigned)((nbias / 4 + 255) / 256)), dim3(256), 0, st, dbp,
