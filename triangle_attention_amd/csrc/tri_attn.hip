@@ -636,15 +636,14 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   constexpr int NC = D / 16;
   constexpr int CPR = D / 8;    // 16-byte chunks per row
   constexpr int NR = D / 2;     // accumulator registers of dK^T / dV^T holding channels c < D
-  // LDS map (bytes): pair-bias tiles x2 | Q,dO x2 | K,V,mask x2 | lse2,-D x2 | dK/dV reduction
-  // (the odd query lanes' partials)
-  constexpr int kBiasB = 8 * 2048;                  // 8 waves x one 32x32 bf16 tile
-  constexpr int kQDB = 2 * 128 * D * 2;             // Q rows then dO rows
+  // LDS map (bytes): per wave, two item buffers of [its 32 Q rows | its 32 dO rows | its 32x32
+  // pair-bias tile | its 32 lse2 values, 32 -D values] | K,V,mask x2 | dK/dV reduction (the odd
+  // query lanes' partials)
+  constexpr int kWQ = 32 * D * 2;                   // 32 rows of Q (or dO)
+  constexpr int kWB = 2 * kWQ + 2048 + 256;         // one item buffer of one wave
   constexpr int kKVB = 2 * 64 * D * 2 + 64 * 4;     // K rows, V rows, 64 mask bytes (one per dword)
-  constexpr int kLDB = 2 * 128 * 4;                 // lse2 rows then -D rows
   constexpr int kREDB = 4 * 2 * NR * 64 * 4;        // dK^T, dV^T partials of four waves
-  constexpr int oBias = 0, oQD = oBias + 2 * kBiasB, oKV = oQD + 2 * kQDB, oLD = oKV + 2 * kKVB;
-  constexpr int oRED = oLD + 2 * kLDB, kLdsBytes = oRED + kREDB;
+  constexpr int oKV = 8 * 2 * kWB, oRED = oKV + 2 * kKVB, kLdsBytes = oRED + kREDB;
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
   __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
 
@@ -692,27 +691,30 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   const int sT = L.sT;
   const int span = L.span_bytes(N, D);                                   // bytes of a slice-head's rows
 
-  // Per-lane byte offset of the streamed Q and dO loads, fixed for the whole work-group; slice
-  // and step enter through the buffer base and the scalar offset.  Q, dO, K and V land swizzled.
-  const unsigned qd_vo = (unsigned)(((tid / CPR) * sT + ((tid % CPR) ^ swz<D>(tid / CPR)) * 8) * 2);
+  // Per-lane byte offsets of the streamed loads of a wave's item, fixed for the whole work-group
+  // (slice and step enter through the buffer base and the scalar offset): Q and dO rows p*32 + l/CPR
+  // (+16 per further load at D = 32), which land swizzled like K and V; the lse2 (lanes 0-7) and
+  // -D (lanes 8-15) values of the wave's 32 queries.
+  const unsigned qd_vo = (unsigned)(((p * 32 + l / CPR) * sT + ((l % CPR) ^ swz<D>(l / CPR)) * 8) * 2);
+  const unsigned ld_vo = (unsigned)((l < 8 ? p * 32 + 4 * l : 128 + p * 32 + 4 * (l - 8)) * 4);
   const bf16* bias_blk = biasB + (((int64_t)(b * H + h) * KB + kb) * NSt + s_base) * (int64_t)8192;
 
   // Per-lane LDS byte offsets of the operand reads; the buffer and the step enter as uniform
   // additions or immediate offsets.
-  //  * row reads (A/B operands of the 32x32x16 products): row rr = (p or kh)*32 + ln, chunk
-  //    cc*2+g in swizzled position; the swizzle of such a row depends on ln only
-  //  * transposed reads of dO/Q (dV^T, dK^T A operands) over query rows p*32 + m2*16 + 4g (+8)
+  //  * row reads (A/B operands of the 32x32x16 products): row ln of the wave's Q / dO rows or row
+  //    kh*32 + ln of K / V, chunk cc*2+g in swizzled position; the swizzle depends on ln only
+  //  * transposed reads of dO/Q (dV^T, dK^T A operands) over the wave's rows m2*16 + 4g (+8)
   const int swl = swz<D>(ln);
   unsigned offR[NC];
 #pragma unroll
   for (int cc = 0; cc < NC; cc++) offR[cc] = (unsigned)((ln * D + (((cc * 2 + g) ^ swl) * 8)) * 2);
-  const unsigned offQ = (unsigned)(p * 32 * D * 2), offK = (unsigned)(kh * 32 * D * 2);
+  const unsigned offK = (unsigned)(kh * 32 * D * 2);
   const int G16 = l >> 4, chalf = G16 & 1;
   const int c0 = D == 32 ? 16 * chalf : 0;
-  const unsigned trA = (unsigned)((tr_off<D>(l, 4 * g, c0) + p * 32 * D) * 2);
-  const unsigned trB = (unsigned)((tr_off<D>(l, 4 * g + 8, c0) + p * 32 * D) * 2);
-  const unsigned offBias = (unsigned)((kh * 4 + p) * 2048 + l * 16);
-  const unsigned offRow = (unsigned)((p * 32 + g * 4) * 4);  // lse2 / -D rows of this lane
+  const unsigned trA = (unsigned)(tr_off<D>(l, 4 * g, c0) * 2);
+  const unsigned trB = (unsigned)(tr_off<D>(l, 4 * g + 8, c0) * 2);
+  const unsigned offBias = (unsigned)(2 * kWQ + l * 16);
+  const unsigned offRow = (unsigned)(2 * kWQ + 2048 + g * 4 * 4);  // lse2 / -D values of this lane's rows
 
   // issue the loads of work item (ii, ss) into LDS buffer `buf`; rows past N read as zeros
   // LDS byte address of the work-group's LDS block; the streamed loads take LDS addresses
@@ -731,17 +733,21 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
     r.ld = raw_rsrc(LDp + sl * 2 * Jpt, Jpt * 8);
     return r;
   };
-  // issue the loads of work item (slice with row descriptors rr, step ss) into LDS buffer `buf`
+  // issue the loads of this wave's part of work item (slice with row descriptors rr, step ss)
+  // into its item buffer `buf`: everything a wave reads during an item but K and V comes from its
+  // own loads, so that between the first items of two slices no wave waits for another
   auto prefetch = [&](const RowRes& rr, int ss, int buf) {
-    static_assert(2 * CPR <= 8, "Q/dO rows of a step in one load per wave");
-    if (w < 2 * CPR) {
-      dma16_asm(rr.q, qd_vo, (s_base + ss) * 128 * sT * 2, lds0 + oQD + buf * kQDB + w * 1024);
-      dma16_asm(rr.dO, qd_vo, (s_base + ss) * 128 * sT * 2, lds0 + oQD + buf * kQDB + 128 * D * 2 + w * 1024);
+    const unsigned dst = lds0 + (unsigned)((w * 2 + buf) * kWB);
+    const int so = (s_base + ss) * 128 * sT * 2;
+#pragma unroll
+    for (int m = 0; m < CPR / 2; m++) {  // 64 lanes x 16 bytes: 16 rows (D = 32) or 32 rows (D = 16)
+      dma16_asm(rr.q, qd_vo, so + m * 16 * sT * 2, dst + m * 1024);
+      dma16_asm(rr.dO, qd_vo, so + m * 16 * sT * 2, dst + kWQ + m * 1024);
     }
-    if (w == 0) dma16_asm(rr.ld, (unsigned)l * 16u, (s_base + ss) * 1024, lds0 + oLD + buf * kLDB);
-    // this step's pair-bias tiles: 16 KiB, 2 KiB per wave
-    dma16_asm(rbias, (unsigned)l * 16u, ss * 16384 + w * 2048, lds0 + oBias + buf * kBiasB + w * 2048);
-    dma16_asm(rbias, (unsigned)l * 16u, ss * 16384 + w * 2048 + 1024, lds0 + oBias + buf * kBiasB + w * 2048 + 1024);
+    // this wave's 32x32 pair-bias tile of the step (2 KiB)
+    dma16_asm(rbias, (unsigned)l * 16u, ss * 16384 + (kh * 4 + p) * 2048, dst + 2 * kWQ);
+    dma16_asm(rbias, (unsigned)l * 16u, ss * 16384 + (kh * 4 + p) * 2048 + 1024, dst + 2 * kWQ + 1024);
+    if (l < 16) dma16_asm(rr.ld, ld_vo, (s_base + ss) * 1024, dst + 2 * kWQ + 2048);
   };
   // K, V and the key-mask bytes of slice ii into K/V buffer kvb
   auto prefetch_kv = [&](int ii, int kvb) {
@@ -791,11 +797,13 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
       // (a run-time value: with constant buffer offsets the compiler would keep a base
       // register per buffer and region live across the loop)
       const int cur = cur_rt;
-      // wait for item t's loads (issued one item earlier); what follows them in the queue
-      // is, at a slice start, the dK/dV stores
+      // wait for this wave's loads of item t (issued one item earlier); what follows them in the
+      // queue is, at a slice start, the dK/dV stores
       if (t == 0) wait_vmcnt(0);
       else wait_vmcnt(s == 0 ? kvStores : 0);
-      lds_barrier();  // item t is in LDS everywhere, the other buffers are free
+      // at a slice start: the slice's K, V and mask bytes (loaded by all waves during the previous
+      // slice) are in LDS everywhere, and no wave reads the previous slice's K/V buffer any more
+      if (s == 0) lds_barrier();
       if (s == 0 && i + 1 < i_end) prefetch_kv(i + 1, (i + 1 - i_begin) & 1);
       {  // the next item: step s+1 of this slice, else step 0 of the next slice
         const bool same = s + 1 < nsteps;
@@ -810,8 +818,8 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
         mterm = (kok && (mb & 0xFFu) == 0) ? -INFINITY : 0.0f;
       }
 
-      const char* qd = lds + oQD + cur * kQDB;   // this item's Q rows, then its dO rows
-      const char* ld = lds + oLD + cur * kLDB + offRow;
+      const char* qd = lds + (w * 2 + cur) * kWB;  // this wave's item buffer: Q rows, dO rows, ...
+      const char* ld = qd + offRow;
 
       // S = Q K^T (rows: 32 queries, cols: 32 keys) and dP - D = dO V^T - D, the second
       // accumulator starting from -D
@@ -821,14 +829,14 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
       bf16x8 aq[NC], kf[NC], ao[NC], vf[NC];
 #pragma unroll
       for (int cc = 0; cc < NC; cc++) {
-        aq[cc] = *(const lbf16x8*)(qd + offQ + offR[cc]);
+        aq[cc] = *(const lbf16x8*)(qd + offR[cc]);
         kf[cc] = *(const lbf16x8*)(Ks + offK + offR[cc]);
-        ao[cc] = *(const lbf16x8*)(qd + 128 * D * 2 + offQ + offR[cc]);
+        ao[cc] = *(const lbf16x8*)(qd + kWQ + offR[cc]);
         vf[cc] = *(const lbf16x8*)(Vs + offK + offR[cc]);
       }
 #pragma unroll
       for (int R = 0; R < 4; R++) {
-        const f32x4 x = *(const lf32x4*)(ld + 512 + R * 32);
+        const f32x4 x = *(const lf32x4*)(ld + 128 + R * 32);
 #pragma unroll
         for (int e = 0; e < 4; e++) dp[R * 4 + e] = x[e];
       }
@@ -845,7 +853,7 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
       // P = exp2(c1 S + log2e bias - lse2) and dS = P (dP - D); dS is summed into the face.
       // The bias term log2e * bias - lse2 comes from one v_fma_mix_f32 per element (fp16
       // bias pairs, -lse2 rows), independent of the products above.
-      const char* bS = lds + oBias + cur * kBiasB + offBias;
+      const char* bS = qd + offBias;
       const u32x4v b0 = *(const lu32x4*)bS, b1 = *(const lu32x4*)(bS + 1024);
       // at D = 16 the four lse2 rows are read at once, while the products run; at D = 32 the
       // registers for that are not free, and each row is read just before its use
@@ -882,8 +890,8 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
       }
 #pragma unroll
       for (int m2 = 0; m2 < 2; m2++) {
-        const bf16x8 ao = cat8(tr16p((const lbf16*)(qd + 128 * D * 2 + trA + m2 * 16 * D * 2)),
-                               tr16p((const lbf16*)(qd + 128 * D * 2 + trB + m2 * 16 * D * 2)));
+        const bf16x8 ao = cat8(tr16p((const lbf16*)(qd + kWQ + trA + m2 * 16 * D * 2)),
+                               tr16p((const lbf16*)(qd + kWQ + trB + m2 * 16 * D * 2)));
         const bf16x8 aq = cat8(tr16p((const lbf16*)(qd + trA + m2 * 16 * D * 2)),
                                tr16p((const lbf16*)(qd + trB + m2 * 16 * D * 2)));
         __builtin_amdgcn_s_setprio(1);
