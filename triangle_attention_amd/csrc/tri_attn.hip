@@ -400,8 +400,10 @@ void fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   const int nkt = (N + KT - 1) / KT;
   if (MASK && tid < KT) Ms_[0][tid] = tid < N ? mrow[tid] : (uint8_t)1;
   prefetch(0, 0, 0.0f);
-  for (int kt = 0; kt < nkt; kt++) {
-    const int cur = kt & 1;
+  // Key tile kt in LDS buffer CUR.  The buffer index is a compile-time constant (the loop below
+  // runs two tiles per pass), so every LDS address is a per-lane offset plus an immediate.
+  auto key_tile = [&](int kt, auto cur_) {
+    constexpr int cur = decltype(cur_)::value;
     // this wave's bias tiles of tile kt: eight 16-byte loads into the score accumulators
     f32x16 s[2];
 #pragma unroll
@@ -431,12 +433,12 @@ void fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
         s[tt] = mfma32(a, qf[cc], s[tt]);
       }
       if (MASK) {
-#pragma unroll
-        for (int R = 0; R < 4; R++) {
-#pragma unroll
-          for (int e = 0; e < 4; e++)
-            if (!Ms_[cur][tt * 32 + R * 8 + g * 4 + e]) s[tt][R * 4 + e] = -INFINITY;
-        }
+        // a masked key's row of S^T gets -2^100 through one k = 8 product (A: -2^100 at k = 0 of
+        // the lane's key row rk_, B: one at k = 0; a kept key's row gets an exact 0): once a kept
+        // key has set the reference its probability is exactly zero, and a row whose maximum stays
+        // below -2^99 has no kept key (epilogue)
+        const u32x2v mA = {(g == 0 && !Ms_[cur][rk_]) ? 0xF180u : 0u, 0u};
+        s[tt] = mfma32k8(mA, u32x2v{g == 0 ? 0x3F80u : 0u, 0u}, s[tt]);
       }
     }
     // running max over this lane's 32 scores, then across the lane pair (l, l^32)
@@ -475,6 +477,8 @@ void fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
     l_run += lsum;
 
     // O^T (channels x queries) += V^T P^T; lane group (l/16) selects channel half and key run
+    // (at D = 16 both halves read channels 0..15: the upper 16 rows of the product repeat the
+    // lower ones and are never stored)
     const int G16 = l >> 4, chalf = G16 & 1;
 #pragma unroll
     for (int tt = 0; tt < 2; tt++)
@@ -482,23 +486,23 @@ void fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
       for (int m2 = 0; m2 < 2; m2++) {
         const bf16x8 pb = pack8(&p[tt][m2 * 8]);
         const int r0 = tt * 32 + m2 * 16 + g * 4;
-        bf16x8 a;
-        if (D == 32 || chalf == 0) {
-          const int c0 = D == 32 ? chalf * 16 : 0;
-          a = cat8(tr16p(Vs + tr_off<D>(l, r0, c0)), tr16p(Vs + tr_off<D>(l, r0 + 8, c0)));
-        } else {
-          a = zero8();
-        }
+        const int c0 = D == 32 ? chalf * 16 : 0;
+        const bf16x8 a = cat8(tr16p(Vs + tr_off<D>(l, r0, c0)), tr16p(Vs + tr_off<D>(l, r0 + 8, c0)));
         acc_o = mfma32(a, pb, acc_o);
       }
     if (MASK && tid < KT) Ms_[cur ^ 1][tid] = mnext;  // read after the next barrier
+  };
+  for (int kt = 0; kt < nkt; kt += 2) {
+    key_tile(kt, std::integral_constant<int, 0>{});
+    if (kt + 1 < nkt) key_tile(kt + 1, std::integral_constant<int, 1>{});
   }
 
   // epilogue: normalise, round, residual, logsumexp.  A query with no key of finite score (every
   // key masked, or every key's bias -inf) attends to nothing: o = 0, residual 0, lse = +inf, which
-  // gives every one of its probabilities in the backward exp(s - lse) = 0.
+  // gives every one of its probabilities in the backward exp(s - lse) = 0.  (With every key masked
+  // the reference maximum is about -2^100, far below any score of a kept key.)
   const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const bool empty = !(l_tot > 0.0f);
+  const bool empty = !(l_tot > 0.0f) || (MASK && !(m_run > -0x1p99f));
   const float inv = empty ? 0.0f : 1.0f / l_tot;
   if (jok) {
     bf16* orow = o + sbase + (int64_t)j * sT;
@@ -1069,10 +1073,14 @@ void dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
 
   f32x16 acc = {};
   const int nkt = (N + KT - 1) / KT;
-  if (MASK && tid < KT) Ms_[0][tid] = tid < N ? mrow[tid] : (uint8_t)1;
-  prefetch(0, 0, 0.0f);
-  for (int kt = 0; kt < nkt; kt++) {
-    const int cur = kt & 1;
+  const int G16 = l >> 4, chalf = G16 & 1;
+  // A operand of the -D start product: ones at k = 0..2 in every key row (lanes of the upper k
+  // half hold k = 4..7, zero)
+  const u32x2v one3 = g == 0 ? u32x2v{0x3F803F80u, 0x3F80u} : u32x2v{0u, 0u};
+  // Key tile kt in LDS buffer CUR.  The buffer index is a compile-time constant (the loop below
+  // runs two tiles per pass), so every LDS address is a per-lane offset plus an immediate.
+  auto key_tile = [&](int kt, auto cur_) {
+    constexpr int cur = decltype(cur_)::value;
     // the next tile's key-mask bytes, loaded ahead of the bias loads (and so covered by the wait
     // below) and stored right after the barrier, to be read after the next one
     uint8_t mnext = 1;
@@ -1097,46 +1105,44 @@ void dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
     if (kt + 1 < nkt) prefetch(kt + 1, cur ^ 1, s[1][15]);
     const lbf16* Ks = (const lbf16*)Ks_[cur];
     const lbf16* Vs = (const lbf16*)Vs_[cur];
-    const int G16 = l >> 4, chalf = G16 & 1;
 
 #pragma unroll
     for (int tt = 0; tt < 2; tt++) {
       const int rk_ = tt * 32 + ln;
-      // (made here on every tile: a constant kept from the loop's start would hold its
-      // registers through the whole loop)
-      u32x2v one3;
-      asm volatile("v_mov_b32 %0, 0x3f803f80\n\tv_mov_b32 %1, 0x3f80" : "=v"(one3.x), "=v"(one3.y));
-      if (g != 0) one3 = u32x2v{0u, 0u};
-      f32x16 dp = mfma32k8(one3, dB, f32x16{});
-      if (MASK) {  // A: -2^100 at k = 0 of a masked key's row (this lane's row is key rk_); B: one at k = 0
-        const u32x2v mA = {(g == 0 && !Ms_[cur][rk_]) ? 0xF180u : 0u, 0u};
-        s[tt] = mfma32k8(mA, u32x2v{one3.x & 0xFFFFu, 0u}, s[tt]);
-      }
+      f32x16 dp;
 #pragma unroll
       for (int cc = 0; cc < NC; cc++) {
         const bf16x8 ka = *(const lbf16x8*)(Ks + rk_ * D + ((cc * 2 + g) ^ swz<D>(rk_)) * 8);
         const bf16x8 va = *(const lbf16x8*)(Vs + rk_ * D + ((cc * 2 + g) ^ swz<D>(rk_)) * 8);
         s[tt] = mfma32(ka, qf[cc], s[tt]);
-        dp = mfma32(va, df[cc], dp);
+        dp = mfma32(va, df[cc], cc == 0 ? f32x16{} : dp);
+        if (cc == 0) dp = mfma32k8(one3, dB, dp);  // dP - D
+      }
+      if (MASK) {  // A: -2^100 at k = 0 of a masked key's row (this lane's row is key rk_); B: one at k = 0
+        const u32x2v mA = {(g == 0 && !Ms_[cur][rk_]) ? 0xF180u : 0u, 0u};
+        s[tt] = mfma32k8(mA, u32x2v{one3.x & 0xFFFFu, 0u}, s[tt]);
       }
       float ds[16];
 #pragma unroll
       for (int r = 0; r < 16; r++) ds[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[tt][r], c1, nl2)) * dp[r];
-      // dQ^T += K^T dS^T; lane group (l/16) selects channel half and key run
+      // dQ^T += K^T dS^T; lane group (l/16) selects channel half and key run (at D = 16 both
+      // halves read channels 0..15: the upper 16 rows of the product repeat the lower ones and
+      // are never stored)
 #pragma unroll
       for (int m2 = 0; m2 < 2; m2++) {
         const bf16x8 sb = pack8(&ds[m2 * 8]);
         const int r0 = tt * 32 + m2 * 16 + g * 4;
-        bf16x8 a;
-        if (D == 32 || chalf == 0) {
-          const int c0 = D == 32 ? chalf * 16 : 0;
-          a = cat8(tr16p(Ks + tr_off<D>(l, r0, c0)), tr16p(Ks + tr_off<D>(l, r0 + 8, c0)));
-        } else {
-          a = zero8();
-        }
+        const int c0 = D == 32 ? chalf * 16 : 0;
+        const bf16x8 a = cat8(tr16p(Ks + tr_off<D>(l, r0, c0)), tr16p(Ks + tr_off<D>(l, r0 + 8, c0)));
         acc = mfma32(a, sb, acc);
       }
     }
+  };
+  if (MASK && tid < KT) Ms_[0][tid] = tid < N ? mrow[tid] : (uint8_t)1;
+  prefetch(0, 0, 0.0f);
+  for (int kt = 0; kt < nkt; kt += 2) {
+    key_tile(kt, std::integral_constant<int, 0>{});
+    if (kt + 1 < nkt) key_tile(kt + 1, std::integral_constant<int, 1>{});
   }
 
   if (jok) {
