@@ -1,8 +1,8 @@
 """Benchmark: triangle attention forward + backward on one MI355X.
 
 One step is the whole hot path on one batch of resident synthetic input: the forward
-(bias conversion + attention kernel) and the backward (bias conversion + correction D, the
-key-tile-parallel kernel for dk, dv and the dbias partials, the query-tile dq kernel and the
+(bias conversion + attention kernel) and the backward (bias conversion, the query-tile kernel
+for dq and the correction D, the key-tile-parallel kernel for dk, dv and the dbias partials, the
 ordered sum of the dbias partials).  W untimed warm-up steps, then exactly K timed steps
 bracketed by torch.cuda.synchronize().
 

@@ -44,7 +44,8 @@
  *   - Every floating-point reduction runs in a fixed order that depends only on the
  *     shape, with no floating-point atomics: repeated calls with the same inputs and
  *     shape on the same device return bitwise-identical outputs.
- *   - Inputs (q, k, v, dO) are finite.
+ *   - Inputs (q, k, v, dO) are finite, and every score alpha*q.k + bias of a kept key stays
+ *     within +-2^99 (the kernels mark masked keys with -2^100 internally).
  */
 #ifndef TRI_ATTN_H
 #define TRI_ATTN_H
@@ -135,9 +136,9 @@ tri_attn_status tri_attn_bwd(int64_t B, int64_t N, int64_t H, int64_t D,
  * arguments and the same workspace; the workspace carries intermediate results from one
  * stage to the next.  Validation is the same as for the unstaged call.
  *   forward : PREP = bias conversion into the workspace; MAIN = attention kernel; FINAL = none
- *   backward: PREP = bias conversion and the correction D; MAIN = the key-tile-parallel kernel
- *             (dk, dv, dbias partials); FINAL = the query-tile dq kernel and the ordered sums
- *             of the dbias partials
+ *   backward: PREP = bias conversion and the query-tile kernel (dq, and the correction D for
+ *             the next stage); MAIN = the key-tile-parallel kernel (dk, dv, dbias partials);
+ *             FINAL = the ordered sum of the dbias partials
  */
 #define TRI_ATTN_STAGE_PREP 1u
 #define TRI_ATTN_STAGE_MAIN 2u

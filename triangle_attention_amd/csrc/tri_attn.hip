@@ -525,49 +525,6 @@ void fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   }
 }
 
-// D[b,i,h,j] = sum_c dO * (o + residual) in FP32 (or dO * o without a residual), written
-// negated (the main kernel starts its dO V^T accumulator from -D), with
-// -lse2 = -lse * log2(e).  Layout: per slice-head row, per 128-query step, 128 values of
-// -lse2 then 128 of -D (zero padding past N): one KiB per step, the block the main kernel
-// streams into LDS with one load per lane.  D/8 adjacent lanes share a row (16 bytes
-// each, so a wave reads contiguous memory); their partial sums combine in a fixed order.
-template <int D, bool STRIDED>
-__global__ __launch_bounds__(256)
-void bwd_pre_kernel(const bf16* __restrict__ dO, const bf16* __restrict__ o, const bf16* __restrict__ res,
-                    const float* __restrict__ lse, float* __restrict__ LDp, int N, int H, int Jp, TokLayout Lg) {
-  const TokLayout L = tok_layout<STRIDED, D>(Lg, N, H);
-  constexpr int LPR = D / 8;  // lanes per row
-  // The grid covers the B*N*H slice-head rows, Jp * LPR threads each (a multiple of 256), so
-  // each work-group lies within one row: the row and its slice are work-group uniform.
-  const unsigned bpr = (unsigned)(Jp * LPR / 256);
-  const unsigned row = blockIdx.x / bpr;  // (b*N + i)*H + h
-  const int local = (int)(blockIdx.x % bpr) * 256 + (int)threadIdx.x;
-  const int j = local / LPR, part = local % LPR;
-  float acc = 0.0f;
-  if (j < N) {
-    const unsigned bi = row / (unsigned)H;
-    const int64_t off = L.slice((int)(bi / (unsigned)N), (int)(bi % (unsigned)N), (int)(row % (unsigned)H)) +
-                        (int64_t)j * L.sT + part * 8;
-    const bf16x8 a = *(const bf16x8*)(dO + off);
-    const bf16x8 ov = ld_nt((const bf16x8*)(o + off));
-    if (res) {
-      const bf16x8 rv = ld_nt((const bf16x8*)(res + off));
-#pragma unroll
-      for (int e = 0; e < 8; e++) acc = __builtin_fmaf((float)a[e], (float)ov[e] + (float)rv[e], acc);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; e++) acc = __builtin_fmaf((float)a[e], (float)ov[e], acc);
-    }
-  }
-  acc += __shfl_xor(acc, 1);
-  if (LPR == 4) acc += __shfl_xor(acc, 2);
-  if (part == 0) {
-    float* dst = LDp + (int64_t)row * 2 * Jp + (j >> 7) * 256 + (j & 127);
-    dst[0] = j < N ? -lse[(int64_t)row * N + j] * kLog2e : 0.0f;
-    dst[128] = -acc;
-  }
-}
-
 // ------------------------------------------------------------------ backward: main
 // One work-group = 8 waves = one block of 64 keys of head h, for a group of G slices.
 // wave w: key half kh = w&1 (32 keys), query lane p = w>>1.  The work items are
@@ -1000,9 +957,12 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   }
 }
 
-// ------------------------------------------------------------------ backward: dQ
+// ------------------------------------------------------------------ backward: dQ and D
 // dq[j] = alpha * sum_k dS[j,k] K[k] for the queries of one slice (b,i,h), with P and dS
 // recomputed from the forward's statistics: P = exp2(c1 S + log2e bias - lse2), dS = P (dP - D).
+// This kernel runs first in the backward and also forms the correction D[j] = sum_c dO (o + r)
+// of its queries, writing the row statistics the key-tile kernel streams: per slice-head row
+// and 128-query step, 128 values of -lse2 = -lse log2(e), then 128 of -D (zero past N).
 // The work-group and its key loop have the forward's shape: 4 waves = 128 queries, wave w owns
 // 32 of them, and 64-key tiles of K and V stream through double-buffered LDS.  S^T = K Q^T
 // (starting from the prepared bias/alpha tile) and dP^T = V dO^T run on 32x32x16 MFMA, each lane
@@ -1019,7 +979,8 @@ template <int D, bool MASK, bool STRIDED>
 __global__ __launch_bounds__(256, 4)
 void dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
                const bf16* __restrict__ dO, const float* __restrict__ biasF, const uint8_t* __restrict__ mask,
-               const float* __restrict__ LDp, bf16* __restrict__ dq, int B, int N, int H, float alpha, TokLayout Lg) {
+               const bf16* __restrict__ o, const bf16* __restrict__ res, const float* __restrict__ lse,
+               float* __restrict__ LDp, bf16* __restrict__ dq, int B, int N, int H, float alpha, TokLayout Lg) {
   const TokLayout L = tok_layout<STRIDED, D>(Lg, N, H);
   constexpr int KT = 64;        // keys per iteration
   constexpr int NC = D / 16;    // 16-wide channel chunks
@@ -1058,18 +1019,45 @@ void dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
     }
   };
 
-  // this lane's query row of Q and dO (B operands of the two score products), -lse2 and -D
+  // this lane's query row of Q and dO (B operands of the two score products); the lane pair
+  // (l, l^32) holds the row's channels cc*16 + 0..7 and cc*16 + 8..15
   bf16x8 qf[NC], df[NC];
 #pragma unroll
   for (int cc = 0; cc < NC; cc++) {
     qf[cc] = jok ? *(const bf16x8*)(q + sbase + (int64_t)j * sT + cc * 16 + g * 8) : zero8();
     df[cc] = jok ? *(const bf16x8*)(dO + sbase + (int64_t)j * sT + cc * 16 + g * 8) : zero8();
   }
-  const float* ldrow = LDp + (((int64_t)b * N + i) * H + h) * 2 * Jp + (j >> 7) * 256 + (j & 127);
-  const float nl2 = ldrow[0];
+  // The correction D[j] = sum_c dO * (o + residual) in FP32 (dO * o without a residual): the
+  // lane's channels in ascending order, then the lane pair's two sums.  -lse2 = -lse * log2(e).
+  // Both are written to the row statistics for the key-tile kernel, which runs after this one
+  // (zero past N).
+  float dsum = 0.0f;
+  if (jok) {
+#pragma unroll
+    for (int cc = 0; cc < NC; cc++) {
+      const int64_t off = sbase + (int64_t)j * sT + cc * 16 + g * 8;
+      const bf16x8 ov = ld_nt((const bf16x8*)(o + off));
+      if (res) {
+        const bf16x8 rv = ld_nt((const bf16x8*)(res + off));
+#pragma unroll
+        for (int e = 0; e < 8; e++) dsum = __builtin_fmaf((float)df[cc][e], (float)ov[e] + (float)rv[e], dsum);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; e++) dsum = __builtin_fmaf((float)df[cc][e], (float)ov[e], dsum);
+      }
+    }
+  }
+  const float Dj = dsum + __shfl_xor(dsum, 32);  // (the same bits on both lanes of the pair)
+  const int64_t srow = ((int64_t)b * N + i) * H + h;  // slice-head row
+  const float nl2 = jok ? -lse[srow * N + j] * kLog2e : 0.0f;
+  if (g == 0) {
+    float* ldrow = LDp + srow * 2 * Jp + (j >> 7) * 256 + (j & 127);
+    ldrow[0] = nl2;
+    ldrow[128] = -Dj;
+  }
   // B operand of the -D start product (parts at k = 0..2 of this lane's query column; the upper
   // lane half holds k = 4..7, zero) and its A operand (ones at k = 0..2 in every key row)
-  const u32x2v dB = g == 0 ? split3_bf16(ldrow[128]) : u32x2v{0u, 0u};
+  const u32x2v dB = g == 0 ? split3_bf16(-Dj) : u32x2v{0u, 0u};
 
   f32x16 acc = {};
   const int nkt = (N + KT - 1) / KT;
@@ -1363,10 +1351,16 @@ tri_attn_status launch_bwd(unsigned stages, const Plan& P, const TokLayout& L, c
                        (const bf16*)bias, (_Float16*)biasB, (int)P.N, (int)P.KB, (int)(P.Jp / 128), nb);
     hipLaunchKernelGGL(bias_prep_fwd_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, st,
                        (const bf16*)bias, biasF, (int)P.N, (int)P.Jp, (int)P.Kp, 1.0f / alpha, nb);
-    const int64_t nrows = P.B * P.N * P.H;
-    hipLaunchKernelGGL((bwd_pre_kernel<D, STRIDED>), dim3((unsigned)(nrows * P.Jp * (D / 8) / 256)), dim3(256), 0, st,
-                       (const bf16*)dO, (const bf16*)o, (const bf16*)res, lse, LDg, (int)P.N, (int)P.H,
-                       (int)P.Jp, L);
+    // dq, and the correction D with the row statistics the key-tile kernel reads
+    const int64_t qtiles = P.B * P.H * P.N * ((P.N + 127) / 128);
+    if (mask)
+      hipLaunchKernelGGL((dq_kernel<D, true, STRIDED>), dim3(grid_xcd(qtiles)), dim3(256), 0, st, (const bf16*)q,
+                         (const bf16*)k, (const bf16*)v, (const bf16*)dO, biasF, mask, (const bf16*)o,
+                         (const bf16*)res, lse, LDg, (bf16*)dq, (int)P.B, (int)P.N, (int)P.H, alpha, L);
+    else
+      hipLaunchKernelGGL((dq_kernel<D, false, STRIDED>), dim3(grid_xcd(qtiles)), dim3(256), 0, st, (const bf16*)q,
+                         (const bf16*)k, (const bf16*)v, (const bf16*)dO, biasF, mask, (const bf16*)o,
+                         (const bf16*)res, lse, LDg, (bf16*)dq, (int)P.B, (int)P.N, (int)P.H, alpha, L);
   }
   float* dkvp = (float*)(base + P.off_dkv);
   if (stages & TRI_ATTN_STAGE_MAIN) {
@@ -1404,15 +1398,6 @@ tri_attn_status launch_bwd(unsigned stages, const Plan& P, const TokLayout& L, c
     }
   }
   if (stages & TRI_ATTN_STAGE_FINAL) {
-    const int64_t qtiles = P.B * P.H * P.N * ((P.N + 127) / 128);
-    if (mask)
-      hipLaunchKernelGGL((dq_kernel<D, true, STRIDED>), dim3(grid_xcd(qtiles)), dim3(256), 0, st, (const bf16*)q,
-                         (const bf16*)k, (const bf16*)v, (const bf16*)dO, biasF, mask, LDg, (bf16*)dq, (int)P.B,
-                         (int)P.N, (int)P.H, alpha, L);
-    else
-      hipLaunchKernelGGL((dq_kernel<D, false, STRIDED>), dim3(grid_xcd(qtiles)), dim3(256), 0, st, (const bf16*)q,
-                         (const bf16*)k, (const bf16*)v, (const bf16*)dO, biasF, mask, LDg, (bf16*)dq, (int)P.B,
-                         (int)P.N, (int)P.H, alpha, L);
     const int64_t nbias = P.B * P.H * P.N * P.N;
     if (nbias % 4 == 0)
       hipLaunchKernelGGL(reduce_dbias_kernel<true>, dim3((unsigned)((nbias / 4 + 255) / 256)), dim3(256), 0, st, dbp,
