@@ -598,12 +598,13 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   constexpr int CPR = D / 8;    // 16-byte chunks per row
   constexpr int NR = D / 2;     // accumulator registers of dK^T / dV^T holding channels c < D
   // LDS map (bytes): per wave, two item buffers of [its 32 Q rows | its 32 dO rows | its 32x32
-  // pair-bias tile | its 32 lse2 values, 32 -D values] | K,V,mask x2 | dK/dV reduction (the odd
-  // query lanes' partials)
+  // pair-bias tile | its 32 lse2 values, 32 -D values] | K,V,mask x2 | dV reduction (the p = 1..3
+  // waves' partials; their dK partials go to their own free item buffer)
   constexpr int kWQ = 32 * D * 2;                   // 32 rows of Q (or dO)
   constexpr int kWB = 2 * kWQ + 2048 + 256;         // one item buffer of one wave
+  static_assert(NR * 64 * 4 <= kWB, "a wave's dK^T partial fits its item buffer");
   constexpr int kKVB = 2 * 64 * D * 2 + 64 * 4;     // K rows, V rows, 64 mask bytes (one per dword)
-  constexpr int kREDB = 4 * 2 * NR * 64 * 4;        // dK^T, dV^T partials of four waves
+  constexpr int kREDB = 2 * 3 * NR * 64 * 4;        // dV^T partials of the p = 1..3 waves of both key halves
   constexpr int oKV = 8 * 2 * kWB, oRED = oKV + 2 * kKVB, kLdsBytes = oRED + kREDB;
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
   __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
@@ -804,13 +805,13 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
       __builtin_amdgcn_sched_barrier(0);
       // raised wave priority while a wave issues its products, so that the arbiter lets it
       // finish them before the other wave of its SIMD takes the issue slots for VALU work
-      __builtin_amdgcn_s_setprio(1);
+      
 #pragma unroll
       for (int cc = 0; cc < NC; cc++) {
         sacc = mfma32(aq[cc], kf[cc], sacc);
         dp = mfma32(ao[cc], vf[cc], dp);
       }
-      __builtin_amdgcn_s_setprio(0);
+      
       // P = exp2(c1 S + log2e bias - lse2) and dS = P (dP - D); dS is summed into the face.
       // The bias term log2e * bias - lse2 comes from one v_fma_mix_f32 per element (fp16
       // bias pairs, -lse2 rows), independent of the products above.
@@ -855,10 +856,10 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
                                tr16p((const lbf16*)(qd + kWQ + trB + m2 * 16 * D * 2)));
         const bf16x8 aq = cat8(tr16p((const lbf16*)(qd + trA + m2 * 16 * D * 2)),
                                tr16p((const lbf16*)(qd + trB + m2 * 16 * D * 2)));
-        __builtin_amdgcn_s_setprio(1);
+        
         dvT = mfma32(ao, pb[m2], dvT);
         dkT = mfma32(aq, sb[m2], dkT);
-        __builtin_amdgcn_s_setprio(0);
+        
       }
       cur_rt ^= 1;
       t++;
@@ -875,72 +876,69 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
     static_assert(NS >= 1 && NS <= kBwdMaxSteps && kBwdMaxSteps == 6, "at most six unrolled steps");
     rr_cur = rr_next;
 
-    // end of slice i: dK^T and dV^T summed over the four query lanes as (p0 + p1) + (p2 + p3)
-    // through a dedicated LDS area (no other data lives there, so the first write needs no
-    // barrier: the previous slice's readers passed this slice's item barriers long ago)
+    // end of slice i: dK^T and dV^T summed over the four query lanes as ((p0 + p1) + p2) + p3.
+    // The p = 1..3 waves put their dK^T partial into their own item buffer of the slice's last
+    // item (free until the prefetch that follows the next slice's first barrier) and their dV^T
+    // partial into a dedicated LDS area (whose readers of the previous slice passed this slice's
+    // first barrier before any writer got here); after one barrier the p = 0 waves sum and store.
+    const int xb = cur_rt ^ 1;  // item buffer of the slice's last item
     lf32* red = (lf32*)(lds + oRED);
-    const int slot_w = (kh * 2 + (p >> 1)) * (2 * NR * 64) + l;
-    if (p & 1) {
+    if (p != 0) {
+      lf32* kx = (lf32*)(lds + (w * 2 + xb) * kWB) + l;
+      lf32* vx = red + (kh * 3 + p - 1) * (NR * 64) + l;
 #pragma unroll
       for (int r = 0; r < NR; r++) {
-        red[slot_w + r * 64] = dkT[r];
-        red[slot_w + (NR + r) * 64] = dvT[r];
+        kx[r * 64] = dkT[r];
+        vx[r * 64] = dvT[r];
       }
     }
     lds_barrier();
-    if (!(p & 1)) {
+    if (p == 0 && any_key) {
 #pragma unroll
-      for (int r = 0; r < NR; r++) {
-        dkT[r] += red[slot_w + r * 64];
-        dvT[r] += red[slot_w + (NR + r) * 64];
-      }
-    }
-    if (p == 2) {  // (p2 + p3) into its own slot, which only this wave read
+      for (int pp = 1; pp < 4; pp++) {
+        const lf32* kx = (const lf32*)(lds + ((pp * 2 + kh) * 2 + xb) * kWB) + l;
+        const lf32* vx = red + (kh * 3 + pp - 1) * (NR * 64) + l;
 #pragma unroll
-      for (int r = 0; r < NR; r++) {
-        red[slot_w + r * 64] = dkT[r];
-        red[slot_w + (NR + r) * 64] = dvT[r];
-      }
-    }
-    lds_barrier();
-    if (CHUNKED && p == 0 && any_key) {  // FP32 partials of this chunk, unscaled
-      const int slot2 = (kh * 2 + 1) * (2 * NR * 64) + l;
-      const int64_t rows = (int64_t)B * N * H * N;
-      float* pk = Ck.dkvp + ((int64_t)(2 * chunk) * rows + sl_row * N + kb * 64) * D;
-      float* pv = pk + rows * D;
-#pragma unroll
-      for (int R = 0; R < NR / 4; R++) {
-        f32x4 k4, v4;
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-          const int r = R * 4 + e;
-          k4[e] = dkT[r] + red[slot2 + r * 64];
-          v4[e] = dvT[r] + red[slot2 + (NR + r) * 64];
-        }
-        if (kok) {
-          const int lh = lane_here();
-          const unsigned lo = (unsigned)(((kh * 32 + (lh & 31)) * D + R * 8 + (lh >> 5) * 4) * 4);
-          *(f32x4*)((char*)pk + lo) = k4;
-          *(f32x4*)((char*)pv + lo) = v4;
+        for (int r = 0; r < NR; r++) {
+          dkT[r] += kx[r * 64];
+          dvT[r] += vx[r * 64];
         }
       }
-    } else if (p == 0 && any_key) {
-      const int slot2 = (kh * 2 + 1) * (2 * NR * 64) + l;
+      if (CHUNKED) {  // FP32 partials of this chunk, unscaled
+        const int64_t rows = (int64_t)B * N * H * N;
+        float* pk = Ck.dkvp + ((int64_t)(2 * chunk) * rows + sl_row * N + kb * 64) * D;
+        float* pv = pk + rows * D;
 #pragma unroll
-      for (int R = 0; R < NR / 4; R++) {
-        bf16x4 ok4, ov4;
+        for (int R = 0; R < NR / 4; R++) {
+          f32x4 k4, v4;
 #pragma unroll
-        for (int e = 0; e < 4; e++) {
-          const int r = R * 4 + e;
-          ok4[e] = (bf16)((dkT[r] + red[slot2 + r * 64]) * alpha);
-          ov4[e] = (bf16)(dvT[r] + red[slot2 + (NR + r) * 64]);
+          for (int e = 0; e < 4; e++) {
+            k4[e] = dkT[R * 4 + e];
+            v4[e] = dvT[R * 4 + e];
+          }
+          if (kok) {
+            const int lh = lane_here();
+            const unsigned lo = (unsigned)(((kh * 32 + (lh & 31)) * D + R * 8 + (lh >> 5) * 4) * 4);
+            *(f32x4*)((char*)pk + lo) = k4;
+            *(f32x4*)((char*)pv + lo) = v4;
+          }
         }
-        if (kok) {  // (the lane offset is recomputed here rather than kept across the slice loop)
-          const int lh = lane_here();
-          const unsigned lo = (unsigned)(((kh * 32 + (lh & 31)) * sT + R * 8 + (lh >> 5) * 4) * 2);
-          const int64_t rb = sbase + (int64_t)kb * 64 * sT;
-          *(bf16x4*)((char*)(dk + rb) + lo) = ok4;
-          *(bf16x4*)((char*)(dv + rb) + lo) = ov4;
+      } else {
+#pragma unroll
+        for (int R = 0; R < NR / 4; R++) {
+          bf16x4 ok4, ov4;
+#pragma unroll
+          for (int e = 0; e < 4; e++) {
+            ok4[e] = (bf16)(dkT[R * 4 + e] * alpha);
+            ov4[e] = (bf16)dvT[R * 4 + e];
+          }
+          if (kok) {  // (the lane offset is recomputed here rather than kept across the slice loop)
+            const int lh = lane_here();
+            const unsigned lo = (unsigned)(((kh * 32 + (lh & 31)) * sT + R * 8 + (lh >> 5) * 4) * 2);
+            const int64_t rb = sbase + (int64_t)kb * 64 * sT;
+            *(bf16x4*)((char*)(dk + rb) + lo) = ok4;
+            *(bf16x4*)((char*)(dv + rb) + lo) = ov4;
+          }
         }
       }
     }
