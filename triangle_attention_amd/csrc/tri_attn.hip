@@ -598,13 +598,16 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   constexpr int CPR = D / 8;    // 16-byte chunks per row
   constexpr int NR = D / 2;     // accumulator registers of dK^T / dV^T holding channels c < D
   // LDS map (bytes): per wave, two item buffers of [its 32 Q rows | its 32 dO rows | its 32x32
-  // pair-bias tile | its 32 lse2 values, 32 -D values] | K,V,mask x2 | dV reduction (the p = 1..3
-  // waves' partials; their dK partials go to their own free item buffer)
+  // pair-bias tile | its 32 lse2 values, 32 -D values] | K,V,mask x2 | dV reduction (the waves'
+  // partials; their dK partials go to their own free item buffer)
   constexpr int kWQ = 32 * D * 2;                   // 32 rows of Q (or dO)
   constexpr int kWB = 2 * kWQ + 2048 + 256;         // one item buffer of one wave
   static_assert(NR * 64 * 4 <= kWB, "a wave's dK^T partial fits its item buffer");
   constexpr int kKVB = 2 * 64 * D * 2 + 64 * 4;     // K rows, V rows, 64 mask bytes (one per dword)
-  constexpr int kREDB = 2 * 3 * NR * 64 * 4;        // dV^T partials of the p = 1..3 waves of both key halves
+  // slice-end dK/dV sums shared by the four query lanes (D = 32), or made by the p = 0 lanes
+  constexpr bool kShared = D == 32;
+  constexpr int kWriters = kShared ? 4 : 3;         // waves per key half writing partials
+  constexpr int kREDB = 2 * kWriters * NR * 64 * 4; // their dV^T partials
   constexpr int oKV = 8 * 2 * kWB, oRED = oKV + 2 * kKVB, kLdsBytes = oRED + kREDB;
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
   __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
@@ -735,11 +738,11 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   prefetch(rr_cur, 0, 0);
 
   // VMEM operations a wave issues after an item's prefetch and before that item's wait: after
-  // the last item of a slice, the dK/dV stores; dk and dv stores of a slice's end: p = 0 waves whose 32 keys are not all past N (the
-  // stores sit behind that wave-uniform test, so each one the count includes is issued with
-  // at least one active lane)
+  // the last item of a slice, its dK/dV stores (two per wave at D = 32; at D = 16 four, by the
+  // p = 0 waves), made only by waves whose 32 keys are not all past N (the stores sit behind that
+  // wave-uniform test, so each one the count includes is issued with at least one active lane)
   const bool any_key = kb * 64 + kh * 32 < N;
-  const int kvStores = (p == 0 && any_key) ? 2 * (NR / 4) : 0;
+  const int kvStores = !any_key ? 0 : kShared ? 2 : (p == 0 ? 2 * (NR / 4) : 0);
   int ns_rt = NS;
   asm volatile("" : "+s"(ns_rt));
   int t = 0;        // item index within the work-group
@@ -877,67 +880,115 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
     rr_cur = rr_next;
 
     // end of slice i: dK^T and dV^T summed over the four query lanes as ((p0 + p1) + p2) + p3.
-    // The p = 1..3 waves put their dK^T partial into their own item buffer of the slice's last
-    // item (free until the prefetch that follows the next slice's first barrier) and their dV^T
-    // partial into a dedicated LDS area (whose readers of the previous slice passed this slice's
-    // first barrier before any writer got here); after one barrier the p = 0 waves sum and store.
+    // The waves put their dK^T partial into their own item buffer of the slice's last item (free
+    // until the prefetch that follows the next slice's first barrier) and their dV^T partial into
+    // a dedicated LDS area (whose readers of the previous slice passed this slice's first barrier
+    // before any writer got here); then one barrier.  At D = 32 every wave writes and the four
+    // query lanes share the sums and the stores, lane p taking channel group p (4 registers) of
+    // both dK and dV; at D = 16 the p = 1..3 waves write and the p = 0 waves sum and store
+    // (measured faster for each head dimension).
     const int xb = cur_rt ^ 1;  // item buffer of the slice's last item
     lf32* red = (lf32*)(lds + oRED);
-    if (p != 0) {
-      lf32* kx = (lf32*)(lds + (w * 2 + xb) * kWB) + l;
-      lf32* vx = red + (kh * 3 + p - 1) * (NR * 64) + l;
-#pragma unroll
-      for (int r = 0; r < NR; r++) {
-        kx[r * 64] = dkT[r];
-        vx[r * 64] = dvT[r];
-      }
-    }
-    lds_barrier();
-    if (p == 0 && any_key) {
-#pragma unroll
-      for (int pp = 1; pp < 4; pp++) {
-        const lf32* kx = (const lf32*)(lds + ((pp * 2 + kh) * 2 + xb) * kWB) + l;
-        const lf32* vx = red + (kh * 3 + pp - 1) * (NR * 64) + l;
+    if constexpr (kShared) {
+      {
+        lf32* kx = (lf32*)(lds + (w * 2 + xb) * kWB) + l;
+        lf32* vx = red + (kh * 4 + p) * (NR * 64) + l;
 #pragma unroll
         for (int r = 0; r < NR; r++) {
-          dkT[r] += kx[r * 64];
-          dvT[r] += vx[r * 64];
+          kx[r * 64] = dkT[r];
+          vx[r * 64] = dvT[r];
         }
       }
-      if (CHUNKED) {  // FP32 partials of this chunk, unscaled
-        const int64_t rows = (int64_t)B * N * H * N;
-        float* pk = Ck.dkvp + ((int64_t)(2 * chunk) * rows + sl_row * N + kb * 64) * D;
-        float* pv = pk + rows * D;
+      lds_barrier();
+      if (any_key) {
 #pragma unroll
-        for (int R = 0; R < NR / 4; R++) {
-          f32x4 k4, v4;
+        for (int arr = 0; arr < 2; arr++) {  // 0: dK, 1: dV; channel group p
+          f32x4 acc4;
 #pragma unroll
-          for (int e = 0; e < 4; e++) {
-            k4[e] = dkT[R * 4 + e];
-            v4[e] = dvT[R * 4 + e];
-          }
-          if (kok) {
-            const int lh = lane_here();
-            const unsigned lo = (unsigned)(((kh * 32 + (lh & 31)) * D + R * 8 + (lh >> 5) * 4) * 4);
-            *(f32x4*)((char*)pk + lo) = k4;
-            *(f32x4*)((char*)pv + lo) = v4;
-          }
-        }
-      } else {
+          for (int pp = 0; pp < 4; pp++) {
+            const lf32* src = arr == 0 ? (const lf32*)(lds + ((pp * 2 + kh) * 2 + xb) * kWB) + l
+                                       : red + (kh * 4 + pp) * (NR * 64) + l;
 #pragma unroll
-        for (int R = 0; R < NR / 4; R++) {
-          bf16x4 ok4, ov4;
-#pragma unroll
-          for (int e = 0; e < 4; e++) {
-            ok4[e] = (bf16)(dkT[R * 4 + e] * alpha);
-            ov4[e] = (bf16)dvT[R * 4 + e];
+            for (int e = 0; e < 4; e++) {
+              const float x = src[(p * 4 + e) * 64];
+              acc4[e] = pp == 0 ? x : acc4[e] + x;
+            }
           }
           if (kok) {  // (the lane offset is recomputed here rather than kept across the slice loop)
             const int lh = lane_here();
-            const unsigned lo = (unsigned)(((kh * 32 + (lh & 31)) * sT + R * 8 + (lh >> 5) * 4) * 2);
-            const int64_t rb = sbase + (int64_t)kb * 64 * sT;
-            *(bf16x4*)((char*)(dk + rb) + lo) = ok4;
-            *(bf16x4*)((char*)(dv + rb) + lo) = ov4;
+            if (CHUNKED) {  // FP32 partials of this chunk, unscaled
+              const int64_t rows = (int64_t)B * N * H * N;
+              float* dst = Ck.dkvp + ((int64_t)(2 * chunk + arr) * rows + sl_row * N + kb * 64) * D;
+              const unsigned lo = (unsigned)(((kh * 32 + (lh & 31)) * D + p * 8 + (lh >> 5) * 4) * 4);
+              *(f32x4*)((char*)dst + lo) = acc4;
+            } else {
+              bf16x4 o4;
+#pragma unroll
+              for (int e = 0; e < 4; e++) o4[e] = (bf16)(arr == 0 ? acc4[e] * alpha : acc4[e]);
+              const unsigned lo = (unsigned)(((kh * 32 + (lh & 31)) * sT + p * 8 + (lh >> 5) * 4) * 2);
+              const int64_t rb = sbase + (int64_t)kb * 64 * sT;
+              *(bf16x4*)((char*)((arr == 0 ? dk : dv) + rb) + lo) = o4;
+            }
+          }
+        }
+      }
+    } else {
+      if (p != 0) {
+        lf32* kx = (lf32*)(lds + (w * 2 + xb) * kWB) + l;
+        lf32* vx = red + (kh * 3 + p - 1) * (NR * 64) + l;
+#pragma unroll
+        for (int r = 0; r < NR; r++) {
+          kx[r * 64] = dkT[r];
+          vx[r * 64] = dvT[r];
+        }
+      }
+      lds_barrier();
+      if (p == 0 && any_key) {
+#pragma unroll
+        for (int pp = 1; pp < 4; pp++) {
+          const lf32* kx = (const lf32*)(lds + ((pp * 2 + kh) * 2 + xb) * kWB) + l;
+          const lf32* vx = red + (kh * 3 + pp - 1) * (NR * 64) + l;
+#pragma unroll
+          for (int r = 0; r < NR; r++) {
+            dkT[r] += kx[r * 64];
+            dvT[r] += vx[r * 64];
+          }
+        }
+        if (CHUNKED) {  // FP32 partials of this chunk, unscaled
+          const int64_t rows = (int64_t)B * N * H * N;
+          float* pk = Ck.dkvp + ((int64_t)(2 * chunk) * rows + sl_row * N + kb * 64) * D;
+          float* pv = pk + rows * D;
+#pragma unroll
+          for (int R = 0; R < NR / 4; R++) {
+            f32x4 k4, v4;
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+              k4[e] = dkT[R * 4 + e];
+              v4[e] = dvT[R * 4 + e];
+            }
+            if (kok) {
+              const int lh = lane_here();
+              const unsigned lo = (unsigned)(((kh * 32 + (lh & 31)) * D + R * 8 + (lh >> 5) * 4) * 4);
+              *(f32x4*)((char*)pk + lo) = k4;
+              *(f32x4*)((char*)pv + lo) = v4;
+            }
+          }
+        } else {
+#pragma unroll
+          for (int R = 0; R < NR / 4; R++) {
+            bf16x4 ok4, ov4;
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+              ok4[e] = (bf16)(dkT[R * 4 + e] * alpha);
+              ov4[e] = (bf16)dvT[R * 4 + e];
+            }
+            if (kok) {  // (the lane offset is recomputed here rather than kept across the slice loop)
+              const int lh = lane_here();
+              const unsigned lo = (unsigned)(((kh * 32 + (lh & 31)) * sT + R * 8 + (lh >> 5) * 4) * 2);
+              const int64_t rb = sbase + (int64_t)kb * 64 * sT;
+              *(bf16x4*)((char*)(dk + rb) + lo) = ok4;
+              *(bf16x4*)((char*)(dv + rb) + lo) = ov4;
+            }
           }
         }
       }
