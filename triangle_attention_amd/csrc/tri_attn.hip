@@ -341,8 +341,10 @@ __device__ __forceinline__ int tr_off(int lane, int r0, int c0) {
 // accumulators (every slice of a head reads the same tiles, so they come from L2), issued
 // before the barrier that publishes tile t so that their latency overlaps that wait; padded
 // keys carry a -inf bias.  K and V rows are XOR-swizzled like the backward's.
+// (five waves per SIMD; the d = 32 instances with a key mask or strided rows need the registers of
+// four to run without spilling, which measured as fast or faster)
 template <int D, bool MASK, bool STRIDED>
-__global__ __launch_bounds__(256, 5)
+__global__ __launch_bounds__(256, D == 32 && (MASK || STRIDED) ? 4 : 5)
 void fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
                 const float* __restrict__ biasF, const uint8_t* __restrict__ mask,
                 bf16* __restrict__ o, float* __restrict__ lse, bf16* __restrict__ res,
