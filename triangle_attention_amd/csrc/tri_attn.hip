@@ -165,10 +165,8 @@ __host__ __device__ __forceinline__ int64_t ctile_off(int m, int n) {
 // (row m = key k%32, column n = query j%32) in accumulator order; value bias[b,h,j,k]/alpha
 // (finite values clamped to +-kBiasMax first, infinities kept), -inf for k >= N, 0 for padded
 // queries j >= N.
-__global__ void bias_prep_fwd_kernel(const bf16* __restrict__ bias, float* __restrict__ out, int N, int Jp, int Kp,
-                                     float inv_alpha, int64_t total) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= total) return;
+__device__ __forceinline__ void bias_prep_fwd_elem(const bf16* __restrict__ bias, float* __restrict__ out, int N,
+                                                   int Jp, int Kp, float inv_alpha, int64_t idx) {
   const int64_t tile = idx >> 10;
   const int off = (int)(idx & 1023);
   const int e = off & 3, n = (off >> 2) & 31, Rg = off >> 7;  // Rg = R*2+g
@@ -188,6 +186,11 @@ __global__ void bias_prep_fwd_kernel(const bf16* __restrict__ bias, float* __res
   }
   out[idx] = val;
 }
+__global__ void bias_prep_fwd_kernel(const bf16* __restrict__ bias, float* __restrict__ out, int N, int Jp, int Kp,
+                                     float inv_alpha, int64_t total) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx < total) bias_prep_fwd_elem(bias, out, N, Jp, Kp, inv_alpha, idx);
+}
 
 // biasB: backward operand, fp16, one contiguous block per (b, h, 64-key block kb) that the
 // backward work-group streams into LDS step by step.  Inside a block: 128-query step s, then
@@ -197,10 +200,8 @@ __global__ void bias_prep_fwd_kernel(const bf16* __restrict__ bias, float* __res
 // score tile.  fp16 holds every bf16 value of magnitude 2^-17..65504 exactly (smaller ones
 // to 2^-25 absolute); larger magnitudes saturate at 65504, infinities stay infinite, and the
 // padding (j >= N or k >= N) is -inf.  The main kernel widens it inside v_fma_mix_f32.
-__global__ void bias_prep_bwd_kernel(const bf16* __restrict__ bias, _Float16* __restrict__ out, int N, int KB,
-                                     int nsteps, int64_t total) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= total) return;
+__device__ __forceinline__ void bias_prep_bwd_elem(const bf16* __restrict__ bias, _Float16* __restrict__ out, int N,
+                                                   int KB, int nsteps, int64_t idx) {
   const int off = (int)(idx & 1023), t = (int)((idx >> 10) & 7);
   int64_t rest = idx >> 13;
   const int s = (int)(rest % nsteps); rest /= nsteps;
@@ -215,6 +216,17 @@ __global__ void bias_prep_bwd_kernel(const bf16* __restrict__ bias, _Float16* __
     if (!__builtin_isinf(x)) x = fminf(fmaxf(x, -kBiasMax), kBiasMax);
   }
   out[idx] = (_Float16)x;
+}
+
+// Both backward operands in one launch (they have the same element count, B*H*Kp*Jp): the
+// backward's fp16 column blocks and, for its dQ kernel, the forward's FP32 tiles.
+__global__ void bias_prep_bwd_kernel(const bf16* __restrict__ bias, _Float16* __restrict__ outB,
+                                     float* __restrict__ outF, int N, int Jp, int Kp, int KB, int nsteps,
+                                     float inv_alpha, int64_t total) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= total) return;
+  bias_prep_bwd_elem(bias, outB, N, KB, nsteps, idx);
+  bias_prep_fwd_elem(bias, outF, N, Jp, Kp, inv_alpha, idx);
 }
 
 // ------------------------------------------------------------------ streaming helpers
@@ -1399,9 +1411,8 @@ tri_attn_status launch_bwd(unsigned stages, const Plan& P, const TokLayout& L, c
   const int64_t nb = P.B * P.H * P.Kp * P.Jp;
   if (stages & TRI_ATTN_STAGE_PREP) {
     hipLaunchKernelGGL(bias_prep_bwd_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, st,
-                       (const bf16*)bias, (_Float16*)biasB, (int)P.N, (int)P.KB, (int)(P.Jp / 128), nb);
-    hipLaunchKernelGGL(bias_prep_fwd_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, st,
-                       (const bf16*)bias, biasF, (int)P.N, (int)P.Jp, (int)P.Kp, 1.0f / alpha, nb);
+                       (const bf16*)bias, (_Float16*)biasB, biasF, (int)P.N, (int)P.Jp, (int)P.Kp, (int)P.KB,
+                       (int)(P.Jp / 128), 1.0f / alpha, nb);
     // dq, and the correction D with the row statistics the key-tile kernel reads
     const int64_t qtiles = P.B * P.H * P.N * ((P.N + 127) / 128);
     if (mask)
