@@ -51,9 +51,9 @@ def test_workspace_sizes(lib):
         f = ta.tri_attn_fwd_workspace_bytes(B, N, H, D)
         b = ta.tri_attn_bwd_workspace_bytes(B, N, H, D)
         assert f > 0 and b > 0 and f % 256 == 0 and b % 256 == 0
-        # the backward holds the pair bias twice (fp16 column blocks, FP32 tiles), the -lse2 and
-        # -D rows (8 bytes per query) and one FP32 pair-bias partial per slice group
-        assert b >= B * H * N * N * (2 + 4 + 4) + B * N * H * N * 8
+        # the backward holds the pair bias twice (fp16 column blocks, FP32 tiles), the row
+        # statistics (16 bytes per query) and one FP32 pair-bias partial per slice group
+        assert b >= B * H * N * N * (2 + 4 + 4) + B * N * H * N * 16
     for bad in [(0, 8, 1, 16), (1, 0, 1, 16), (1, 8, 0, 16), (1, 8, 1, 64), (1, 4097, 1, 16)]:
         assert ta.tri_attn_fwd_workspace_bytes(*bad) == 0
         assert ta.tri_attn_bwd_workspace_bytes(*bad) == 0

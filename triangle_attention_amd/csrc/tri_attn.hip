@@ -455,27 +455,35 @@ void fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
         s[tt] = mfma32k8(mA, u32x2v{g == 0 ? 0x3F80u : 0u, 0u}, s[tt]);
       }
     }
-    // running max over this lane's 32 scores, then across the lane pair (l, l^32)
-    float mx = s[0][0];
+    // maximum over this lane's 32 scores (NaN-propagating maximum: three-operand instructions
+    // with no quieting of the matrix products' results)
+    float mx = __builtin_elementwise_maximum(s[0][0], s[0][1]);
 #pragma unroll
-    for (int r = 1; r < 16; r++) mx = fmaxf(mx, s[0][r]);
+    for (int r = 2; r < 16; r += 2)
+      mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx, s[0][r]), s[0][r + 1]);
 #pragma unroll
-    for (int r = 0; r < 16; r++) mx = fmaxf(mx, s[1][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    for (int r = 0; r < 16; r += 2)
+      mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx, s[1][r]), s[1][r + 1]);
     // the next tile's K and V, issued once this tile's scores exist: the compiler's waits for
     // the bias loads then never include them, and they stream during the softmax and PV
     if (kt + 1 < nkt) prefetch(kt + 1, cur ^ 1, mx);
     // The reference maximum of a query moves only when a score exceeds it by more than
     // 2^8 in probability (exp2 units): probabilities stay <= 256, exact in FP32 and with
     // bf16's relative precision, and most tiles skip the rescale of the accumulators.  The
-    // test is written so that a NaN comparison counts as growth.
-    if (!(mx * c1 <= m_run * c1 + 8.0f)) {
-      const float m_new = fmaxf(m_run, mx);
-      const float scale = __builtin_amdgcn_exp2f((m_run - m_new) * c1);
-      m_run = m_new;
-      l_run *= scale;
+    // tests are written so that a NaN comparison counts as growth.  A query's scores are split
+    // over the lane pair (l, l^32): the pair's maximum exceeds the bound only if one lane's does,
+    // so the exchange between the two lanes happens only when some lane of the wave sees
+    // growth (a wave-uniform branch, all lanes active for the exchange).
+    if (__builtin_amdgcn_ballot_w64(!(mx * c1 <= m_run * c1 + 8.0f))) {
+      mx = __builtin_elementwise_maximum(mx, __shfl_xor(mx, 32));
+      if (!(mx * c1 <= m_run * c1 + 8.0f)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float scale = __builtin_amdgcn_exp2f((m_run - m_new) * c1);
+        m_run = m_new;
+        l_run *= scale;
 #pragma unroll
-      for (int r = 0; r < 16; r++) acc_o[r] *= scale;
+        for (int r = 0; r < 16; r++) acc_o[r] *= scale;
+      }
     }
     // (while every score so far is -inf, the reference is 0: exp2(-inf - 0) = 0, not NaN)
     const float nm = m_run == -INFINITY ? 0.0f : m_run * c1;
@@ -605,17 +613,17 @@ template <int D, bool MASK, int NS, bool STRIDED, bool CHUNKED>
 __global__ __launch_bounds__(512, 1)
 void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
                 const bf16* __restrict__ dO, const bf16* __restrict__ biasB, const uint8_t* __restrict__ mask,
-                const float* __restrict__ LDp, float* __restrict__ dbp, bf16* __restrict__ dk, bf16* __restrict__ dv,
+                const unsigned* __restrict__ LDp, float* __restrict__ dbp, bf16* __restrict__ dk, bf16* __restrict__ dv,
                 int B, int N, int H, int G, int ngroups, float alpha, TokLayout Lg, Chunking Ck) {
   const TokLayout L = tok_layout<STRIDED, D>(Lg, N, H);
   constexpr int NC = D / 16;
   constexpr int CPR = D / 8;    // 16-byte chunks per row
   constexpr int NR = D / 2;     // accumulator registers of dK^T / dV^T holding channels c < D
   // LDS map (bytes): per wave, two item buffers of [its 32 Q rows | its 32 dO rows | its 32x32
-  // pair-bias tile | its 32 lse2 values, 32 -D values] | K,V,mask x2 | dV reduction (the waves'
-  // partials; their dK partials go to their own free item buffer)
+  // pair-bias tile | its 32 queries' row statistics, 16 bytes each] | K,V,mask x2 | dV reduction
+  // (the waves' partials; their dK partials go to their own free item buffer)
   constexpr int kWQ = 32 * D * 2;                   // 32 rows of Q (or dO)
-  constexpr int kWB = 2 * kWQ + 2048 + 256;         // one item buffer of one wave
+  constexpr int kWB = 2 * kWQ + 2048 + 512;         // one item buffer of one wave
   static_assert(NR * 64 * 4 <= kWB, "a wave's dK^T partial fits its item buffer");
   constexpr int kKVB = 2 * 64 * D * 2 + 64 * 4;     // K rows, V rows, 64 mask bytes (one per dword)
   // slice-end dK/dV sums shared by the four query lanes (D = 32), or made by the p = 0 lanes
@@ -672,10 +680,10 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
 
   // Per-lane byte offsets of the streamed loads of a wave's item, fixed for the whole work-group
   // (slice and step enter through the buffer base and the scalar offset): Q and dO rows p*32 + l/CPR
-  // (+16 per further load at D = 32), which land swizzled like K and V; the lse2 (lanes 0-7) and
-  // -D (lanes 8-15) values of the wave's 32 queries.
+  // (+16 per further load at D = 32), which land swizzled like K and V; the row statistics of the
+  // wave's 32 queries (lanes 0-31, one query each).
   const unsigned qd_vo = (unsigned)(((p * 32 + l / CPR) * sT + ((l % CPR) ^ swz<D>(l / CPR)) * 8) * 2);
-  const unsigned ld_vo = (unsigned)((l < 8 ? p * 32 + 4 * l : 128 + p * 32 + 4 * (l - 8)) * 4);
+  const unsigned ld_vo = (unsigned)((p * 32 + (l & 31)) * 16);
   const bf16* bias_blk = biasB + (((int64_t)(b * H + h) * KB + kb) * NSt + s_base) * (int64_t)8192;
 
   // Per-lane LDS byte offsets of the operand reads; the buffer and the step enter as uniform
@@ -693,7 +701,8 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   const unsigned trA = (unsigned)(tr_off<D>(l, 4 * g, c0) * 2);
   const unsigned trB = (unsigned)(tr_off<D>(l, 4 * g + 8, c0) * 2);
   const unsigned offBias = (unsigned)(2 * kWQ + l * 16);
-  const unsigned offRow = (unsigned)(2 * kWQ + 2048 + g * 4 * 4);  // lse2 / -D values of this lane's rows
+  const u32x2v one3 = g == 0 ? u32x2v{0x3F803F80u, 0x3F80u} : u32x2v{0u, 0u};  // ones at k = 0..2
+  const unsigned offRow = (unsigned)(2 * kWQ + 2048 + ln * 16);  // row statistics of query row ln
 
   // issue the loads of work item (ii, ss) into LDS buffer `buf`; rows past N read as zeros
   // LDS byte address of the work-group's LDS block; the streamed loads take LDS addresses
@@ -709,7 +718,7 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
     const int64_t tb = L.slice(b, ii, h);
     r.q = raw_rsrc(q + tb, span);
     r.dO = raw_rsrc(dO + tb, span);
-    r.ld = raw_rsrc(LDp + sl * 2 * Jpt, Jpt * 8);
+    r.ld = raw_rsrc(LDp + sl * 4 * Jpt, Jpt * 16);
     return r;
   };
   // issue the loads of this wave's part of work item (slice with row descriptors rr, step ss)
@@ -726,7 +735,7 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
     // this wave's 32x32 pair-bias tile of the step (2 KiB)
     dma16_asm(rbias, (unsigned)l * 16u, ss * 16384 + (kh * 4 + p) * 2048, dst + 2 * kWQ);
     dma16_asm(rbias, (unsigned)l * 16u, ss * 16384 + (kh * 4 + p) * 2048 + 1024, dst + 2 * kWQ + 1024);
-    if (l < 16) dma16_asm(rr.ld, ld_vo, (s_base + ss) * 1024, dst + 2 * kWQ + 2048);
+    if (l < 32) dma16_asm(rr.ld, ld_vo, (s_base + ss) * 2048, dst + 2 * kWQ + 2048);
   };
   // K, V and the key-mask bytes of slice ii into K/V buffer kvb
   auto prefetch_kv = [&](int ii, int kvb) {
@@ -770,6 +779,9 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
     float mterm = 0.0f;
     f32x16 dkT = {}, dvT = {};
     const RowRes rr_next = row_res(min(i + 1, i_end - 1));  // descriptors of slice i+1
+    // this wave's K and V rows of the slice (B operands of the two score products), read from
+    // LDS at the slice's first item and held in registers for the rest of the slice
+    bf16x8 kf[NC], vf[NC];
 
     auto step = [&](auto S_) {
       constexpr int s = decltype(S_)::value;
@@ -800,61 +812,44 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
       const char* qd = lds + (w * 2 + cur) * kWB;  // this wave's item buffer: Q rows, dO rows, ...
       const char* ld = qd + offRow;
 
-      // S = Q K^T (rows: 32 queries, cols: 32 keys) and dP - D = dO V^T - D, the second
-      // accumulator starting from -D
-      f32x16 sacc = {}, dp;
+      // S - lse/alpha = Q K^T - lse/alpha (rows: 32 queries, cols: 32 keys) and dP - D = dO V^T - D.
+      // The row terms enter through one k = 8 product each: A holds the three bf16 parts of the
+      // row's value at k = 0..2 (lanes of the upper k half hold k = 4..7, multiplied by zeros of
+      // B), B holds ones at k = 0..2.  The parts sum exactly to the FP32 value.
+      f32x16 sacc, dp;
       // all operand reads of the two products are issued before the first product, so that
       // their latencies overlap instead of chaining read -> product -> read
-      bf16x8 aq[NC], kf[NC], ao[NC], vf[NC];
+      bf16x8 aq[NC], ao[NC];
 #pragma unroll
       for (int cc = 0; cc < NC; cc++) {
         aq[cc] = *(const lbf16x8*)(qd + offR[cc]);
-        kf[cc] = *(const lbf16x8*)(Ks + offK + offR[cc]);
+        if (s == 0) kf[cc] = *(const lbf16x8*)(Ks + offK + offR[cc]);
         ao[cc] = *(const lbf16x8*)(qd + kWQ + offR[cc]);
-        vf[cc] = *(const lbf16x8*)(Vs + offK + offR[cc]);
+        if (s == 0) vf[cc] = *(const lbf16x8*)(Vs + offK + offR[cc]);
       }
-#pragma unroll
-      for (int R = 0; R < 4; R++) {
-        const f32x4 x = *(const lf32x4*)(ld + 128 + R * 32);
-#pragma unroll
-        for (int e = 0; e < 4; e++) dp[R * 4 + e] = x[e];
-      }
+      const u32x4v rs = *(const lu32x4*)ld;  // row statistics of this lane's query row
       __builtin_amdgcn_sched_barrier(0);
-      // raised wave priority while a wave issues its products, so that the arbiter lets it
-      // finish them before the other wave of its SIMD takes the issue slots for VALU work
-      
+      sacc = mfma32k8(u32x2v{rs.x, rs.y}, one3, f32x16{});
+      dp = mfma32k8(u32x2v{rs.z, rs.w}, one3, f32x16{});
 #pragma unroll
       for (int cc = 0; cc < NC; cc++) {
         sacc = mfma32(aq[cc], kf[cc], sacc);
         dp = mfma32(ao[cc], vf[cc], dp);
       }
-      
-      // P = exp2(c1 S + log2e bias - lse2) and dS = P (dP - D); dS is summed into the face.
-      // The bias term log2e * bias - lse2 comes from one v_fma_mix_f32 per element (fp16
-      // bias pairs, -lse2 rows), independent of the products above.
+
+      // P = exp2(c1 (S - lse/alpha) + log2e bias) and dS = P (dP - D); dS is summed into the face.
+      // The bias term is one v_fma_mix_f32 per element (fp16 bias pairs).
       const char* bS = qd + offBias;
       const u32x4v b0 = *(const lu32x4*)bS, b1 = *(const lu32x4*)(bS + 1024);
-      // at D = 16 the four lse2 rows are read at once, while the products run; at D = 32 the
-      // registers for that are not free, and each row is read just before its use
-      f32x4 lvb[4];
-      if (D == 16) {
-#pragma unroll
-        for (int R = 0; R < 4; R++) lvb[R] = *(const lf32x4*)(ld + R * 32);
-      }
       float P[16], dS[16];
 #pragma unroll
-      for (int R = 0; R < 4; R++) {
-        const f32x4 lv = D == 16 ? lvb[R] : *(const lf32x4*)(ld + R * 32);
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-          const int r = R * 4 + e;
-          const unsigned pr = r < 8 ? b0[(r & 7) >> 1] : b1[(r & 7) >> 1];
-          const float zb = (r & 1) ? fma_mix_f16<1>(pr, kLog2e, lv[e]) : fma_mix_f16<0>(pr, kLog2e, lv[e]);
-          float z = __builtin_fmaf(sacc[r], c1, zb);
-          if (MASK) z += mterm;
-          P[r] = __builtin_amdgcn_exp2f(z);
-          dS[r] = P[r] * dp[r];
-        }
+      for (int r = 0; r < 16; r++) {
+        const unsigned pr = r < 8 ? b0[(r & 7) >> 1] : b1[(r & 7) >> 1];
+        const float t = sacc[r] * c1;
+        float z = (r & 1) ? fma_mix_f16<1>(pr, kLog2e, t) : fma_mix_f16<0>(pr, kLog2e, t);
+        if (MASK) z += mterm;
+        P[r] = __builtin_amdgcn_exp2f(z);
+        dS[r] = P[r] * dp[r];
       }
 #pragma unroll
       for (int r = 0; r < 16; r++) face[s][r] += dS[r];
@@ -876,7 +871,6 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
         
         dvT = mfma32(ao, pb[m2], dvT);
         dkT = mfma32(aq, sb[m2], dkT);
-        
       }
       cur_rt ^= 1;
       t++;
@@ -1024,8 +1018,9 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
 // dq[j] = alpha * sum_k dS[j,k] K[k] for the queries of one slice (b,i,h), with P and dS
 // recomputed from the forward's statistics: P = exp2(c1 S + log2e bias - lse2), dS = P (dP - D).
 // This kernel runs first in the backward and also forms the correction D[j] = sum_c dO (o + r)
-// of its queries, writing the row statistics the key-tile kernel streams: per slice-head row
-// and 128-query step, 128 values of -lse2 = -lse log2(e), then 128 of -D (zero past N).
+// of its queries, writing the row statistics the key-tile kernel streams: 16 bytes per query
+// of a slice-head row, the three bf16 parts (split3_bf16) of -lse/alpha and a zero, then those
+// of -D and a zero (zeros past N; -2^100 in place of -lse/alpha for a row with no finite score).
 // The work-group and its key loop have the forward's shape: 4 waves = 128 queries, wave w owns
 // 32 of them, and 64-key tiles of K and V stream through double-buffered LDS.  S^T = K Q^T
 // (starting from the prepared bias/alpha tile) and dP^T = V dO^T run on 32x32x16 MFMA, each lane
@@ -1043,7 +1038,7 @@ __global__ __launch_bounds__(256, 4)
 void dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
                const bf16* __restrict__ dO, const float* __restrict__ biasF, const uint8_t* __restrict__ mask,
                const bf16* __restrict__ o, const bf16* __restrict__ res, const float* __restrict__ lse,
-               float* __restrict__ LDp, bf16* __restrict__ dq, int B, int N, int H, float alpha, TokLayout Lg) {
+               unsigned* __restrict__ LDp, bf16* __restrict__ dq, int B, int N, int H, float alpha, TokLayout Lg) {
   const TokLayout L = tok_layout<STRIDED, D>(Lg, N, H);
   constexpr int KT = 64;        // keys per iteration
   constexpr int NC = D / 16;    // 16-wide channel chunks
@@ -1112,15 +1107,16 @@ void dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
   }
   const float Dj = dsum + __shfl_xor(dsum, 32);  // (the same bits on both lanes of the pair)
   const int64_t srow = ((int64_t)b * N + i) * H + h;  // slice-head row
-  const float nl2 = jok ? -lse[srow * N + j] * kLog2e : 0.0f;
+  const float lse_j = jok ? lse[srow * N + j] : 0.0f;
+  const float nl2 = -lse_j * kLog2e;
+  const u32x2v dsp = split3_bf16(-Dj);
   if (g == 0) {
-    float* ldrow = LDp + srow * 2 * Jp + (j >> 7) * 256 + (j & 127);
-    ldrow[0] = nl2;
-    ldrow[128] = -Dj;
+    const u32x2v lsp = split3_bf16(lse_j == INFINITY ? -0x1p100f : -lse_j / alpha);
+    *(u32x4v*)(LDp + (srow * Jp + j) * 4) = u32x4v{lsp.x, lsp.y, dsp.x, dsp.y};
   }
   // B operand of the -D start product (parts at k = 0..2 of this lane's query column; the upper
   // lane half holds k = 4..7, zero) and its A operand (ones at k = 0..2 in every key row)
-  const u32x2v dB = g == 0 ? split3_bf16(-Dj) : u32x2v{0u, 0u};
+  const u32x2v dB = g == 0 ? dsp : u32x2v{0u, 0u};
 
   f32x16 acc = {};
   const int nkt = (N + KT - 1) / KT;
@@ -1326,10 +1322,10 @@ Plan make_plan(int64_t B, int64_t N, int64_t H, int64_t D) {
   p.rows = B * N * H * N;
   p.bias_f32_bytes = round_up(B * H * p.Kp * p.Jp * 4, kAlign);
   p.bias_b16_bytes = round_up(B * H * p.Kp * p.Jp * 2, kAlign);
-  // backward workspace: fp16 bias column blocks | -lse2, -D rows | FP32 bias/alpha tiles (the dQ
+  // backward workspace: fp16 bias column blocks | row statistics | FP32 bias/alpha tiles (the dQ
   // kernel's, as the forward's) | pair-bias gradient partials | chunked dK / dV partials
   p.off_LD = p.bias_b16_bytes;
-  p.off_bF = p.off_LD + round_up(B * N * H * p.Jp * 2 * 4, kAlign);
+  p.off_bF = p.off_LD + round_up(B * N * H * p.Jp * 16, kAlign);
   p.off_dbp = p.off_bF + p.bias_f32_bytes;
   p.off_dkv = p.off_dbp + round_up(p.ngroups * B * H * N * N * 4, kAlign);
   // FP32 dK / dV partials per query chunk, only when there is more than one chunk
@@ -1405,7 +1401,7 @@ tri_attn_status launch_bwd(unsigned stages, const Plan& P, const TokLayout& L, c
   const float alpha = 1.0f / sqrtf((float)D);
   char* base = (char*)ws;
   bf16* biasB = (bf16*)base;
-  float* LDg = (float*)(base + P.off_LD);
+  unsigned* LDg = (unsigned*)(base + P.off_LD);
   float* biasF = (float*)(base + P.off_bF);
   float* dbp = (float*)(base + P.off_dbp);
   const int64_t nb = P.B * P.H * P.Kp * P.Jp;
