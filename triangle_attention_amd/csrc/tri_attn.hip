@@ -895,32 +895,31 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
     // query lanes share the sums and the stores, lane p taking channel group p (4 registers) of
     // both dK and dV; at D = 16 the p = 1..3 waves write and the p = 0 waves sum and store
     // (measured faster for each head dimension).
+    // A partial is stored as NR/4 chunks of [64 lanes][4 registers]: chunk c holds registers
+    // 4c..4c+3 of every lane, 16 contiguous bytes per lane (one conflict-free 16-byte access).
     const int xb = cur_rt ^ 1;  // item buffer of the slice's last item
-    lf32* red = (lf32*)(lds + oRED);
+    lf32x4* red = (lf32x4*)(lds + oRED);
     if constexpr (kShared) {
       {
-        lf32* kx = (lf32*)(lds + (w * 2 + xb) * kWB) + l;
-        lf32* vx = red + (kh * 4 + p) * (NR * 64) + l;
+        lf32x4* kx = (lf32x4*)(lds + (w * 2 + xb) * kWB) + l;
+        lf32x4* vx = red + (kh * 4 + p) * (NR / 4 * 64) + l;
 #pragma unroll
-        for (int r = 0; r < NR; r++) {
-          kx[r * 64] = dkT[r];
-          vx[r * 64] = dvT[r];
+        for (int c = 0; c < NR / 4; c++) {
+          kx[c * 64] = f32x4{dkT[4 * c], dkT[4 * c + 1], dkT[4 * c + 2], dkT[4 * c + 3]};
+          vx[c * 64] = f32x4{dvT[4 * c], dvT[4 * c + 1], dvT[4 * c + 2], dvT[4 * c + 3]};
         }
       }
       lds_barrier();
       if (any_key) {
 #pragma unroll
-        for (int arr = 0; arr < 2; arr++) {  // 0: dK, 1: dV; channel group p
+        for (int arr = 0; arr < 2; arr++) {  // 0: dK, 1: dV; channel group p (chunk p)
           f32x4 acc4;
 #pragma unroll
           for (int pp = 0; pp < 4; pp++) {
-            const lf32* src = arr == 0 ? (const lf32*)(lds + ((pp * 2 + kh) * 2 + xb) * kWB) + l
-                                       : red + (kh * 4 + pp) * (NR * 64) + l;
-#pragma unroll
-            for (int e = 0; e < 4; e++) {
-              const float x = src[(p * 4 + e) * 64];
-              acc4[e] = pp == 0 ? x : acc4[e] + x;
-            }
+            const lf32x4* src = arr == 0 ? (const lf32x4*)(lds + ((pp * 2 + kh) * 2 + xb) * kWB) + l
+                                         : red + (kh * 4 + pp) * (NR / 4 * 64) + l;
+            const f32x4 x = src[p * 64];
+            acc4 = pp == 0 ? x : acc4 + x;
           }
           if (kok) {  // (the lane offset is recomputed here rather than kept across the slice loop)
             const int lh = lane_here();
@@ -942,24 +941,28 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
       }
     } else {
       if (p != 0) {
-        lf32* kx = (lf32*)(lds + (w * 2 + xb) * kWB) + l;
-        lf32* vx = red + (kh * 3 + p - 1) * (NR * 64) + l;
+        lf32x4* kx = (lf32x4*)(lds + (w * 2 + xb) * kWB) + l;
+        lf32x4* vx = red + (kh * 3 + p - 1) * (NR / 4 * 64) + l;
 #pragma unroll
-        for (int r = 0; r < NR; r++) {
-          kx[r * 64] = dkT[r];
-          vx[r * 64] = dvT[r];
+        for (int c = 0; c < NR / 4; c++) {
+          kx[c * 64] = f32x4{dkT[4 * c], dkT[4 * c + 1], dkT[4 * c + 2], dkT[4 * c + 3]};
+          vx[c * 64] = f32x4{dvT[4 * c], dvT[4 * c + 1], dvT[4 * c + 2], dvT[4 * c + 3]};
         }
       }
       lds_barrier();
       if (p == 0 && any_key) {
 #pragma unroll
         for (int pp = 1; pp < 4; pp++) {
-          const lf32* kx = (const lf32*)(lds + ((pp * 2 + kh) * 2 + xb) * kWB) + l;
-          const lf32* vx = red + (kh * 3 + pp - 1) * (NR * 64) + l;
+          const lf32x4* kx = (const lf32x4*)(lds + ((pp * 2 + kh) * 2 + xb) * kWB) + l;
+          const lf32x4* vx = red + (kh * 3 + pp - 1) * (NR / 4 * 64) + l;
 #pragma unroll
-          for (int r = 0; r < NR; r++) {
-            dkT[r] += kx[r * 64];
-            dvT[r] += vx[r * 64];
+          for (int c = 0; c < NR / 4; c++) {
+            const f32x4 k4 = kx[c * 64], v4 = vx[c * 64];
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+              dkT[4 * c + e] += k4[e];
+              dvT[4 * c + e] += v4[e];
+            }
           }
         }
         if (CHUNKED) {  // FP32 partials of this chunk, unscaled
