@@ -868,7 +868,6 @@ void bwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
                                tr16p((const lbf16*)(qd + kWQ + trB + m2 * 16 * D * 2)));
         const bf16x8 aq = cat8(tr16p((const lbf16*)(qd + trA + m2 * 16 * D * 2)),
                                tr16p((const lbf16*)(qd + trB + m2 * 16 * D * 2)));
-        
         dvT = mfma32(ao, pb[m2], dvT);
         dkT = mfma32(aq, sb[m2], dkT);
       }
@@ -1090,8 +1089,8 @@ void dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
   }
   // The correction D[j] = sum_c dO * (o + residual) in FP32 (dO * o without a residual): the
   // lane's channels in ascending order, then the lane pair's two sums.  -lse2 = -lse * log2(e).
-  // Both are written to the row statistics for the key-tile kernel, which runs after this one
-  // (zero past N).
+  // The row statistics for the key-tile kernel, which runs after this one, hold the bf16 parts
+  // of -lse/alpha and of -D (zero past N).
   float dsum = 0.0f;
   if (jok) {
 #pragma unroll
