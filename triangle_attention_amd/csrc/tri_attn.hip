@@ -559,14 +559,15 @@ void fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
 // dQ is not formed here: it sums over every key block, and dq_kernel computes it on its own
 // (see there), so nothing leaves this work-group but dK, dV and the pair-bias gradient.
 //
-// One barrier per item.  Software pipeline: while item t is computed, item t+1's Q, dO, lse2,
-// -D and pair-bias
-// tiles stream from global memory straight into the other half of double-buffered LDS
-// (direct-to-LDS loads, no registers involved), and the next slice's K, V and key-mask
-// bytes stream into the other of two K/V buffers from the first item of a slice on (the
-// first barrier of a slice is the point after which no wave reads the previous slice's).  Rows past N read
-// as zeros through the buffer range check, and the -inf padding of the prepared bias turns
-// every padded query or key into an exact zero probability.
+// Software pipeline: while item t is computed, each wave's own part of item t+1 (its 32 Q and dO
+// rows, its pair-bias tile and its queries' row statistics) streams from global memory straight
+// into the other half of the wave's private double buffer in LDS (direct-to-LDS loads, no
+// registers involved; each wave waits for its own loads), and the next slice's K, V and
+// key-mask bytes stream into the other of two shared K/V buffers from the first item of a slice
+// on.  The work-group meets at two barriers per slice: at its start (the slice's K/V are in LDS
+// and no wave reads the previous slice's any more) and in the dK/dV reduction at its end.  Rows
+// past N read as zeros through the buffer range check, and the -inf padding of the prepared bias
+// turns every padded query or key into an exact zero probability.
 //
 // Rows of Q, dO, K and V in LDS hold their 16-byte chunks in XOR-swizzled order (chunk c
 // of row r sits in slot c ^ swz(r)), which spreads the row-wise operand reads of a wave
