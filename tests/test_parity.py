@@ -89,7 +89,7 @@ def test_small_shape_n1_closed_form():
     assert torch.equal(out["o"].cpu(), torch.from_numpy(inp["v"].view(np.int16)).view(torch.bfloat16))
     assert torch.equal(out["dv"].cpu(), torch.from_numpy(inp["dO"].view(np.int16)).view(torch.bfloat16))
     # dS = P (dP - D) with P = 1: dP and D are the same dot product dO.v summed in two FP32
-    # orders (MFMA vs. the correction kernel), so they agree to a few ulps of |dO.v| (~5)
+    # orders (MFMA vs. the correction formed in the dQ kernel), so they agree to a few ulps of |dO.v|
     assert float(out["dq"].float().abs().max()) < 1e-5
     assert float(out["dk"].float().abs().max()) < 1e-5
     assert float(out["dbias"].abs().max()) < 1e-5

@@ -38,6 +38,7 @@ namespace {
 
 typedef __bf16 bf16;
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -1089,7 +1090,8 @@ void dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
     df[cc] = jok ? *(const bf16x8*)(dO + sbase + (int64_t)j * sT + cc * 16 + g * 8) : zero8();
   }
   // The correction D[j] = sum_c dO * (o + residual) in FP32 (dO * o without a residual): the
-  // lane's channels in ascending order, then the lane pair's two sums.  -lse2 = -lse * log2(e).
+  // lane's channels in ascending pairs, each pair's dO.o then dO.r products (exact in FP32)
+  // summed by one two-term dot instruction, then the lane pair's two sums.  -lse2 = -lse * log2(e).
   // The row statistics for the key-tile kernel, which runs after this one, hold the bf16 parts
   // of -lse/alpha and of -D (zero past N).
   float dsum = 0.0f;
@@ -1101,20 +1103,25 @@ void dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
       if (res) {
         const bf16x8 rv = ld_nt((const bf16x8*)(res + off));
 #pragma unroll
-        for (int e = 0; e < 8; e++) dsum = __builtin_fmaf((float)df[cc][e], (float)ov[e] + (float)rv[e], dsum);
+        for (int e = 0; e < 8; e += 2) {
+          dsum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{df[cc][e], df[cc][e + 1]}, bf16x2{ov[e], ov[e + 1]}, dsum, false);
+          dsum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{df[cc][e], df[cc][e + 1]}, bf16x2{rv[e], rv[e + 1]}, dsum, false);
+        }
       } else {
 #pragma unroll
-        for (int e = 0; e < 8; e++) dsum = __builtin_fmaf((float)df[cc][e], (float)ov[e], dsum);
+        for (int e = 0; e < 8; e += 2)
+          dsum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{df[cc][e], df[cc][e + 1]}, bf16x2{ov[e], ov[e + 1]}, dsum, false);
       }
     }
   }
   const float Dj = dsum + __shfl_xor(dsum, 32);  // (the same bits on both lanes of the pair)
   const int64_t srow = ((int64_t)b * N + i) * H + h;  // slice-head row
   const float lse_j = jok ? lse[srow * N + j] : 0.0f;
+  const float inv_alpha = 1.0f / alpha;
   const float nl2 = -lse_j * kLog2e;
   const u32x2v dsp = split3_bf16(-Dj);
   if (g == 0) {
-    const u32x2v lsp = split3_bf16(lse_j == INFINITY ? -0x1p100f : -lse_j / alpha);
+    const u32x2v lsp = split3_bf16(lse_j == INFINITY ? -0x1p100f : -lse_j * inv_alpha);
     *(u32x4v*)(LDp + (srow * Jp + j) * 4) = u32x4v{lsp.x, lsp.y, dsp.x, dsp.y};
   }
   // B operand of the -D start product (parts at k = 0..2 of this lane's query column; the upper
