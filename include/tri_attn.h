@@ -33,9 +33,10 @@
  *   - All pointers are device pointers, 16-byte aligned (key_mask: any alignment).
  *   - Supported shapes: D in {16, 32}; B, H >= 1; 1 <= N <= TRI_ATTN_MAX_N for the backward
  *     (and the forward that feeds it), 1 <= N <= TRI_ATTN_FWD_MAX_N for the forward alone.
- *   - The library allocates no memory and keeps no state between calls.  Scratch
- *     space comes from the caller through (workspace, workspace_bytes), sized by the
- *     matching *_workspace_bytes function, and is only valid for the call it is passed to.
+ *   - The library allocates no memory and keeps no state between calls (the one exception,
+ *     tri_attn_fwd_noalloc below, keeps a fixed scratch array per GPU).  Scratch space comes
+ *     from the caller through (workspace, workspace_bytes), sized by the matching
+ *     *_workspace_bytes function, and is only valid for the call it is passed to.
  *   - Arguments are validated synchronously before anything is launched.  On any
  *     error nothing is launched and no output is written.
  *   - Work is enqueued on `stream` and runs asynchronously; faults inside kernels
