@@ -1127,6 +1127,13 @@ void dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
   // B operand of the -D start product (parts at k = 0..2 of this lane's query column; the upper
   // lane half holds k = 4..7, zero) and its A operand (ones at k = 0..2 in every key row)
   const u32x2v dB = g == 0 ? dsp : u32x2v{0u, 0u};
+  // at D = 16 (one product per dP^T tile) the registers allow -D itself as the product's start
+  // value: every accumulator register of a lane belongs to its query column
+  f32x16 dstart;
+  if constexpr (D == 16) {
+#pragma unroll
+    for (int r = 0; r < 16; r++) dstart[r] = -Dj;
+  }
 
   f32x16 acc = {};
   const int nkt = (N + KT - 1) / KT;
@@ -1172,8 +1179,12 @@ void dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf1
         const bf16x8 ka = *(const lbf16x8*)(Ks + rk_ * D + ((cc * 2 + g) ^ swz<D>(rk_)) * 8);
         const bf16x8 va = *(const lbf16x8*)(Vs + rk_ * D + ((cc * 2 + g) ^ swz<D>(rk_)) * 8);
         s[tt] = mfma32(ka, qf[cc], s[tt]);
-        dp = mfma32(va, df[cc], cc == 0 ? f32x16{} : dp);
-        if (cc == 0) dp = mfma32k8(one3, dB, dp);  // dP - D
+        if constexpr (D == 16) {
+          dp = mfma32(va, df[cc], dstart);  // dP - D
+        } else {
+          dp = mfma32(va, df[cc], cc == 0 ? f32x16{} : dp);
+          if (cc == 0) dp = mfma32k8(one3, dB, dp);  // dP - D
+        }
       }
       if (MASK) {  // A: -2^100 at k = 0 of a masked key's row (this lane's row is key rk_); B: one at k = 0
         const u32x2v mA = {(g == 0 && !Ms_[cur][rk_]) ? 0xF180u : 0u, 0u};
