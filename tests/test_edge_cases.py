@@ -2,6 +2,8 @@
 
 - Rows with no key of finite score (fully masked slices of a padded batch, queries whose every
   key carries a -inf bias) attend to nothing: o = 0, lse = +inf, no gradient.
+- Slices that keep exactly one key: probability 1, o = v bit for bit, gradients that vanish in
+  exact arithmetic stay within the dot-product rounding bound.
 - -inf and very large bias values; finite bias magnitudes above 65504 are clamped alike in
   both passes (include/tri_attn.h).
 - Backward shapes whose last key block has a 32-key half entirely past N without query chunks
@@ -81,6 +83,53 @@ def test_fully_masked_slices(B, N, H, D):
         assert torch.isposinf(out["lse"][b, sl]).all()
         for n in ("o", "res", "dq", "dk", "dv"):
             assert float(out[n][b, sl].float().abs().max()) == 0.0, n
+
+
+@pytest.mark.parametrize("N,D", [(150, 32), (287, 32), (200, 16)])
+def test_one_kept_key_per_slice(N, D):
+    """Every slice keeps exactly one key (a different one per slice), with a wide bias.  Each
+    query's probability is then exactly 1 on that key: o equals its v row bit for bit, lse is
+    its score, dv is the sum of dO over the queries.  dS = dP - D is zero in exact arithmetic,
+    where dP and D are the same dot product dO.v summed in two FP32 orders, so dq, dk and dbias
+    are rounding noise, bounded by the standard dot-product error bounds: D's own sum of d terms
+    (d eps S) and the product's sum of -D and d terms of magnitude up to 2S ((d + 1) eps 2S),
+    |dP - D| <= 4 d eps S with S = sum_c |dO_c v_c| and eps = 2^-24, per query; times alpha
+    max|k| for dq (one key per query), alpha max|q| summed over the queries for dk, and summed
+    over the slices for dbias."""
+    B, H = 1, 2
+    print(f"one kept key per slice N={N} D={D}", flush=True)
+    inp = make_inputs(B, N, H, D, seed=500 + N + D, bias_std=4.0)
+    rng = np.random.default_rng(N + D)
+    kept = rng.integers(0, N, size=N)
+    m = np.zeros((B, N, N), dtype=np.uint8)
+    m[0, np.arange(N), kept] = 1
+    inp["key_mask"] = m
+    out = run_gpu(inp)
+    x = inputs64(inp)
+    o64, lse64 = oracle.forward64(x["q"], x["k"], x["v"], x["bias"], m)
+    _, _, dv64, _ = oracle.backward64(x["q"], x["k"], x["v"], x["bias"], x["dO"], m)
+    v = x["v"][0]                                             # [N(slice), H, N(key), D]
+    o = f64(out["o"])[0]
+    for i in range(N):
+        assert np.array_equal(o[i], np.broadcast_to(v[i, :, kept[i]][:, None, :], o[i].shape)), i
+    assert maxabs(f64(out["lse"]), lse64) <= TOL_LSE_MAXABS
+    assert rrmse(f64(out["dv"]), dv64) <= TOL_GRAD_RRMSE
+    alpha = D ** -0.5
+    eps = 2.0 ** -24
+    dO = x["dO"][0]                                           # [N, H, N(query), D]
+    vk = np.stack([v[i, :, kept[i]] for i in range(N)])      # [N, H, D]: the kept key's v row
+    dsb = 4 * D * eps * np.abs(dO * vk[:, :, None, :]).sum(-1)  # [N, H, N(query)]: |dS| bound
+    kk = np.stack([x["k"][0][i, :, kept[i]] for i in range(N)])  # [N, H, D]
+    dq_b = alpha * dsb.max() * np.abs(kk).max()
+    dk_b = alpha * dsb.sum(-1).max() * np.abs(x["q"]).max()
+    db_b = dsb.sum(0).max()
+    print(f"  bounds dq {dq_b:.2e} dk {dk_b:.2e} dbias {db_b:.2e}; "
+          f"max |dq| {float(out['dq'].float().abs().max()):.2e} |dk| {float(out['dk'].float().abs().max()):.2e} "
+          f"|dbias| {float(out['dbias'].abs().max()):.2e}", flush=True)
+    # dq and dk are rounded to bf16 (at most 2^-9 relative); dbias adds N FP32 terms
+    assert float(out["dq"].float().abs().max()) <= dq_b * (1 + 2 ** -8)
+    assert float(out["dk"].float().abs().max()) <= dk_b * (1 + 2 ** -8)
+    assert float(out["dbias"].abs().max()) <= db_b * (1 + 2 ** -10)
 
 
 @pytest.mark.parametrize("D", [16, 32])
