@@ -369,6 +369,8 @@ void fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   __shared__ __attribute__((aligned(16))) bf16 Ks_[2][KT * D];
   __shared__ __attribute__((aligned(16))) bf16 Vs_[2][KT * D];
   __shared__ __attribute__((aligned(16))) uint8_t Ms_[2][KT];
+  // D = 16: a tile of ones read in place of V by the lanes of the product's upper 16 rows
+  __shared__ __attribute__((aligned(16))) bf16 Ones_[D == 16 ? KT * 16 : 8];
 
   const int QT = (N + 127) / 128;
   const int64_t ntiles = (int64_t)B * H * N * QT;
@@ -414,6 +416,7 @@ void fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
 
   const int nkt = (N + KT - 1) / KT;
   if (MASK && tid < KT) Ms_[0][tid] = tid < N ? mrow[tid] : (uint8_t)1;
+  if (D == 16) ((__attribute__((address_space(3))) u32x2v*)Ones_)[tid] = u32x2v{0x3F803F80u, 0x3F803F80u};  // read after the first barrier
   prefetch(0, 0, 0.0f);
   // Key tile kt in LDS buffer CUR.  The buffer index is a compile-time constant (the loop below
   // runs two tiles per pass), so every LDS address is a per-lane offset plus an immediate.
@@ -499,10 +502,11 @@ void fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
       }
     l_run += lsum;
 
-    // O^T (channels x queries) += V^T P^T; lane group (l/16) selects channel half and key run
-    // (at D = 16 both halves read channels 0..15: the upper 16 rows of the product repeat the
-    // lower ones and are never stored)
+    // O^T (channels x queries) += V^T P^T; lane group (l/16) selects channel half and key run.
+    // At D = 16 the lanes of the upper 16 rows read ones: those rows accumulate the sum of the
+    // bf16 probabilities that multiply V, which normalises o (the FP32 sum gives lse).
     const int G16 = l >> 4, chalf = G16 & 1;
+    const lbf16* Va = (D == 16 && chalf) ? (const lbf16*)Ones_ : Vs;
 #pragma unroll
     for (int tt = 0; tt < 2; tt++)
 #pragma unroll
@@ -510,7 +514,7 @@ void fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
         const bf16x8 pb = pack8(&p[tt][m2 * 8]);
         const int r0 = tt * 32 + m2 * 16 + g * 4;
         const int c0 = D == 32 ? chalf * 16 : 0;
-        const bf16x8 a = cat8(tr16p(Vs + tr_off<D>(l, r0, c0)), tr16p(Vs + tr_off<D>(l, r0 + 8, c0)));
+        const bf16x8 a = cat8(tr16p(Va + tr_off<D>(l, r0, c0)), tr16p(Va + tr_off<D>(l, r0 + 8, c0)));
         acc_o = mfma32(a, pb, acc_o);
       }
     if (MASK && tid < KT) Ms_[cur ^ 1][tid] = mnext;  // read after the next barrier
@@ -526,7 +530,9 @@ void fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   // the reference maximum is about -2^100, far below any score of a kept key.)
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const bool empty = !(l_tot > 0.0f) || (MASK && !(m_run > -0x1p99f));
-  const float inv = empty ? 0.0f : 1.0f / l_tot;
+  // o is normalised by the sum of the probabilities as they entered the product (D = 16: an
+  // upper row of the product; every kept row has one probability >= 1 there)
+  const float inv = empty ? 0.0f : 1.0f / (D == 16 ? acc_o[8] : l_tot);
   if (jok) {
     bf16* orow = o + sbase + (int64_t)j * sT;
     bf16* rrow = res ? res + sbase + (int64_t)j * sT : nullptr;
