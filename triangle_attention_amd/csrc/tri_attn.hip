@@ -413,6 +413,14 @@ void fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
 
   f32x16 acc_o = {};
   float m_run = -INFINITY, l_run = 0.0f;
+  // D = 32: the sum of the bf16 probabilities that multiply V, through one 16x16x32 product per
+  // PV product (A: ones in row 0 at the k groups of query n, row 1 at those of query n + 16);
+  // lanes 0-15 hold it for queries l and l + 16 in registers 0 and 1
+  f32x4 psum = {};
+  const int lm = l & 15, lk = l >> 4;
+  const bool onesA = (lm == 0 && (lk & 1) == 0) || (lm == 1 && (lk & 1) == 1);
+  const unsigned oa = onesA ? 0x3F803F80u : 0u;
+  const bf16x8 oneA = __builtin_bit_cast(bf16x8, u32x4v{oa, oa, oa, oa});
 
   const int nkt = (N + KT - 1) / KT;
   if (MASK && tid < KT) Ms_[0][tid] = tid < N ? mrow[tid] : (uint8_t)1;
@@ -480,13 +488,17 @@ void fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
     // growth (a wave-uniform branch, all lanes active for the exchange).
     if (__builtin_amdgcn_ballot_w64(!(mx * c1 <= m_run * c1 + 8.0f))) {
       mx = __builtin_elementwise_maximum(mx, __shfl_xor(mx, 32));
-      if (!(mx * c1 <= m_run * c1 + 8.0f)) {
-        const float m_new = fmaxf(m_run, mx);
-        const float scale = __builtin_amdgcn_exp2f((m_run - m_new) * c1);
-        m_run = m_new;
-        l_run *= scale;
+      const bool grow = !(mx * c1 <= m_run * c1 + 8.0f);
+      const float m_new = grow ? fmaxf(m_run, mx) : m_run;
+      const float scale = grow ? __builtin_amdgcn_exp2f((m_run - m_new) * c1) : 1.0f;
+      m_run = m_new;
+      l_run *= scale;
 #pragma unroll
-        for (int r = 0; r < 16; r++) acc_o[r] *= scale;
+      for (int r = 0; r < 16; r++) acc_o[r] *= scale;
+      if (D == 32) {
+        const float s16 = __shfl(scale, lm + 16);
+        psum[0] *= scale;
+        psum[1] *= s16;
       }
     }
     // (while every score so far is -inf, the reference is 0: exp2(-inf - 0) = 0, not NaN)
@@ -516,6 +528,7 @@ void fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
         const int c0 = D == 32 ? chalf * 16 : 0;
         const bf16x8 a = cat8(tr16p(Va + tr_off<D>(l, r0, c0)), tr16p(Va + tr_off<D>(l, r0 + 8, c0)));
         acc_o = mfma32(a, pb, acc_o);
+        if (D == 32) psum = mfma16(oneA, pb, psum);
       }
     if (MASK && tid < KT) Ms_[cur ^ 1][tid] = mnext;  // read after the next barrier
   };
@@ -532,7 +545,8 @@ void fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf
   const bool empty = !(l_tot > 0.0f) || (MASK && !(m_run > -0x1p99f));
   // o is normalised by the sum of the probabilities as they entered the product (D = 16: an
   // upper row of the product; every kept row has one probability >= 1 there)
-  const float inv = empty ? 0.0f : 1.0f / (D == 16 ? acc_o[8] : l_tot);
+  const float plo = __shfl(psum[0], ln & 15), phi = __shfl(psum[1], ln & 15);
+  const float inv = empty ? 0.0f : 1.0f / (D == 16 ? acc_o[8] : (ln < 16 ? plo : phi));
   if (jok) {
     bf16* orow = o + sbase + (int64_t)j * sT;
     bf16* rrow = res ? res + sbase + (int64_t)j * sT : nullptr;
