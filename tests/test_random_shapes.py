@@ -7,7 +7,7 @@ bound of 2e-2 is checked where the bias is as wide as the workloads' (std <= 1).
 of std 4 a row can be dominated by one key whose bf16 probability in the PV product carries a
 relative rounding error up to 2^-9, and the output itself is rounded to bf16 (half an ulp is
 up to 2^-8 of |o|); there the check is |o - o64| <= 2^-8 (max|o64| + max|v|), which those two
-roundings respect (measured: 2.2e-2 at most, where that bound is about 4e-2).
+roundings respect.
 Method: TurboPairFormer (arXiv 2610.05854), Abstract.
 """
 import numpy as np
