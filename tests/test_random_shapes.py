@@ -4,10 +4,9 @@ on every slice.
 
 Bounds as in test_parity.py (o rel-RMSE, lse, every gradient's rel-RMSE).  The forward max-abs
 bound of 2e-2 is checked where the bias is as wide as the workloads' (std <= 1).  With a bias
-of std 4 a row can be dominated by one key whose bf16 probability in the PV product carries a
-relative rounding error up to 2^-9, and the output itself is rounded to bf16 (half an ulp is
-up to 2^-8 of |o|); there the check is |o - o64| <= 2^-8 (max|o64| + max|v|), which those two
-roundings respect.
+of std 4 rows are peaked and outputs larger; there the check is the two bf16 roundings that
+reach o: the output's (half an ulp, up to 2^-8 of |o|) and that of the probabilities that
+multiply V (up to 2^-9 each, relative), |o - o64| <= 2^-8 (max|o64| + max|v|).
 Method: TurboPairFormer (arXiv 2610.05854), Abstract.
 """
 import numpy as np
